@@ -1,0 +1,168 @@
+/*
+ * pkv.h -- C ABI of the paged-KV attention library for MI355X (gfx950).
+ *
+ * Attention over a paged KV cache: the keys and values of every sequence live
+ * in fixed-size token blocks of one shared pool ("Building a minimal vLLM
+ * implementation", section config.py, kvcache_block_size), and each sequence
+ * reaches its blocks through a block table that maps logical blocks to
+ * physical ones (same page, section sequence.py, block_table). The pool's
+ * blocks are numbered 0..num_blocks-1 ("Implementation Details", section
+ * "PagedAttention -- BlockPool"). Decode runs one query row per sequence;
+ * prefill runs chunks of query rows after the tokens already cached (section
+ * sequence.py, num_cached_tokens). Both compute exactly what naive softmax
+ * attention over the gathered K/V computes ("A vLLM engine small enough to
+ * read in one sitting", sections "What it does" and "The interesting bit").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    keeps no pointer after a call returns and allocates nothing.
+ *  - Layouts are dense and row-major:
+ *        q, out (decode)     [num_seqs, num_q_heads, head_dim]
+ *        q, out (prefill)    [total_q,  num_q_heads, head_dim]   (packed chunks)
+ *        k, v (new rows)     [num_tokens, num_kv_heads, head_dim]
+ *        k_cache, v_cache    [num_blocks, block_size, num_kv_heads, head_dim]
+ *        block_tables        int32 [num_seqs, max_blocks_per_seq]
+ *        context_lens        int32 [num_seqs]
+ *        slot_mapping        int32 [num_tokens]
+ *        cu_seqlens_q        int32 [num_seqs + 1]
+ *  - Position p of sequence s lives in physical block
+ *    block_tables[s][p / block_size], row p % block_size. Table entries past
+ *    ceil(context_lens[s] / block_size) are never read and may hold anything.
+ *  - context_lens[s] counts every token of the sequence whose K/V is in the
+ *    cache, including the rows stored in the same step; 0 yields zero output.
+ *  - GQA: q-head h reads kv-head h / (num_q_heads / num_kv_heads).
+ *  - Logits are scale * (q . k); softmax and accumulation run in fp32; the
+ *    output has the dtype of q and is rounded to nearest-even once.
+ *  - q, caches, new rows and out share one dtype (PKV_F32 or PKV_BF16).
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL is the null
+ *    stream) and never synchronizes. The host never reads device memory:
+ *    values held in device arrays (block ids, lengths, slots) are the
+ *    caller's contract; kernels skip slots and block rows outside the pool
+ *    rather than touching memory out of bounds.
+ *  - Return value: PKV_OK, or a negative pkv_status with a message available
+ *    from pkv_last_error() in the calling thread. Invalid arguments are
+ *    reported before anything is launched. No exception crosses the ABI and
+ *    nothing aborts.
+ *  - out must not alias q or the caches. The store writes the caches in place.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_EINVAL = -1,        /* bad pointer, size, or inconsistent arguments */
+  PKV_EUNSUPPORTED = -2,  /* valid request outside what the kernels implement */
+  PKV_EWORKSPACE = -3,    /* split-K workspace missing or too small */
+  PKV_EHIP = -4           /* the HIP runtime reported an error at launch */
+} pkv_status;
+
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+/* Decode kernel family. AUTO picks the matrix-core kernel for bf16 and the
+ * vector kernel for fp32. */
+typedef enum {
+  PKV_DECODE_AUTO = 0,
+  PKV_DECODE_VALU = 1,    /* vector FMA dot products, lane-shuffle reductions */
+  PKV_DECODE_MFMA = 2     /* GQA group packed into matrix-core tiles (bf16 only) */
+} pkv_decode_algo;
+
+/* Library version as major*10000 + minor*100 + patch. */
+int pkv_version(void);
+
+/* Message describing the last non-OK status returned in this thread. */
+const char* pkv_last_error(void);
+
+/*
+ * kv_cache_store: for every token t with 0 <= slot_mapping[t] < num_blocks *
+ * block_size, copy k[t] into k_cache row (slot / block_size, slot %
+ * block_size) and v[t] into the same row of v_cache. Negative slots are
+ * padding and write nothing; slots past the pool are skipped. The copy is
+ * bit-exact. Two tokens naming the same slot race (the result is one of
+ * them); callers keep slots unique.
+ *   num_tokens >= 0 (0 launches nothing); num_blocks, block_size,
+ *   num_kv_heads, head_dim > 0; num_kv_heads * head_dim * dtype size must be
+ *   a multiple of 16 bytes.
+ */
+int pkv_kv_cache_store(const void* k, const void* v, void* k_cache, void* v_cache,
+                       const int32_t* slot_mapping, int32_t num_tokens,
+                       int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                       int32_t head_dim, pkv_dtype dtype, void* stream);
+
+/*
+ * Bytes of split-K workspace needed by pkv_paged_attention_decode for the
+ * same num_seqs, num_q_heads, head_dim, max_context_len and partition_size:
+ * fp32 running max, sum and unnormalised output for every (sequence, q-head,
+ * partition). 0 when partition_size is 0 (single pass). Layout inside:
+ *   m [num_seqs, num_q_heads, P], l [num_seqs, num_q_heads, P],
+ *   o [num_seqs, num_q_heads, P, head_dim],  P = ceil(max_context_len / partition_size).
+ */
+size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_context_len, int32_t partition_size);
+
+/*
+ * paged_attention_decode: out[s, h] = softmax_j(scale * q[s, h] . K_s[j, g])
+ * . V_s[j, g] over positions j < context_lens[s], g = h / (Hq / Hkv), with
+ * K_s, V_s gathered through block_tables[s].
+ *   max_context_len: a host-side bound >= every context_lens[s] and <=
+ *     max_blocks_per_seq * block_size; it sizes the grid and the workspace.
+ *     A device length above it breaks the contract and is truncated to it.
+ *   partition_size: 0 runs one pass per (sequence, kv-head). Otherwise a
+ *     positive multiple of 16: each (sequence, kv-head) is split into
+ *     partitions of that many tokens whose partial results (running max,
+ *     sum, unnormalised output) go to `workspace`, and a second launch merges
+ *     them (log-sum-exp). Sequences that fit in one partition are written
+ *     directly.
+ *   workspace / workspace_bytes: device buffer of at least
+ *     pkv_decode_workspace_size(...) bytes (may be NULL when that is 0).
+ *   algo: pkv_decode_algo. The MFMA kernel needs bf16 and
+ *     num_q_heads / num_kv_heads <= 16.
+ * Supported: head_dim in {64, 128}; block_size a multiple of 16 up to 256;
+ * num_q_heads / num_kv_heads <= 16.
+ */
+int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_tables,
+                               const int32_t* context_lens, int32_t num_seqs,
+                               int32_t max_blocks_per_seq, int32_t max_context_len,
+                               int32_t num_blocks, int32_t block_size,
+                               int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, float scale, int32_t partition_size,
+                               void* workspace, size_t workspace_bytes,
+                               pkv_dtype dtype, int32_t algo, void* stream);
+
+/*
+ * paged_attention_prefill_chunk: attention of packed query chunks over their
+ * paged contexts. Chunk c owns q rows cu_seqlens_q[c] .. cu_seqlens_q[c+1]-1
+ * (L_c rows); context_lens[c] >= L_c counts its cached tokens plus its own
+ * L_c rows, whose K/V must already be stored. Row i of chunk c sits at
+ * position P0 + i with P0 = context_lens[c] - L_c and, when causal != 0,
+ * attends to positions 0 .. P0 + i; otherwise to all context_lens[c]
+ * positions.
+ *   total_q: rows of q and out; max_q_len >= every L_c (sizes the grid);
+ *   max_context_len >= every context_lens[c], <= max_blocks_per_seq * block_size.
+ * Supported: bf16, head_dim 128, block_size a multiple of 16 up to 256,
+ * num_q_heads / num_kv_heads in {1, 2, 4, 8}.
+ */
+int pkv_paged_attention_prefill_chunk(void* out, const void* q, const void* k_cache,
+                                      const void* v_cache, const int32_t* block_tables,
+                                      const int32_t* cu_seqlens_q,
+                                      const int32_t* context_lens, int32_t num_seqs,
+                                      int32_t total_q, int32_t max_q_len,
+                                      int32_t max_blocks_per_seq, int32_t max_context_len,
+                                      int32_t num_blocks, int32_t block_size,
+                                      int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, float scale, int32_t causal,
+                                      pkv_dtype dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

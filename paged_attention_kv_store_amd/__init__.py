@@ -1,7 +1,18 @@
 """Paged-KV attention for MI355X (gfx950).
 
 The compute path is a C-ABI shared library of hand-written HIP kernels
-(csrc/); this package is its thin ctypes binding plus the seeded input
-generators. Importing the package does not load the library; the first call
-does, and raises if it has not been built.
+(csrc/, interface in include/pkv.h); this package is its thin ctypes binding
+plus the seeded input generators. Importing the package does not load the
+library; the first call does, and raises if it has not been built.
 """
+
+from .binding import (  # noqa: F401
+    DECODE_ALGOS,
+    PkvError,
+    decode_workspace_size,
+    kv_cache_store,
+    lib,
+    library_path,
+    paged_attention_decode,
+    paged_attention_prefill_chunk,
+)

@@ -1,0 +1,181 @@
+"""ctypes binding of libpkv.so (include/pkv.h), with the same entry-point names.
+
+Argument marshalling only: shape and dtype checks on torch tensors, then the
+raw device pointers, sizes and the current HIP stream go to the C ABI. Every
+step of the computation runs in the library's HIP kernels. torch supplies
+device memory and streams; nothing here computes on the data. If the library
+has not been built, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
+_lock = threading.Lock()
+_lib = None
+
+PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EWORKSPACE, PKV_EHIP = 0, -1, -2, -3, -4
+PKV_F32, PKV_BF16 = 0, 1
+DECODE_ALGOS = {"auto": 0, "valu": 1, "mfma": 2}
+
+_i32 = ctypes.c_int32
+_vp = ctypes.c_void_p
+_SIGNATURES = {
+    "pkv_version": ([], ctypes.c_int),
+    "pkv_last_error": ([], ctypes.c_char_p),
+    "pkv_kv_cache_store": ([_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _vp],
+                           ctypes.c_int),
+    "pkv_decode_workspace_size": ([_i32, _i32, _i32, _i32, _i32], ctypes.c_size_t),
+    "pkv_paged_attention_decode": ([_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                    _i32, _i32, _i32, ctypes.c_float, _i32, _vp, ctypes.c_size_t,
+                                    ctypes.c_int, _i32, _vp], ctypes.c_int),
+    "pkv_paged_attention_prefill_chunk": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                           _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                           ctypes.c_float, _i32, ctypes.c_int, _vp], ctypes.c_int),
+}
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"pkv status {status}: {message}")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """Load libpkv.so once; raise if it is missing (no fallback exists)."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(_LIB_PATH):
+                    raise RuntimeError(
+                        f"{_LIB_PATH} is not built; run paged_attention_kv_store_amd/build.py")
+                handle = ctypes.CDLL(_LIB_PATH)
+                for name, (args, res) in _SIGNATURES.items():
+                    fn = getattr(handle, name)
+                    fn.argtypes = args
+                    fn.restype = res
+                _lib = handle
+    return _lib
+
+
+def exported_symbols():
+    return sorted(_SIGNATURES)
+
+
+def _check(status):
+    if status != PKV_OK:
+        raise PkvError(status, lib().pkv_last_error().decode(errors="replace"))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return PKV_F32
+    if t.dtype == torch.bfloat16:
+        return PKV_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _dev(*ts):
+    for t in ts:
+        _need(t.is_cuda, "tensors must be on the GPU")
+        _need(t.is_contiguous(), "tensors must be contiguous")
+
+
+def kv_cache_store(k, v, k_cache, v_cache, slot_mapping, stream=None):
+    """Copy k[t], v[t] into the cache row named by slot_mapping[t] (in place)."""
+    _dev(k, v, k_cache, v_cache, slot_mapping)
+    _need(k.dim() == 3 and v.shape == k.shape, "k, v must be [T, Hkv, D]")
+    _need(k_cache.dim() == 4 and v_cache.shape == k_cache.shape, "caches must be [NB, bs, Hkv, D]")
+    _need(k_cache.shape[2:] == k.shape[1:], "cache and new rows disagree on heads/dims")
+    _need(slot_mapping.dtype == torch.int32 and slot_mapping.shape == (k.shape[0],),
+          "slot_mapping must be int32 [T]")
+    _need(k.dtype == v.dtype == k_cache.dtype == v_cache.dtype, "dtypes must match")
+    nb, bs, hkv, d = k_cache.shape
+    _check(lib().pkv_kv_cache_store(_ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache),
+                                    _ptr(slot_mapping), k.shape[0], nb, bs, hkv, d,
+                                    _dtype_code(k), _stream(stream)))
+
+
+def decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len, partition_size):
+    return int(lib().pkv_decode_workspace_size(num_seqs, num_q_heads, head_dim,
+                                               max_context_len, partition_size))
+
+
+def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                           max_context_len, partition_size=0, workspace=None, algo="auto",
+                           stream=None):
+    """One query row per sequence over its paged context; writes out [S, Hq, D].
+
+    max_context_len is a host-side bound on context_lens (it sizes the grid).
+    With partition_size > 0 the split-K workspace is taken from `workspace`
+    (a uint8 device tensor) or allocated here through torch when omitted.
+    """
+    _dev(out, q, k_cache, v_cache, block_tables, context_lens)
+    _need(q.dim() == 3 and out.shape == q.shape and out.dtype == q.dtype, "q/out must be [S, Hq, D]")
+    _need(k_cache.dim() == 4 and v_cache.shape == k_cache.shape, "caches must be [NB, bs, Hkv, D]")
+    _need(q.dtype == k_cache.dtype == v_cache.dtype, "dtypes must match")
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
+          and block_tables.shape[0] == q.shape[0], "block_tables must be int32 [S, MB]")
+    _need(context_lens.dtype == torch.int32 and context_lens.shape == (q.shape[0],),
+          "context_lens must be int32 [S]")
+    _need(k_cache.shape[3] == q.shape[2], "head_dim mismatch")
+    s, hq, d = q.shape
+    nb, bs, hkv, _ = k_cache.shape
+    need = decode_workspace_size(s, hq, d, max_context_len, partition_size) if partition_size else 0
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().pkv_paged_attention_decode(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+        s, block_tables.shape[1], int(max_context_len), nb, bs, hq, hkv, d, float(scale),
+        int(partition_size), _ptr(workspace), ws_bytes, _dtype_code(q), DECODE_ALGOS[algo],
+        _stream(stream)))
+    return out
+
+
+def paged_attention_prefill_chunk(out, q, k_cache, v_cache, block_tables, cu_seqlens_q,
+                                  context_lens, scale, max_q_len, max_context_len, causal=True,
+                                  stream=None):
+    """Packed query chunks over their paged contexts; writes out [Tq, Hq, D]."""
+    _dev(out, q, k_cache, v_cache, block_tables, cu_seqlens_q, context_lens)
+    _need(q.dim() == 3 and out.shape == q.shape and out.dtype == q.dtype, "q/out must be [Tq, Hq, D]")
+    _need(k_cache.dim() == 4 and v_cache.shape == k_cache.shape, "caches must be [NB, bs, Hkv, D]")
+    _need(q.dtype == k_cache.dtype == v_cache.dtype, "dtypes must match")
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2, "block_tables must be int32")
+    n = block_tables.shape[0]
+    _need(cu_seqlens_q.dtype == torch.int32 and cu_seqlens_q.shape == (n + 1,),
+          "cu_seqlens_q must be int32 [S+1]")
+    _need(context_lens.dtype == torch.int32 and context_lens.shape == (n,),
+          "context_lens must be int32 [S]")
+    tq, hq, d = q.shape
+    nb, bs, hkv, _ = k_cache.shape
+    _check(lib().pkv_paged_attention_prefill_chunk(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(cu_seqlens_q),
+        _ptr(context_lens), n, tq, int(max_q_len), block_tables.shape[1], int(max_context_len),
+        nb, bs, hq, hkv, d, float(scale), int(bool(causal)), _dtype_code(q), _stream(stream)))
+    return out

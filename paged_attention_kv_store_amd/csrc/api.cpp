@@ -1,0 +1,252 @@
+// C ABI of the library: argument validation, launch configuration, dispatch.
+// The contract of every entry point is documented in include/pkv.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "common.h"
+#include "pkv.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return PKV_OK;
+  return fail(PKV_EHIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int elt_size(int dt) { return dt == PKV_F32 ? 4 : dt == PKV_BF16 ? 2 : 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Partitions per (sequence, kv-head) and the tokens in each; single pass
+// (partition_size 0) is one partition spanning the longest context.
+void partitioning(int32_t max_ctx, int32_t partition_size, int32_t* part, int64_t* nparts) {
+  if (partition_size == 0) {
+    *part = (int32_t)(ceil_div(max_ctx > 16 ? max_ctx : 16, 16) * 16);
+    *nparts = 1;
+  } else {
+    *part = partition_size;
+    *nparts = max_ctx > 0 ? ceil_div(max_ctx, partition_size) : 1;
+  }
+}
+
+int check_common(const char* fn, int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                 int32_t head_dim, int dtype) {
+  if (elt_size(dtype) == 0) return fail(PKV_EINVAL, "%s: unknown dtype %d", fn, dtype);
+  if (num_blocks <= 0 || block_size <= 0 || num_kv_heads <= 0 || head_dim <= 0)
+    return fail(PKV_EINVAL, "%s: num_blocks, block_size, num_kv_heads and head_dim must be positive", fn);
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" int pkv_version(void) { return 100; }
+
+extern "C" const char* pkv_last_error(void) { return g_last_error.c_str(); }
+
+extern "C" int pkv_kv_cache_store(const void* k, const void* v, void* k_cache, void* v_cache,
+                                  const int32_t* slot_mapping, int32_t num_tokens,
+                                  int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                                  int32_t head_dim, pkv_dtype dtype, void* stream) {
+  const char* fn = "pkv_kv_cache_store";
+  if (num_tokens < 0) return fail(PKV_EINVAL, "%s: num_tokens < 0", fn);
+  if (int rc = check_common(fn, num_blocks, block_size, num_kv_heads, head_dim, dtype)) return rc;
+  const int64_t row_bytes = (int64_t)num_kv_heads * head_dim * elt_size(dtype);
+  if (row_bytes % 16 != 0)
+    return fail(PKV_EUNSUPPORTED, "%s: a token row (%lld bytes) must be a multiple of 16 bytes", fn,
+                (long long)row_bytes);
+  if (num_tokens == 0) return PKV_OK;
+  if (!k || !v || !k_cache || !v_cache || !slot_mapping)
+    return fail(PKV_EINVAL, "%s: null pointer", fn);
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(slot_mapping, 4))
+    return fail(PKV_EINVAL, "%s: K/V pointers must be 16-byte aligned, slots 4-byte aligned", fn);
+  pkv::StoreParams p;
+  p.k = k;
+  p.v = v;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.slot_mapping = slot_mapping;
+  p.num_tokens = num_tokens;
+  p.num_slots = (int64_t)num_blocks * block_size;
+  p.row_vec16 = (int32_t)(row_bytes / 16);
+  return hip_status(pkv::launch_store(p, (hipStream_t)stream), fn);
+}
+
+extern "C" size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                            int32_t max_context_len, int32_t partition_size) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0 || partition_size <= 0)
+    return 0;
+  int32_t part;
+  int64_t nparts;
+  partitioning(max_context_len, partition_size, &part, &nparts);
+  if (nparts <= 1) return 0;
+  return (size_t)num_seqs * num_q_heads * nparts * (head_dim + 2) * sizeof(float);
+}
+
+extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
+                                          const void* v_cache, const int32_t* block_tables,
+                                          const int32_t* context_lens, int32_t num_seqs,
+                                          int32_t max_blocks_per_seq, int32_t max_context_len,
+                                          int32_t num_blocks, int32_t block_size,
+                                          int32_t num_q_heads, int32_t num_kv_heads,
+                                          int32_t head_dim, float scale, int32_t partition_size,
+                                          void* workspace, size_t workspace_bytes,
+                                          pkv_dtype dtype, int32_t algo, void* stream) {
+  const char* fn = "pkv_paged_attention_decode";
+  if (num_seqs < 0) return fail(PKV_EINVAL, "%s: num_seqs < 0", fn);
+  if (int rc = check_common(fn, num_blocks, block_size, num_kv_heads, head_dim, dtype)) return rc;
+  if (num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return fail(PKV_EINVAL, "%s: num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)", fn,
+                num_q_heads, num_kv_heads);
+  const int group = num_q_heads / num_kv_heads;
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_EUNSUPPORTED, "%s: head_dim %d not in {64, 128}", fn, head_dim);
+  if (block_size % 16 != 0 || block_size > 256)
+    return fail(PKV_EUNSUPPORTED, "%s: block_size %d must be a multiple of 16 up to 256", fn, block_size);
+  if (max_blocks_per_seq <= 0) return fail(PKV_EINVAL, "%s: max_blocks_per_seq must be positive", fn);
+  if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
+    return fail(PKV_EINVAL, "%s: max_context_len %d outside [0, max_blocks_per_seq * block_size = %lld]", fn,
+                max_context_len, (long long)max_blocks_per_seq * block_size);
+  if (partition_size < 0 || partition_size % 16 != 0)
+    return fail(PKV_EINVAL, "%s: partition_size %d must be 0 or a positive multiple of 16", fn,
+                partition_size);
+  if (!std::isfinite(scale)) return fail(PKV_EINVAL, "%s: scale is not finite", fn);
+  if (algo == PKV_DECODE_AUTO) algo = dtype == PKV_BF16 ? PKV_DECODE_MFMA : PKV_DECODE_VALU;
+  if (algo == PKV_DECODE_MFMA) {
+    if (dtype != PKV_BF16) return fail(PKV_EUNSUPPORTED, "%s: the MFMA kernel needs bf16", fn);
+    if (group > 16) return fail(PKV_EUNSUPPORTED, "%s: GQA group %d > 16", fn, group);
+  } else if (algo == PKV_DECODE_VALU) {
+    if (group > 8) return fail(PKV_EUNSUPPORTED, "%s: the VALU kernel supports GQA groups up to 8", fn);
+  } else {
+    return fail(PKV_EINVAL, "%s: unknown algo %d", fn, algo);
+  }
+  if (num_seqs > 65535 || num_kv_heads > 65535)
+    return fail(PKV_EUNSUPPORTED, "%s: num_seqs and num_kv_heads are limited to 65535", fn);
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PKV_EINVAL, "%s: null pointer", fn);
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 4) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4))
+    return fail(PKV_EINVAL, "%s: q and caches must be 16-byte aligned; out and index arrays 4-byte", fn);
+
+  int32_t part;
+  int64_t nparts;
+  partitioning(max_context_len, partition_size, &part, &nparts);
+  if (nparts > 0x7fffffff) return fail(PKV_EUNSUPPORTED, "%s: too many partitions", fn);
+  pkv::DecodeParams p;
+  p.out = out;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.num_seqs = num_seqs;
+  p.max_blocks = max_blocks_per_seq;
+  p.num_blocks = num_blocks;
+  p.block_size = block_size;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.group = group;
+  p.scale_log2 = scale * pkv::kLog2e;
+  p.max_ctx = max_context_len;
+  p.partition_size = part;
+  p.num_partitions = (int32_t)nparts;
+  p.ws_m = p.ws_l = p.ws_o = nullptr;
+  if (nparts > 1) {
+    const size_t need = pkv_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len,
+                                                  partition_size);
+    if (!workspace || workspace_bytes < need)
+      return fail(PKV_EWORKSPACE, "%s: split-K needs %zu workspace bytes, got %zu", fn, need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 16)) return fail(PKV_EINVAL, "%s: workspace must be 16-byte aligned", fn);
+    const int64_t cells = (int64_t)num_seqs * num_q_heads * nparts;
+    float* ws = reinterpret_cast<float*>(workspace);
+    p.ws_m = ws;
+    p.ws_l = ws + cells;
+    p.ws_o = ws + 2 * cells;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = algo == PKV_DECODE_MFMA ? pkv::launch_decode_mfma(p, head_dim, st)
+                                         : pkv::launch_decode_valu(p, head_dim, dtype, st);
+  if (e != hipSuccess) return hip_status(e, fn);
+  if (nparts > 1) return hip_status(pkv::launch_splitk_reduce(p, head_dim, dtype, st), fn);
+  return PKV_OK;
+}
+
+extern "C" int pkv_paged_attention_prefill_chunk(void* out, const void* q, const void* k_cache,
+                                                 const void* v_cache, const int32_t* block_tables,
+                                                 const int32_t* cu_seqlens_q,
+                                                 const int32_t* context_lens, int32_t num_seqs,
+                                                 int32_t total_q, int32_t max_q_len,
+                                                 int32_t max_blocks_per_seq, int32_t max_context_len,
+                                                 int32_t num_blocks, int32_t block_size,
+                                                 int32_t num_q_heads, int32_t num_kv_heads,
+                                                 int32_t head_dim, float scale, int32_t causal,
+                                                 pkv_dtype dtype, void* stream) {
+  const char* fn = "pkv_paged_attention_prefill_chunk";
+  if (num_seqs < 0 || total_q < 0 || max_q_len < 0)
+    return fail(PKV_EINVAL, "%s: negative size", fn);
+  if (int rc = check_common(fn, num_blocks, block_size, num_kv_heads, head_dim, dtype)) return rc;
+  if (num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return fail(PKV_EINVAL, "%s: num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)", fn,
+                num_q_heads, num_kv_heads);
+  const int group = num_q_heads / num_kv_heads;
+  if (dtype != PKV_BF16) return fail(PKV_EUNSUPPORTED, "%s: prefill supports bf16 only", fn);
+  if (head_dim != 128) return fail(PKV_EUNSUPPORTED, "%s: prefill supports head_dim 128 only", fn);
+  if (group != 1 && group != 2 && group != 4 && group != 8)
+    return fail(PKV_EUNSUPPORTED, "%s: GQA group %d not in {1, 2, 4, 8}", fn, group);
+  if (block_size % 16 != 0 || block_size > 256)
+    return fail(PKV_EUNSUPPORTED, "%s: block_size %d must be a multiple of 16 up to 256", fn, block_size);
+  if (max_blocks_per_seq <= 0) return fail(PKV_EINVAL, "%s: max_blocks_per_seq must be positive", fn);
+  if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
+    return fail(PKV_EINVAL, "%s: max_context_len outside [0, max_blocks_per_seq * block_size]", fn);
+  if (max_q_len > max_context_len) return fail(PKV_EINVAL, "%s: max_q_len exceeds max_context_len", fn);
+  if (!std::isfinite(scale)) return fail(PKV_EINVAL, "%s: scale is not finite", fn);
+  if (num_seqs > 65535 || num_kv_heads > 65535)
+    return fail(PKV_EUNSUPPORTED, "%s: num_seqs and num_kv_heads are limited to 65535", fn);
+  if (num_seqs == 0 || total_q == 0 || max_q_len == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !cu_seqlens_q || !context_lens)
+    return fail(PKV_EINVAL, "%s: null pointer", fn);
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(cu_seqlens_q, 4))
+    return fail(PKV_EINVAL, "%s: q, out and caches must be 16-byte aligned; index arrays 4-byte", fn);
+  pkv::PrefillParams p;
+  p.out = out;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_tables = block_tables;
+  p.cu_seqlens_q = cu_seqlens_q;
+  p.context_lens = context_lens;
+  p.num_seqs = num_seqs;
+  p.max_q_len = max_q_len;
+  p.max_blocks = max_blocks_per_seq;
+  p.num_blocks = num_blocks;
+  p.block_size = block_size;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.group = group;
+  p.max_ctx = max_context_len;
+  p.scale_log2 = scale * pkv::kLog2e;
+  p.causal = causal != 0;
+  return hip_status(pkv::launch_prefill(p, head_dim, (hipStream_t)stream), fn);
+}

@@ -1,0 +1,82 @@
+// Shared declarations of the HIP kernels' launchers and small device helpers.
+// Internal to the library: the public interface is include/pkv.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// log2(e): softmax runs in base 2 (v_exp_f32 computes 2^x), so logits are
+// pre-multiplied by scale * log2(e); exp(a - b) == exp2(log2e*a - log2e*b).
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Lazy rescaling threshold, in log2 units. The running max used as the
+// softmax reference is raised only when a new logit exceeds it by more than
+// this, so exp2(logit - reference) <= 2^8 and the fp32 sums stay far from
+// overflow; the final division by the sum removes the reference exactly.
+constexpr float kRescaleThreshold = 8.0f;
+
+struct StoreParams {
+  const void* k;
+  const void* v;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* slot_mapping;
+  int32_t num_tokens;
+  int64_t num_slots;     // num_blocks * block_size
+  int32_t row_vec16;     // bytes of one token row (kv_heads * head_dim * elt) / 16
+};
+
+struct DecodeParams {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int32_t num_seqs;
+  int32_t max_blocks;        // block table row length
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;             // num_q_heads / num_kv_heads
+  float scale_log2;          // scale * log2(e)
+  int32_t max_ctx;           // host bound; a larger device length is truncated to it
+  int32_t partition_size;    // tokens per partition (single pass: >= max context)
+  int32_t num_partitions;    // partitions per (sequence, kv-head) in the grid
+  float* ws_m;               // [num_seqs, num_q_heads, num_partitions]
+  float* ws_l;               // same
+  float* ws_o;               // [num_seqs, num_q_heads, num_partitions, head_dim]
+};
+
+struct PrefillParams {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* cu_seqlens_q;
+  const int32_t* context_lens;
+  int32_t num_seqs;
+  int32_t max_q_len;
+  int32_t max_blocks;
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;
+  int32_t max_ctx;
+  float scale_log2;
+  int32_t causal;
+};
+
+// dtype codes match pkv_dtype
+hipError_t launch_store(const StoreParams& p, hipStream_t stream);
+hipError_t launch_decode_valu(const DecodeParams& p, int head_dim, int dtype, hipStream_t stream);
+hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_splitk_reduce(const DecodeParams& p, int head_dim, int dtype, hipStream_t stream);
+hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t stream);
+
+}  // namespace pkv

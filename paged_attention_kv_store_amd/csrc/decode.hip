@@ -1,0 +1,505 @@
+// Decode attention over a paged KV cache: one query row per (sequence, q-head).
+//
+// Work unit: one workgroup of 4 wavefronts per (partition, kv-head, sequence).
+// It serves all G = Hq/Hkv q-heads that share the kv-head, so each K/V byte is
+// read once for the whole group. The partition's tokens are cut into 16-token
+// tiles; wave w takes tiles w, w+4, w+8, ... Every tile lies inside one
+// physical block (block_size is a multiple of 16 and tiles start at multiples
+// of 16), so one block-table entry gives the tile's 16 cache rows. Each wave
+// keeps an online-softmax state (reference max in log2 units, sum, fp32
+// output accumulator); the four states are merged through LDS at the end.
+// A partition that is the sequence's only one writes the normalised output;
+// otherwise it writes (max, sum, unnormalised output) to the split-K
+// workspace and splitk_reduce_kernel merges the partitions.
+//
+// Two kernel families compute the same thing:
+//  * decode_valu_kernel: lanes split a cache row into 16-byte pieces; q.k dot
+//    products are vector FMAs finished by xor-shuffle sums across the lanes of
+//    a row; P.V is vector FMAs. Any dtype, G <= 8.
+//  * decode_mfma_kernel (bf16): q.k for the 16 tile tokens x the G heads is a
+//    16x16x32 bf16 matrix-core product per 32 dims of head_dim (the G heads
+//    are padded to 16 columns); P.V is 16x16x4 fp32 matrix-core steps whose
+//    B operand is V read in plain row order (4 tokens x 16 column groups), so
+//    no transposition of V is needed and P stays in fp32.
+#include "common.h"
+#include "device_utils.h"
+
+namespace pkv {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTile = 16;
+
+template <typename T>
+__device__ __forceinline__ void store_out(void* out, int64_t idx, float v);
+template <>
+__device__ __forceinline__ void store_out<float>(void* out, int64_t idx, float v) {
+  reinterpret_cast<float*>(out)[idx] = v;
+}
+template <>
+__device__ __forceinline__ void store_out<uint16_t>(void* out, int64_t idx, float v) {
+  reinterpret_cast<uint16_t*>(out)[idx] = f32_to_bf16_rne(v);
+}
+
+// Rows of q-heads g*G .. g*G+G-1 of sequence s set to zero (empty context).
+template <typename T, int D>
+__device__ void write_zero_rows(const DecodeParams& p, int s, int g) {
+  const int G = p.group;
+  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+    const int h = idx / D, d = idx - h * D;
+    store_out<T>(p.out, ((int64_t)s * p.num_q_heads + g * G + h) * D + d, 0.f);
+  }
+}
+
+// Merge the per-wave softmax states held in LDS and write either the final
+// output (single partition) or this partition's split-K partials.
+//   s_m[w*16 + h], s_l[w*16 + h]: wave w's reference max (log2) and sum
+//   s_o[(w*GP + h)*D + d]: wave w's unnormalised output
+template <typename T, int D, int GP>
+__device__ void merge_and_write(const DecodeParams& p, int s, int g, int part, int n_parts,
+                                const float* s_m, const float* s_l, const float* s_o,
+                                bool poisoned) {
+  const int G = p.group;
+  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+    const int h = idx / D, d = idx - h * D;
+    float M = neg_inf();
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w * 16 + h]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = s_m[w * 16 + h];
+      const float f = (mw == neg_inf()) ? 0.f : fast_exp2(mw - M);
+      L += s_l[w * 16 + h] * f;
+      O += s_o[(w * GP + h) * D + d] * f;
+    }
+    if (poisoned) L = __builtin_nanf("");
+    const int qh = g * G + h;
+    if (n_parts <= 1) {
+      store_out<T>(p.out, ((int64_t)s * p.num_q_heads + qh) * D + d, O / L);
+    } else {
+      const int64_t base = ((int64_t)s * p.num_q_heads + qh) * p.num_partitions + part;
+      p.ws_o[base * D + d] = O;
+      if (d == 0) {
+        p.ws_m[base] = M;
+        p.ws_l[base] = L;
+      }
+    }
+  }
+}
+
+// Context length as read from device memory, kept inside [0, max_ctx]: the
+// grid, the block-table row and the split-K workspace are sized by the host
+// bound, so a longer (invalid) length must not index past them.
+__device__ __forceinline__ int clamp_ctx(int ctx, int max_ctx) { return min(max(ctx, 0), max_ctx); }
+
+// Physical block of the tile starting at logical position tok0; an entry
+// outside the pool is replaced by block 0 and flags the result as invalid.
+__device__ __forceinline__ int64_t tile_row0(const int32_t* bt, int tok0, int bs, int num_blocks,
+                                             bool& poisoned) {
+  const int lb = tok0 / bs;
+  int blk = bt[lb];
+  if ((unsigned)blk >= (unsigned)num_blocks) {
+    blk = 0;
+    poisoned = true;
+  }
+  return (int64_t)blk * bs + (tok0 - lb * bs);
+}
+
+// ---------------------------------------------------------------------------
+// Vector-ALU decode
+// ---------------------------------------------------------------------------
+template <typename T>
+struct Widen;
+template <>
+struct Widen<float> {
+  static constexpr int kEPL = 4;
+  __device__ static void run(const uint4& v, float* f) {
+    f[0] = __uint_as_float(v.x);
+    f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z);
+    f[3] = __uint_as_float(v.w);
+  }
+};
+template <>
+struct Widen<uint16_t> {
+  static constexpr int kEPL = 8;
+  __device__ static void run(const uint4& v, float* f) {
+    f[0] = bf16_lo(v.x);
+    f[1] = bf16_hi(v.x);
+    f[2] = bf16_lo(v.y);
+    f[3] = bf16_hi(v.y);
+    f[4] = bf16_lo(v.z);
+    f[5] = bf16_hi(v.z);
+    f[6] = bf16_lo(v.w);
+    f[7] = bf16_hi(v.w);
+  }
+};
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
+  constexpr int EPL = Widen<T>::kEPL;   // elements per 16-byte lane piece
+  constexpr int LPR = D / EPL;          // lanes covering one cache row
+  constexpr int RPI = 64 / LPR;         // rows per wave-wide load
+  constexpr int LOADS = kTile / RPI;    // loads per 16-token tile
+  static_assert(LPR >= 2 && LPR <= 64 && 64 % LPR == 0 && kTile % RPI == 0, "bad shape");
+
+  __shared__ float s_m[kWaves * 16], s_l[kWaves * 16];
+  __shared__ float s_o[kWaves * G * D];
+
+  const int part = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = lane % LPR, rg = lane / LPR;
+  const int ctx = clamp_ctx(p.context_lens[s], p.max_ctx);
+  const int P = p.partition_size;
+  const int t0 = part * P;
+  if (t0 >= ctx) {
+    if (part == 0) write_zero_rows<T, D>(p, s, g);
+    return;
+  }
+  const int n_parts = (ctx + P - 1) / P;
+  const int t1 = min(ctx, t0 + P);
+  const int n_tiles = (t1 - t0 + kTile - 1) / kTile;
+  const int64_t row_elems = (int64_t)p.num_kv_heads * D;
+  const int bs = p.block_size;
+
+  float qf[G][EPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const T* qrow = reinterpret_cast<const T*>(p.q) + ((int64_t)s * p.num_q_heads + g * G + h) * D;
+    Widen<T>::run(load16(qrow + c * EPL), qf[h]);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qf[h][e] *= p.scale_log2;
+  }
+
+  const T* kc = reinterpret_cast<const T*>(p.k_cache) + g * D + c * EPL;
+  const T* vc = reinterpret_cast<const T*>(p.v_cache) + g * D + c * EPL;
+  const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks;
+
+  float m_ref[G], l_part[G], acc[G][EPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m_ref[h] = neg_inf();
+    l_part[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+  }
+  bool poisoned = false;
+
+  for (int it = w; it < n_tiles; it += kWaves) {
+    const int tok0 = t0 + it * kTile;
+    const int64_t row0 = tile_row0(bt, tok0, bs, p.num_blocks, poisoned);
+    uint4 kr[LOADS], vr[LOADS];
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) kr[i] = load16(kc + (row0 + rg + RPI * i) * row_elems);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) vr[i] = load16(vc + (row0 + rg + RPI * i) * row_elems);
+
+    float x[LOADS][G];
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      float kf[EPL];
+      Widen<T>::run(kr[i], kf);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float a = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) a = fmaf(qf[h][e], kf[e], a);
+#pragma unroll
+        for (int m = 1; m < LPR; m <<= 1) a += shfl_xor_f(a, m);
+        x[i][h] = (tok0 + rg + RPI * i < t1) ? a : neg_inf();
+      }
+    }
+    bool grow = false;
+    float mt[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float v = x[0][h];
+#pragma unroll
+      for (int i = 1; i < LOADS; ++i) v = fmaxf(v, x[i][h]);
+#pragma unroll
+      for (int m = LPR; m < 64; m <<= 1) v = fmaxf(v, shfl_xor_f(v, m));
+      mt[h] = v;
+      grow |= v > m_ref[h] + kRescaleThreshold;
+    }
+    if (__any(grow)) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float m_new = fmaxf(m_ref[h], mt[h]);
+        const float alpha = fast_exp2(m_ref[h] - m_new);
+        l_part[h] *= alpha;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
+        m_ref[h] = m_new;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      float vf[EPL];
+      Widen<T>::run(vr[i], vf);
+      const bool live = tok0 + rg + RPI * i < t1;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) vf[e] = live ? vf[e] : 0.f;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float pr = fast_exp2(x[i][h] - m_ref[h]);
+        l_part[h] += pr;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pr, vf[e], acc[h][e]);
+      }
+    }
+  }
+
+  // fold the row groups of the wave together
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+#pragma unroll
+    for (int m = LPR; m < 64; m <<= 1) {
+      l_part[h] += shfl_xor_f(l_part[h], m);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] += shfl_xor_f(acc[h][e], m);
+    }
+  }
+  if (lane < LPR) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s_o[(w * G + h) * D + c * EPL + e] = acc[h][e];
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      s_m[w * 16 + h] = m_ref[h];
+      s_l[w * 16 + h] = l_part[h];
+    }
+  }
+  poisoned = __any(poisoned);
+  __shared__ int s_poison;
+  if (threadIdx.x == 0) s_poison = 0;
+  __syncthreads();
+  if (poisoned && lane == 0) s_poison = 1;
+  __syncthreads();
+  merge_and_write<T, D, G>(p, s, g, part, n_parts, s_m, s_l, s_o, s_poison != 0);
+}
+
+// ---------------------------------------------------------------------------
+// Matrix-core decode (bf16)
+// ---------------------------------------------------------------------------
+template <int D, int GP>
+__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
+  constexpr int KCH = D / 32;   // 16x16x32 steps over head_dim = 16-byte K pieces per lane
+  constexpr int EPL = D / 16;   // V elements per lane per row (16 lanes cover a row)
+
+  __shared__ float s_m[kWaves * 16], s_l[kWaves * 16];
+  __shared__ float s_o[kWaves * GP * D];
+  __shared__ int s_poison;
+
+  const int part = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int n = lane & 15, qg = lane >> 4;
+  const int G = p.group;
+  const int ctx = clamp_ctx(p.context_lens[s], p.max_ctx);
+  const int P = p.partition_size;
+  const int t0 = part * P;
+  if (t0 >= ctx) {
+    if (part == 0) write_zero_rows<uint16_t, D>(p, s, g);
+    return;
+  }
+  const int n_parts = (ctx + P - 1) / P;
+  const int t1 = min(ctx, t0 + P);
+  const int n_tiles = (t1 - t0 + kTile - 1) / kTile;
+  const int64_t row_elems = (int64_t)p.num_kv_heads * D;
+  const int bs = p.block_size;
+
+  // B operand of q.k^T: column n is q-head g*G+n (zero past the group); lane
+  // group qg holds head_dim elements [qg*D/4, (qg+1)*D/4) as KCH pieces of 8.
+  // The K operand uses the same element order, so the contraction pairs
+  // matching elements whatever order the hardware sums them in.
+  bf16x8_t qb[KCH];
+  {
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) +
+                           ((int64_t)s * p.num_q_heads + g * G + n) * D + qg * (D / 4);
+#pragma unroll
+    for (int j = 0; j < KCH; ++j) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (n < G) v = load16(qrow + 8 * j);
+      qb[j] = bit_cast_to<bf16x8_t>(v);
+    }
+  }
+
+  const uint16_t* kc = reinterpret_cast<const uint16_t*>(p.k_cache) + g * D + qg * (D / 4);
+  const uint16_t* vc = reinterpret_cast<const uint16_t*>(p.v_cache) + g * D + EPL * n;
+  const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks;
+
+  float m_ref = neg_inf();   // reference max of head n (replicated over qg)
+  float l_part = 0.f;        // sum over this lane's tokens for head n
+  f32x4_t acc[EPL];          // O[head 4*qg + r][EPL*n + e] in acc[e][r]
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  bool poisoned = false;
+
+  for (int it = w; it < n_tiles; it += kWaves) {
+    const int tok0 = t0 + it * kTile;
+    const int64_t row0 = tile_row0(bt, tok0, bs, p.num_blocks, poisoned);
+    // K: lane reads token row0+n, its D/4-element slice
+    uint4 kr[KCH];
+    const uint16_t* kp = kc + (row0 + n) * row_elems;
+#pragma unroll
+    for (int j = 0; j < KCH; ++j) kr[j] = load16(kp + 8 * j);
+    // V: step st reads token row0 + 4*qg + st, elements [EPL*n, EPL*n + EPL)
+    uint4 vr[4];
+    const uint16_t* vp = vc + (row0 + 4 * qg) * row_elems;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      if constexpr (EPL == 8) {
+        vr[st] = load16(vp + st * row_elems);
+      } else {
+        const uint2 h = load8(vp + st * row_elems);
+        vr[st] = make_uint4(h.x, h.y, 0, 0);
+      }
+    }
+
+    // S[token 4*qg + r][head n] in sc[r]
+    f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < KCH; ++j)
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bit_cast_to<bf16x8_t>(kr[j]), qb[j], sc, 0, 0, 0);
+
+    const int tokq = tok0 + 4 * qg;
+    float x[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x[r] = (tokq + r < t1) ? sc[r] * p.scale_log2 : neg_inf();
+    float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    mt = fmaxf(mt, shfl_xor_f(mt, 16));
+    mt = fmaxf(mt, shfl_xor_f(mt, 32));
+    if (__any(mt > m_ref + kRescaleThreshold)) {
+      const float m_new = fmaxf(m_ref, mt);
+      const float alpha = fast_exp2(m_ref - m_new);
+      l_part *= alpha;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float a = __shfl(alpha, 4 * qg + r, 64);   // factor of head 4*qg + r
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e][r] *= a;
+      }
+      m_ref = m_new;
+    }
+    float pr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(x[r] - m_ref);
+    l_part += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+
+    // O[h][d] += sum over the 4 tokens of step st: P[h][token] * V[token][d]
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      float vf[8];
+      Widen<uint16_t>::run(vr[st], vf);
+      const bool live = tokq + st < t1;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const float b = live ? vf[e] : 0.f;
+        acc[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(pr[st], b, acc[e], 0, 0, 0);
+      }
+    }
+  }
+
+  l_part += shfl_xor_f(l_part, 16);
+  l_part += shfl_xor_f(l_part, 32);
+  if (lane < 16) {
+    s_m[w * 16 + lane] = m_ref;
+    s_l[w * 16 + lane] = l_part;
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int h = 4 * qg + r;
+    if (h < G) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s_o[(w * GP + h) * D + EPL * n + e] = acc[e][r];
+    }
+  }
+  poisoned = __any(poisoned);
+  if (threadIdx.x == 0) s_poison = 0;
+  __syncthreads();
+  if (poisoned && lane == 0) s_poison = 1;
+  __syncthreads();
+  merge_and_write<uint16_t, D, GP>(p, s, g, part, n_parts, s_m, s_l, s_o, s_poison != 0);
+}
+
+// ---------------------------------------------------------------------------
+// Split-K merge: out = sum_k 2^(m_k - M) o_k / sum_k 2^(m_k - M) l_k
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(D) void splitk_reduce_kernel(DecodeParams p) {
+  const int h = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
+  const int ctx = clamp_ctx(p.context_lens[s], p.max_ctx);
+  const int P = p.partition_size;
+  const int n = (ctx + P - 1) / P;
+  if (n <= 1) return;   // written directly by the partition pass
+  const int64_t base = ((int64_t)s * p.num_q_heads + h) * p.num_partitions;
+  float M = neg_inf();
+  for (int k = 0; k < n; ++k) M = fmaxf(M, p.ws_m[base + k]);
+  float L = 0.f, O = 0.f;
+  for (int k = 0; k < n; ++k) {
+    const float f = fast_exp2(p.ws_m[base + k] - M);
+    L += p.ws_l[base + k] * f;
+    O += p.ws_o[(base + k) * D + d] * f;
+  }
+  store_out<T>(p.out, ((int64_t)s * p.num_q_heads + h) * D + d, O / L);
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+static hipError_t launch_valu_g(const DecodeParams& p, hipStream_t stream) {
+  const dim3 grid(p.num_partitions, p.num_kv_heads, p.num_seqs);
+  switch (p.group) {
+#define PKV_G(GV) \
+  case GV: hipLaunchKernelGGL((decode_valu_kernel<T, D, GV>), grid, dim3(kThreads), 0, stream, p); break;
+    PKV_G(1) PKV_G(2) PKV_G(3) PKV_G(4) PKV_G(5) PKV_G(6) PKV_G(7) PKV_G(8)
+#undef PKV_G
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_valu(const DecodeParams& p, int head_dim, int dtype, hipStream_t stream) {
+  if (dtype == 0) return head_dim == 64 ? launch_valu_g<float, 64>(p, stream) : launch_valu_g<float, 128>(p, stream);
+  return head_dim == 64 ? launch_valu_g<uint16_t, 64>(p, stream) : launch_valu_g<uint16_t, 128>(p, stream);
+}
+
+template <int D>
+static hipError_t launch_mfma_d(const DecodeParams& p, hipStream_t stream) {
+  const dim3 grid(p.num_partitions, p.num_kv_heads, p.num_seqs);
+  if (p.group <= 4)
+    hipLaunchKernelGGL((decode_mfma_kernel<D, 4>), grid, dim3(kThreads), 0, stream, p);
+  else if (p.group <= 8)
+    hipLaunchKernelGGL((decode_mfma_kernel<D, 8>), grid, dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_mfma_kernel<D, 16>), grid, dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, hipStream_t stream) {
+  return head_dim == 64 ? launch_mfma_d<64>(p, stream) : launch_mfma_d<128>(p, stream);
+}
+
+hipError_t launch_splitk_reduce(const DecodeParams& p, int head_dim, int dtype, hipStream_t stream) {
+  const dim3 grid(p.num_q_heads, p.num_seqs);
+  if (dtype == 0) {
+    if (head_dim == 64)
+      hipLaunchKernelGGL((splitk_reduce_kernel<float, 64>), grid, dim3(64), 0, stream, p);
+    else
+      hipLaunchKernelGGL((splitk_reduce_kernel<float, 128>), grid, dim3(128), 0, stream, p);
+  } else {
+    if (head_dim == 64)
+      hipLaunchKernelGGL((splitk_reduce_kernel<uint16_t, 64>), grid, dim3(64), 0, stream, p);
+    else
+      hipLaunchKernelGGL((splitk_reduce_kernel<uint16_t, 128>), grid, dim3(128), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -1,0 +1,158 @@
+"""The C-ABI library loads, exports every symbol include/pkv.h declares, and
+rejects invalid arguments on the host before launching anything (CPU only:
+no call here reaches a kernel)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_attention_kv_store_amd as pkv
+from paged_attention_kv_store_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(pkv.library_path()),
+                               reason="libpkv.so not built")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_symbols() == binding.exported_symbols()
+
+
+@needs_lib
+def test_library_exports_every_declared_symbol():
+    lib = pkv.lib()
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    assert lib.pkv_version() >= 100
+
+
+def _decode(lib, **over):
+    args = dict(out=1024, q=1024, k=1024, v=1024, bt=1024, cl=1024, S=4, MB=16, max_ctx=256,
+                NB=64, bs=16, Hq=8, Hkv=4, D=64, scale=0.125, part=0, ws=None, ws_bytes=0,
+                dtype=0, algo=0, stream=None)
+    args.update(over)
+    a = args
+    return lib.pkv_paged_attention_decode(a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"],
+                                          a["S"], a["MB"], a["max_ctx"], a["NB"], a["bs"],
+                                          a["Hq"], a["Hkv"], a["D"], a["scale"], a["part"],
+                                          a["ws"], a["ws_bytes"], a["dtype"], a["algo"],
+                                          a["stream"])
+
+
+@needs_lib
+@pytest.mark.parametrize("over,code", [
+    (dict(S=-1), binding.PKV_EINVAL),
+    (dict(Hq=6, Hkv=4), binding.PKV_EINVAL),
+    (dict(Hkv=0), binding.PKV_EINVAL),
+    (dict(D=96), binding.PKV_EUNSUPPORTED),
+    (dict(bs=8), binding.PKV_EUNSUPPORTED),
+    (dict(bs=512), binding.PKV_EUNSUPPORTED),
+    (dict(dtype=7), binding.PKV_EINVAL),
+    (dict(max_ctx=257), binding.PKV_EINVAL),
+    (dict(part=24), binding.PKV_EINVAL),
+    (dict(part=-16), binding.PKV_EINVAL),
+    (dict(part=64), binding.PKV_EWORKSPACE),
+    (dict(part=64, ws=1024, ws_bytes=100), binding.PKV_EWORKSPACE),
+    (dict(algo=2, dtype=0), binding.PKV_EUNSUPPORTED),
+    (dict(algo=9), binding.PKV_EINVAL),
+    (dict(Hq=36, Hkv=2, algo=1, dtype=1), binding.PKV_EUNSUPPORTED),
+    (dict(Hq=34, Hkv=2, algo=2, dtype=1), binding.PKV_EUNSUPPORTED),
+    (dict(q=None), binding.PKV_EINVAL),
+    (dict(q=1028), binding.PKV_EINVAL),
+    (dict(scale=float("nan")), binding.PKV_EINVAL),
+    (dict(S=70000), binding.PKV_EUNSUPPORTED),
+])
+def test_decode_rejects(over, code):
+    lib = pkv.lib()
+    assert _decode(lib, **over) == code
+    assert lib.pkv_last_error()
+
+
+@needs_lib
+def test_decode_empty_batch_is_a_no_op():
+    assert _decode(pkv.lib(), S=0, out=None, q=None) == binding.PKV_OK
+
+
+@needs_lib
+def test_workspace_size():
+    lib = pkv.lib()
+    # 32 seqs x 32 heads x ceil(32768/512)=64 partitions x (128 + 2) floats
+    assert pkv.decode_workspace_size(32, 32, 128, 32768, 512) == 32 * 32 * 64 * 130 * 4
+    assert pkv.decode_workspace_size(32, 32, 128, 512, 512) == 0      # one partition
+    assert pkv.decode_workspace_size(32, 32, 128, 513, 512) == 32 * 32 * 2 * 130 * 4
+    assert lib.pkv_decode_workspace_size(4, 8, 64, 100, 0) == 0
+
+
+def _store(lib, **over):
+    a = dict(k=1024, v=1024, kc=1024, vc=1024, slots=1024, T=4, NB=64, bs=16, Hkv=4, D=64,
+             dtype=0, stream=None)
+    a.update(over)
+    return lib.pkv_kv_cache_store(a["k"], a["v"], a["kc"], a["vc"], a["slots"], a["T"], a["NB"],
+                                  a["bs"], a["Hkv"], a["D"], a["dtype"], a["stream"])
+
+
+@needs_lib
+@pytest.mark.parametrize("over,code", [
+    (dict(T=-1), binding.PKV_EINVAL),
+    (dict(NB=0), binding.PKV_EINVAL),
+    (dict(dtype=3), binding.PKV_EINVAL),
+    (dict(Hkv=1, D=2, dtype=1), binding.PKV_EUNSUPPORTED),
+    (dict(k=None), binding.PKV_EINVAL),
+    (dict(kc=1032), binding.PKV_EINVAL),
+])
+def test_store_rejects(over, code):
+    lib = pkv.lib()
+    assert _store(lib, **over) == code
+    assert lib.pkv_last_error()
+
+
+@needs_lib
+def test_store_zero_tokens_is_a_no_op():
+    assert _store(pkv.lib(), T=0, k=None, v=None) == binding.PKV_OK
+
+
+def _prefill(lib, **over):
+    a = dict(out=1024, q=1024, k=1024, v=1024, bt=1024, cu=1024, cl=1024, S=2, Tq=64, maxq=32,
+             MB=16, max_ctx=256, NB=64, bs=16, Hq=32, Hkv=8, D=128, scale=0.08, causal=1,
+             dtype=1, stream=None)
+    a.update(over)
+    return lib.pkv_paged_attention_prefill_chunk(a["out"], a["q"], a["k"], a["v"], a["bt"],
+                                                 a["cu"], a["cl"], a["S"], a["Tq"], a["maxq"],
+                                                 a["MB"], a["max_ctx"], a["NB"], a["bs"],
+                                                 a["Hq"], a["Hkv"], a["D"], a["scale"],
+                                                 a["causal"], a["dtype"], a["stream"])
+
+
+@needs_lib
+@pytest.mark.parametrize("over,code", [
+    (dict(S=-1), binding.PKV_EINVAL),
+    (dict(dtype=0), binding.PKV_EUNSUPPORTED),
+    (dict(D=64), binding.PKV_EUNSUPPORTED),
+    (dict(Hq=24, Hkv=8), binding.PKV_EUNSUPPORTED),
+    (dict(Hq=30, Hkv=8), binding.PKV_EINVAL),
+    (dict(max_ctx=300), binding.PKV_EINVAL),
+    (dict(maxq=300, max_ctx=256), binding.PKV_EINVAL),
+    (dict(cu=None), binding.PKV_EINVAL),
+    (dict(out=1030), binding.PKV_EINVAL),
+])
+def test_prefill_rejects(over, code):
+    lib = pkv.lib()
+    assert _prefill(lib, **over) == code
+    assert lib.pkv_last_error()
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "_LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        binding.lib()

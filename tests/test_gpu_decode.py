@@ -1,0 +1,195 @@
+"""GPU parity of paged_attention_decode (single pass, split-K + reduce, VALU
+and MFMA kernels) against the float64 oracle, through the C ABI."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_attention_kv_store_amd as pkv
+from paged_attention_kv_store_amd import workloads as W
+from tests.gpu_helpers import (TOL, assert_close, gpu_decode, oracle_caches, oracle_decode, say,
+                               to_device)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("partition", [0, 16, 32, 64, 256])
+def test_tiny_fp32(partition):
+    b = W.tiny().batches[0]
+    say(f"tiny fp32 partition={partition}")
+    got = gpu_decode(b, algo="valu", partition_size=partition)
+    assert_close(got, oracle_decode(b), torch.float32, f"tiny p={partition}")
+
+
+SWEEP = [
+    # (dtype, hq, hkv, d, max_ctx, algo)
+    (torch.float32, 8, 4, 64, 300, "valu"),
+    (torch.float32, 8, 8, 128, 170, "valu"),
+    (torch.float32, 24, 3, 64, 120, "valu"),
+    (torch.bfloat16, 16, 8, 128, 300, "valu"),
+    (torch.bfloat16, 32, 8, 128, 300, "valu"),
+    (torch.bfloat16, 12, 2, 64, 250, "valu"),
+    (torch.bfloat16, 16, 8, 128, 300, "mfma"),
+    (torch.bfloat16, 32, 8, 128, 300, "mfma"),
+    (torch.bfloat16, 8, 8, 128, 200, "mfma"),
+    (torch.bfloat16, 32, 2, 128, 200, "mfma"),
+    (torch.bfloat16, 12, 4, 64, 250, "mfma"),
+    (torch.bfloat16, 64, 4, 64, 150, "mfma"),
+]
+
+
+@pytest.mark.parametrize("case", SWEEP, ids=lambda c: f"{str(c[0])[6:]}-{c[1]}x{c[2]}-d{c[3]}-{c[5]}")
+@pytest.mark.parametrize("partition", [0, 32, 128])
+def test_random_sweep(case, partition):
+    dtype, hq, hkv, d, max_ctx, algo = case
+    b = W.random_decode_batch(hq * 131 + d + max_ctx, 9, hq, hkv, d, dtype, max_ctx=max_ctx,
+                              min_ctx=0)
+    say(f"sweep {case} p={partition} ctx={b.pool.context_lens.tolist()}")
+    got = gpu_decode(b, algo=algo, partition_size=partition)
+    assert_close(got, oracle_decode(b), dtype, f"{algo} p={partition}")
+
+
+@pytest.mark.parametrize("bs", [32, 64])
+@pytest.mark.parametrize("algo", ["valu", "mfma"])
+def test_larger_blocks(bs, algo):
+    b = W.random_decode_batch(3 + bs, 6, 16, 4, 128, torch.bfloat16, max_ctx=400, min_ctx=1,
+                              block_size=bs)
+    say(f"block_size {bs} {algo}")
+    got = gpu_decode(b, algo=algo, partition_size=64)
+    assert_close(got, oracle_decode(b), torch.bfloat16, f"bs={bs} {algo}")
+
+
+@pytest.mark.parametrize("algo", ["valu", "mfma"])
+def test_context_one_returns_the_v_row_exactly(algo):
+    b = W.random_decode_batch(21, 7, 32, 8, 128, torch.bfloat16, max_ctx=1, min_ctx=1,
+                              store=False)
+    say(f"ctx=1 {algo}")
+    v = W.host_bits(b.v_cache)
+    want = np.stack([v[b.pool.block_tables[s, 0], 0] for s in range(7)])
+    want = np.repeat(want, 4, axis=1)          # q-head h reads kv-head h // 4
+    for partition in (0, 16):
+        got = gpu_decode(b, algo=algo, partition_size=partition, store=False)
+        np.testing.assert_array_equal(got, oracle.to_f64(want))
+
+
+@pytest.mark.parametrize("algo", ["valu", "mfma"])
+def test_identical_keys_give_mean_of_v(algo):
+    b = W.random_decode_batch(23, 5, 16, 8, 128, torch.bfloat16, max_ctx=200, min_ctx=1,
+                              store=False)
+    b.k_cache.fill_(0.5)                        # every key equal
+    say(f"identical keys {algo}")
+    got = gpu_decode(b, algo=algo, store=False)
+    v = oracle_caches(b, store=False)[1]
+    want = np.zeros_like(got)
+    for s, c in enumerate(b.pool.context_lens.tolist()):
+        rows = oracle.gather_context(v, b.pool.block_tables[s], c, b.block_size).mean(axis=0)
+        want[s] = np.repeat(rows, 2, axis=0)
+    assert_close(got, want, torch.bfloat16, "mean of V")
+
+
+@pytest.mark.parametrize("algo", ["valu", "mfma"])
+def test_block_permutation_invariance_is_bit_exact(algo):
+    b = W.random_decode_batch(29, 8, 32, 8, 128, torch.bfloat16, max_ctx=500, min_ctx=100,
+                              store=False)
+    dev = to_device(b)
+    out1 = gpu_decode(b, dev=dev, algo=algo, partition_size=64, store=False)
+    pi = torch.as_tensor(np.random.default_rng(1).permutation(b.pool.num_blocks), device="cuda")
+    kc2 = torch.empty_like(dev["k_cache"])
+    vc2 = torch.empty_like(dev["v_cache"])
+    kc2[pi.long()] = dev["k_cache"]
+    vc2[pi.long()] = dev["v_cache"]
+    dev2 = dict(dev, k_cache=kc2, v_cache=vc2,
+                block_tables=pi.to(torch.int32)[dev["block_tables"].long()].contiguous())
+    out2 = gpu_decode(b, dev=dev2, algo=algo, partition_size=64, store=False)
+    np.testing.assert_array_equal(out1, out2)
+
+
+@pytest.mark.parametrize("algo", ["valu", "mfma"])
+def test_deterministic(algo):
+    b = W.random_decode_batch(31, 16, 32, 8, 128, torch.bfloat16, max_ctx=900, min_ctx=1)
+    dev = to_device(b)
+    a = gpu_decode(b, dev=dev, algo=algo, partition_size=128)
+    c = gpu_decode(b, dev=dev, algo=algo, partition_size=128, store=False)
+    np.testing.assert_array_equal(a, c)
+
+
+def test_empty_contexts_give_zero_rows():
+    b = W.random_decode_batch(37, 6, 16, 8, 128, torch.bfloat16, max_ctx=50, min_ctx=0)
+    b.pool.context_lens[:] = 0
+    for algo in ("valu", "mfma"):
+        for partition in (0, 16):
+            got = gpu_decode(b, algo=algo, partition_size=partition, store=False)
+            assert (got == 0).all()
+
+
+def test_out_of_pool_block_ids_poison_the_row():
+    b = W.random_decode_batch(41, 4, 16, 8, 128, torch.bfloat16, max_ctx=64, min_ctx=40,
+                              store=False)
+    b.pool.block_tables[2, 0] = b.pool.num_blocks + 5    # rejected in-kernel, not dereferenced
+    for algo in ("valu", "mfma"):
+        got = gpu_decode(b, algo=algo, store=False)
+        assert np.isnan(got[2]).all()
+        want = oracle_decode(b, seqs=[0, 1, 3], store=False)
+        assert_close(got[[0, 1, 3]], want, torch.bfloat16, f"rows beside the bad one {algo}")
+
+
+# --------------------------------------------------------------------------
+# the standard workloads at full size, in the launch configurations the
+# benchmark times
+# --------------------------------------------------------------------------
+
+@pytest.mark.slow
+@pytest.mark.parametrize("algo", ["mfma", "valu"])
+def test_qwen3_decode_full_layer(algo):
+    wl = W.qwen3_decode(layers=1)
+    b = wl.batches[0]
+    say(f"qwen3 layer: S={b.num_seqs} NB={b.pool.num_blocks} {algo}")
+    want = oracle_decode(b)
+    for partition in (0, 256):
+        assert_close(gpu_decode(b, algo=algo, partition_size=partition), want, torch.bfloat16,
+                     f"qwen3 {algo} p={partition}")
+
+
+@pytest.mark.slow
+def test_llama_prefix_full_sampled():
+    b = W.llama_prefix().batches[0]
+    say(f"llama prefix: S={b.num_seqs} NB={b.pool.num_blocks}")
+    dev = to_device(b)
+    seqs = list(range(0, 256, 9)) + [255]
+    caches = oracle_caches(b, store=False)
+    want = oracle_decode(b, caches=caches, seqs=seqs)
+    for algo, partition in (("mfma", 0), ("mfma", 512), ("valu", 0)):
+        got = gpu_decode(b, dev=dev, algo=algo, partition_size=partition, store=False)
+        assert_close(got[seqs], want, torch.bfloat16, f"llama {algo} p={partition}")
+
+
+@pytest.mark.slow
+def test_long_splitk_full_sampled():
+    b = W.long_splitk().batches[0]
+    say(f"long split-K: ctx max {b.max_ctx}")
+    dev = to_device(b)
+    order = np.argsort(b.pool.context_lens)
+    seqs = sorted(set(order[:3].tolist() + order[-3:].tolist() + [7, 15]))
+    caches = oracle_caches(b, store=False)
+    want = oracle_decode(b, caches=caches, seqs=seqs)
+    for algo, partition in (("mfma", 512), ("mfma", 0), ("valu", 512)):
+        got = gpu_decode(b, dev=dev, algo=algo, partition_size=partition, store=False)
+        assert_close(got[seqs], want, torch.bfloat16, f"long {algo} p={partition}")
+
+
+@pytest.mark.slow
+def test_mixed_decode_part_full():
+    wl = W.mixed()
+    pre, dec = wl.prefill, wl.batches[0]
+    say("mixed: store 4224 tokens then decode 128 seqs")
+    dev = to_device(pre)
+    pkv.kv_cache_store(dev["k_new"], dev["v_new"], dev["k_cache"], dev["v_cache"],
+                       dev["slot_mapping"])
+    ddev = to_device(dec)
+    ddev["k_cache"], ddev["v_cache"] = dev["k_cache"], dev["v_cache"]
+    caches = oracle_caches(pre)
+    seqs = list(range(0, 128, 5))
+    want = oracle_decode(dec, caches=caches, seqs=seqs)
+    got = gpu_decode(dec, dev=ddev, algo="mfma", partition_size=0, store=False)
+    assert_close(got[seqs], want, torch.bfloat16, "mixed decode")
