@@ -29,6 +29,14 @@ namespace pkv {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 16;
+#ifndef PKV_DECODE_STAGES
+#define PKV_DECODE_STAGES 2
+#endif
+// Tiles in flight per wave in the matrix-core decode (register ring depth).
+constexpr int kStages = PKV_DECODE_STAGES;
+#ifndef PKV_DECODE_WAVES_PER_SIMD
+#define PKV_DECODE_WAVES_PER_SIMD 2
+#endif
 
 template <typename T>
 __device__ __forceinline__ void store_out(void* out, int64_t idx, float v);
@@ -286,17 +294,41 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
 // ---------------------------------------------------------------------------
 // Matrix-core decode (bf16)
 // ---------------------------------------------------------------------------
+// Per wave: tiles w, w+4, w+8, ... of the partition. Loads run kStages-1
+// tiles ahead of the math in a ring of register buffers, and each tile's
+// physical block id comes from a scalar load issued kStages tiles ahead. The
+// prefetch is unconditional (past the wave's last tile it re-reads that tile,
+// an L2 hit) so that the wait before a tile's math covers only its own loads.
+//
+// q.k: 16x16x32 bf16 MFMA, A = the tile's 16 K rows, B = q^T with the G heads
+// as columns (padded to 16). Its output gives lane l the scores of tokens
+// 4*(l/16)+r, r=0..3, for head l%16 -- exactly the A operand (P, heads as
+// rows, 4 tokens per lane) of the 16x16x16 bf16 MFMA used for P.V. For the
+// B operand (4 consecutive tokens of one column per lane) each 16-lane group
+// reads its 4 V rows whole (lane n holds columns EPL*n .. EPL*n+EPL-1 of all
+// 4 tokens), so step i of P.V takes column EPL*n+i of the 4 rows with two
+// in-lane byte permutes: no lane exchange, and every V load reads full rows.
+template <int D>
+struct MfmaTile {
+  static constexpr int KCH = D / 32;   // 16-byte K pieces per lane
+  static constexpr int EPL = D / 16;   // V columns per lane
+  uint4 k[KCH];
+  uint4 v[4];                          // rows 4*qg + 0..3 (EPL bf16 each, rest unused)
+};
+
 template <int D, int GP>
-__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
-  constexpr int KCH = D / 32;   // 16x16x32 steps over head_dim = 16-byte K pieces per lane
-  constexpr int EPL = D / 16;   // V elements per lane per row (16 lanes cover a row)
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PKV_DECODE_WAVES_PER_SIMD, PKV_DECODE_WAVES_PER_SIMD)))
+void decode_mfma_kernel(DecodeParams p) {
+  constexpr int KCH = MfmaTile<D>::KCH;
+  constexpr int EPL = MfmaTile<D>::EPL;   // also the number of 16x16x16 P.V steps
 
   __shared__ float s_m[kWaves * 16], s_l[kWaves * 16];
   __shared__ float s_o[kWaves * GP * D];
   __shared__ int s_poison;
 
   const int part = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, qg = lane >> 4;
   const int G = p.group;
   const int ctx = clamp_ctx(p.context_lens[s], p.max_ctx);
@@ -309,62 +341,76 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   const int n_parts = (ctx + P - 1) / P;
   const int t1 = min(ctx, t0 + P);
   const int n_tiles = (t1 - t0 + kTile - 1) / kTile;
+  const int my_tiles = w < n_tiles ? (n_tiles - w + kWaves - 1) / kWaves : 0;
   const int64_t row_elems = (int64_t)p.num_kv_heads * D;
   const int bs = p.block_size;
 
-  // B operand of q.k^T: column n is q-head g*G+n (zero past the group); lane
-  // group qg holds head_dim elements [qg*D/4, (qg+1)*D/4) as KCH pieces of 8.
-  // The K operand uses the same element order, so the contraction pairs
-  // matching elements whatever order the hardware sums them in.
+  // B operand of q.k^T: column n is q-head g*G+n (zero past the group). In
+  // step c, lane group qg holds head_dim elements [32c + 8qg, 32c + 8qg + 8),
+  // so the four lanes of a K row read 64 contiguous bytes per load. The K
+  // operand uses the same element order, so the contraction pairs matching
+  // elements whatever order the hardware sums them in.
   bf16x8_t qb[KCH];
   {
     const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) +
-                           ((int64_t)s * p.num_q_heads + g * G + n) * D + qg * (D / 4);
+                           ((int64_t)s * p.num_q_heads + g * G + n) * D + 8 * qg;
 #pragma unroll
     for (int j = 0; j < KCH; ++j) {
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (n < G) v = load16(qrow + 8 * j);
+      if (n < G) v = load16(qrow + 32 * j);
       qb[j] = bit_cast_to<bf16x8_t>(v);
     }
   }
 
-  const uint16_t* kc = reinterpret_cast<const uint16_t*>(p.k_cache) + g * D + qg * (D / 4);
+  const uint16_t* kc = reinterpret_cast<const uint16_t*>(p.k_cache) + g * D + 8 * qg;
+  // V: lane reads rows 4*qg + st (st = 0..3), columns EPL*n .. EPL*n+EPL-1
   const uint16_t* vc = reinterpret_cast<const uint16_t*>(p.v_cache) + g * D + EPL * n;
   const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks;
 
   float m_ref = neg_inf();   // reference max of head n (replicated over qg)
   float l_part = 0.f;        // sum over this lane's tokens for head n
-  f32x4_t acc[EPL];          // O[head 4*qg + r][EPL*n + e] in acc[e][r]
+  f32x4_t acc[EPL];          // acc[i][r] = O[head 4*qg + r][EPL*n + i]
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  bool poisoned = false;
+  bool bad = false;
 
-  for (int it = w; it < n_tiles; it += kWaves) {
-    const int tok0 = t0 + it * kTile;
-    const int64_t row0 = tile_row0(bt, tok0, bs, p.num_blocks, poisoned);
-    // K: lane reads token row0+n, its D/4-element slice
-    uint4 kr[KCH];
+  // Logical position of the first token of the wave's j-th tile (j clamped
+  // to the wave's last tile) and its physical block.
+  auto tile_tok0 = [&](int j) { return t0 + (w + kWaves * min(j, my_tiles - 1)) * kTile; };
+  auto block_of = [&](int j) { return bt[tile_tok0(j) / bs]; };
+
+  // Issue the loads of the wave's j-th tile, whose physical block is blk (an
+  // id outside the pool reads block 0 and poisons the result).
+  auto issue = [&](int j, int blk, MfmaTile<D>& t) {
+    if ((unsigned)blk >= (unsigned)p.num_blocks) {
+      blk = 0;
+      bad = true;
+    }
+    const int tok0 = tile_tok0(j);
+    const int64_t row0 = (int64_t)blk * bs + (tok0 % bs);
     const uint16_t* kp = kc + (row0 + n) * row_elems;
-#pragma unroll
-    for (int j = 0; j < KCH; ++j) kr[j] = load16(kp + 8 * j);
-    // V: step st reads token row0 + 4*qg + st, elements [EPL*n, EPL*n + EPL)
-    uint4 vr[4];
     const uint16_t* vp = vc + (row0 + 4 * qg) * row_elems;
+#pragma unroll
+    for (int c = 0; c < KCH; ++c) t.k[c] = load16(kp + 32 * c);
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       if constexpr (EPL == 8) {
-        vr[st] = load16(vp + st * row_elems);
+        t.v[st] = load16(vp + st * row_elems);
       } else {
         const uint2 h = load8(vp + st * row_elems);
-        vr[st] = make_uint4(h.x, h.y, 0, 0);
+        t.v[st] = make_uint4(h.x, h.y, 0, 0);
       }
     }
+  };
 
+  // Scores, online softmax and P.V of the wave's j-th tile.
+  auto compute = [&](int j, const MfmaTile<D>& t) {
+    const int tok0 = tile_tok0(j);
     // S[token 4*qg + r][head n] in sc[r]
     f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < KCH; ++j)
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bit_cast_to<bf16x8_t>(kr[j]), qb[j], sc, 0, 0, 0);
+    for (int c = 0; c < KCH; ++c)
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bit_cast_to<bf16x8_t>(t.k[c]), qb[c], sc, 0, 0, 0);
 
     const int tokq = tok0 + 4 * qg;
     float x[4];
@@ -385,21 +431,64 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
       }
       m_ref = m_new;
     }
-    float pr[4];
+    // P in bf16 (rounded to nearest even); the sum uses the rounded weights
+    // so numerator and denominator see the same values.
+    uint32_t pw[2];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(x[r] - m_ref);
-    l_part += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+    for (int h = 0; h < 2; ++h) {
+      pw[h] = pack_bf16x2(fast_exp2(x[2 * h] - m_ref), fast_exp2(x[2 * h + 1] - m_ref));
+      l_part += bf16_lo(pw[h]) + bf16_hi(pw[h]);
+    }
+    const short4_t pa = __builtin_bit_cast(short4_t, make_uint2(pw[0], pw[1]));
 
-    // O[h][d] += sum over the 4 tokens of step st: P[h][token] * V[token][d]
+    // V rows past the context may hold anything (NaN included): zero them
+    // before they meet a zero weight (only the last tile can be partial).
+    uint32_t vd[4][4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      float vf[8];
-      Widen<uint16_t>::run(vr[st], vf);
-      const bool live = tokq + st < t1;
+      vd[st][0] = t.v[st].x;
+      vd[st][1] = t.v[st].y;
+      vd[st][2] = t.v[st].z;
+      vd[st][3] = t.v[st].w;
+    }
+    if (tok0 + kTile > t1) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        const float b = live ? vf[e] : 0.f;
-        acc[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(pr[st], b, acc[e], 0, 0, 0);
+      for (int st = 0; st < 4; ++st) {
+        const bool live = tokq + st < t1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vd[st][i] = live ? vd[st][i] : 0u;
+      }
+    }
+    // step i: B column n = V[tokens 4*qg + 0..3][EPL*n + i]
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+      const uint32_t b0 = __builtin_amdgcn_perm(vd[1][i / 2], vd[0][i / 2], sel);
+      const uint32_t b1 = __builtin_amdgcn_perm(vd[3][i / 2], vd[2][i / 2], sel);
+      acc[i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+          pa, __builtin_bit_cast(short4_t, make_uint2(b0, b1)), acc[i], 0, 0, 0);
+    }
+  };
+
+  if (my_tiles > 0) {
+    // kStages register buffers in a ring; the loop is unrolled by the ring
+    // size so every buffer index is a compile-time constant and no register
+    // copy (which would wait on its pending load) is needed.
+    MfmaTile<D> buf[kStages];
+    int blk_ahead = block_of(0);
+#pragma unroll
+    for (int i = 0; i < kStages - 1; ++i) {
+      const int b = blk_ahead;
+      blk_ahead = block_of(i + 1);
+      issue(i, b, buf[i]);
+    }
+    for (int j = 0; j < my_tiles; j += kStages) {
+#pragma unroll
+      for (int u = 0; u < kStages; ++u) {
+        const int b = blk_ahead;
+        blk_ahead = block_of(j + u + kStages);
+        issue(j + u + kStages - 1, b, buf[(u + kStages - 1) % kStages]);
+        if (j + u < my_tiles) compute(j + u, buf[u]);
       }
     }
   }
@@ -418,7 +507,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
       for (int e = 0; e < EPL; ++e) s_o[(w * GP + h) * D + EPL * n + e] = acc[e][r];
     }
   }
-  poisoned = __any(poisoned);
+  const bool poisoned = __any(bad);
   if (threadIdx.x == 0) s_poison = 0;
   __syncthreads();
   if (poisoned && lane == 0) s_poison = 1;
@@ -428,23 +517,64 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
 
 // ---------------------------------------------------------------------------
 // Split-K merge: out = sum_k 2^(m_k - M) o_k / sum_k 2^(m_k - M) l_k
+// One workgroup of D threads per (q-head, sequence). The partition weights
+// 2^(m_k - M) are computed once per chunk of D partitions into LDS; thread d
+// then sums column d of the partials with independent, unrolled loads.
 // ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ float block_reduce(float v, bool is_max, float* scratch) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const float o = shfl_xor_f(v, m);
+    v = is_max ? fmaxf(v, o) : v + o;
+  }
+  if constexpr (D > 64) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (lane == 0) scratch[w] = v;
+    __syncthreads();
+    v = scratch[0];
+#pragma unroll
+    for (int i = 1; i < D / 64; ++i) v = is_max ? fmaxf(v, scratch[i]) : v + scratch[i];
+    __syncthreads();
+  }
+  return v;
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(D) void splitk_reduce_kernel(DecodeParams p) {
+  __shared__ float s_f[D];
+  __shared__ float s_red[D / 64 > 0 ? D / 64 : 1];
   const int h = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
   const int ctx = clamp_ctx(p.context_lens[s], p.max_ctx);
   const int P = p.partition_size;
   const int n = (ctx + P - 1) / P;
   if (n <= 1) return;   // written directly by the partition pass
   const int64_t base = ((int64_t)s * p.num_q_heads + h) * p.num_partitions;
+  const float* wm = p.ws_m + base;
+  const float* wl = p.ws_l + base;
+  const float* wo = p.ws_o + base * D;
   float M = neg_inf();
-  for (int k = 0; k < n; ++k) M = fmaxf(M, p.ws_m[base + k]);
+  for (int k = d; k < n; k += D) M = fmaxf(M, wm[k]);
+  M = block_reduce<D>(M, true, s_red);
   float L = 0.f, O = 0.f;
-  for (int k = 0; k < n; ++k) {
-    const float f = fast_exp2(p.ws_m[base + k] - M);
-    L += p.ws_l[base + k] * f;
-    O += p.ws_o[(base + k) * D + d] * f;
+  for (int kb = 0; kb < n; kb += D) {
+    const int k = kb + d;
+    const float f = k < n ? fast_exp2(wm[k] - M) : 0.f;
+    if (k < n) L += f * wl[k];
+    s_f[d] = f;
+    __syncthreads();
+    const int lim = min(D, n - kb);
+    const float* col = wo + (int64_t)kb * D + d;
+    int kk = 0;
+    for (; kk + 4 <= lim; kk += 4) {
+      const float o0 = col[(kk + 0) * D], o1 = col[(kk + 1) * D];
+      const float o2 = col[(kk + 2) * D], o3 = col[(kk + 3) * D];
+      O += s_f[kk] * o0 + s_f[kk + 1] * o1 + s_f[kk + 2] * o2 + s_f[kk + 3] * o3;
+    }
+    for (; kk < lim; ++kk) O += s_f[kk] * col[kk * D];
+    __syncthreads();
   }
+  L = block_reduce<D>(L, false, s_red);
   store_out<T>(p.out, ((int64_t)s * p.num_q_heads + h) * D + d, O / L);
 }
 
