@@ -238,6 +238,7 @@ extern "C" int pkv_paged_attention_prefill_chunk(void* out, const void* q, const
   p.cu_seqlens_q = cu_seqlens_q;
   p.context_lens = context_lens;
   p.num_seqs = num_seqs;
+  p.total_q = total_q;
   p.max_q_len = max_q_len;
   p.max_blocks = max_blocks_per_seq;
   p.num_blocks = num_blocks;

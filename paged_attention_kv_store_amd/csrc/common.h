@@ -60,6 +60,7 @@ struct PrefillParams {
   const int32_t* cu_seqlens_q;
   const int32_t* context_lens;
   int32_t num_seqs;
+  int32_t total_q;
   int32_t max_q_len;
   int32_t max_blocks;
   int32_t num_blocks;

@@ -1,0 +1,136 @@
+"""GPU parity of paged_attention_prefill_chunk against the float64 oracle,
+through the C ABI (bf16, head_dim 128, causal and non-causal)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_attention_kv_store_amd as pkv
+from paged_attention_kv_store_amd import workloads as W
+from tests.gpu_helpers import assert_close, oracle_caches, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_prefill(b, dev=None, causal=True, store=True):
+    dev = dev or to_device(b)
+    if store and b.k_new is not None:
+        pkv.kv_cache_store(dev["k_new"], dev["v_new"], dev["k_cache"], dev["v_cache"],
+                           dev["slot_mapping"])
+    out = torch.empty_like(dev["q"])
+    cu = b.cu_seqlens_q
+    pkv.paged_attention_prefill_chunk(out, dev["q"], dev["k_cache"], dev["v_cache"],
+                                      dev["block_tables"], dev["cu_seqlens_q"],
+                                      dev["context_lens"], b.scale, int(np.diff(cu).max()),
+                                      b.max_ctx, causal=causal)
+    torch.cuda.synchronize()
+    return out.float().cpu().double().numpy()
+
+
+def oracle_prefill(b, caches=None, causal=True, rows=None):
+    kc, vc = caches if caches is not None else oracle_caches(b)
+    q = W.host_bits(b.q)
+    return oracle.paged_attention_prefill_chunk(q, kc, vc, b.pool.block_tables, b.cu_seqlens_q,
+                                                b.pool.context_lens, b.scale, b.block_size,
+                                                causal=causal)
+
+
+CASES = [
+    # (hq, hkv, chunks, max_rows, max_prior)
+    (32, 8, 3, 150, 300),
+    (16, 8, 4, 70, 90),
+    (8, 8, 2, 200, 20),
+    (32, 4, 3, 40, 200),
+    (8, 1, 2, 33, 64),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[0]}x{c[1]}-r{c[3]}-p{c[4]}")
+@pytest.mark.parametrize("causal", [True, False])
+def test_random_chunks(case, causal):
+    hq, hkv, chunks, max_rows, max_prior = case
+    b = W.random_prefill_batch(hq * 7 + max_rows, chunks, hq, hkv, 128, torch.bfloat16,
+                               max_rows=max_rows, max_prior=max_prior)
+    say(f"prefill {case} causal={causal} rows={np.diff(b.cu_seqlens_q).tolist()} "
+        f"ctx={b.pool.context_lens.tolist()}")
+    got = gpu_prefill(b, causal=causal)
+    assert_close(got, oracle_prefill(b, causal=causal), torch.bfloat16, f"prefill causal={causal}")
+
+
+@pytest.mark.parametrize("bs", [32, 64])
+def test_larger_blocks(bs):
+    b = W.random_prefill_batch(50 + bs, 3, 32, 8, 128, torch.bfloat16, max_rows=100,
+                               max_prior=150, block_size=bs)
+    assert_close(gpu_prefill(b), oracle_prefill(b), torch.bfloat16, f"bs={bs}")
+
+
+def test_single_row_chunk_matches_decode():
+    b = W.random_prefill_batch(61, 4, 32, 8, 128, torch.bfloat16, max_rows=1, max_prior=700)
+    dev = to_device(b)
+    got = gpu_prefill(b, dev=dev)
+    out = torch.empty_like(dev["q"])
+    pkv.paged_attention_decode(out, dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
+                               dev["context_lens"], b.scale, b.max_ctx)
+    torch.cuda.synchronize()
+    dec = out.float().cpu().double().numpy()
+    # both within tolerance of the oracle, and of each other
+    want = oracle_prefill(b)
+    assert_close(got, want, torch.bfloat16, "prefill L=1")
+    assert_close(dec, want, torch.bfloat16, "decode")
+
+
+def test_first_row_without_prior_returns_v_row():
+    b = W.random_prefill_batch(67, 2, 16, 8, 128, torch.bfloat16, max_rows=40, max_prior=0)
+    got = gpu_prefill(b)
+    kc, vc = oracle_caches(b)
+    for c in range(2):
+        row0 = b.cu_seqlens_q[c]
+        v0 = oracle.gather_context(vc, b.pool.block_tables[c], 1, b.block_size)[0]
+        np.testing.assert_array_equal(got[row0], np.repeat(v0, 2, axis=0))
+
+
+def test_deterministic():
+    b = W.random_prefill_batch(71, 3, 32, 8, 128, torch.bfloat16, max_rows=130, max_prior=500)
+    dev = to_device(b)
+    a = gpu_prefill(b, dev=dev)
+    c = gpu_prefill(b, dev=dev, store=False)
+    np.testing.assert_array_equal(a, c)
+
+
+def test_out_of_pool_block_poisons_its_chunk():
+    b = W.random_prefill_batch(73, 3, 32, 8, 128, torch.bfloat16, max_rows=60, max_prior=80)
+    dev = to_device(b)
+    pkv.kv_cache_store(dev["k_new"], dev["v_new"], dev["k_cache"], dev["v_cache"],
+                       dev["slot_mapping"])
+    bt = b.pool.block_tables.copy()
+    bt[1, 0] = b.pool.num_blocks + 3
+    dev["block_tables"] = torch.as_tensor(bt, device="cuda")
+    got = gpu_prefill(b, dev=dev, store=False)
+    cu = b.cu_seqlens_q
+    assert np.isnan(got[cu[1]:cu[2]]).all()
+    want = oracle_prefill(b)
+    for c in (0, 2):
+        assert_close(got[cu[c]:cu[c + 1]], want[cu[c]:cu[c + 1]], torch.bfloat16, f"chunk {c}")
+
+
+@pytest.mark.slow
+def test_mixed_prefill_full_sampled_rows():
+    wl = W.mixed()
+    b = wl.prefill
+    say(f"mixed prefill: ctx={b.pool.context_lens.tolist()}")
+    got = gpu_prefill(b)
+    kc, vc = oracle_caches(b)
+    # oracle on a sample of rows of every chunk: first, last, and a stride
+    cu = b.cu_seqlens_q
+    q = W.host_bits(b.q)
+    for c in range(8):
+        rows = sorted({0, 1, 63, 64, 255, 511} | set(range(7, 512, 97)))
+        ctx = int(b.pool.context_lens[c])
+        prior = ctx - 512
+        for i in rows:
+            # row i of chunk c equals decode over the first prior + i + 1 keys
+            want = oracle.paged_attention_decode(q[cu[c] + i][None], kc, vc,
+                                                 b.pool.block_tables[c:c + 1],
+                                                 np.array([prior + i + 1]), b.scale, 16)
+            assert_close(got[cu[c] + i][None], want, torch.bfloat16, f"chunk {c} row {i}")
