@@ -147,7 +147,7 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
  * positions.
  *   total_q: rows of q and out; max_q_len >= every L_c (sizes the grid);
  *   max_context_len >= every context_lens[c], <= max_blocks_per_seq * block_size.
- * Supported: bf16, head_dim 128, block_size a multiple of 16 up to 256,
+ * Supported: bf16, head_dim 128, block_size a power of two in [16, 256],
  * num_q_heads / num_kv_heads in {1, 2, 4, 8}.
  */
 int pkv_paged_attention_prefill_chunk(void* out, const void* q, const void* k_cache,

@@ -214,8 +214,8 @@ extern "C" int pkv_paged_attention_prefill_chunk(void* out, const void* q, const
   if (head_dim != 128) return fail(PKV_EUNSUPPORTED, "%s: prefill supports head_dim 128 only", fn);
   if (group != 1 && group != 2 && group != 4 && group != 8)
     return fail(PKV_EUNSUPPORTED, "%s: GQA group %d not in {1, 2, 4, 8}", fn, group);
-  if (block_size % 16 != 0 || block_size > 256)
-    return fail(PKV_EUNSUPPORTED, "%s: block_size %d must be a multiple of 16 up to 256", fn, block_size);
+  if (block_size < 16 || block_size > 256 || (block_size & (block_size - 1)) != 0)
+    return fail(PKV_EUNSUPPORTED, "%s: block_size %d must be a power of two in [16, 256]", fn, block_size);
   if (max_blocks_per_seq <= 0) return fail(PKV_EINVAL, "%s: max_blocks_per_seq must be positive", fn);
   if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
     return fail(PKV_EINVAL, "%s: max_context_len outside [0, max_blocks_per_seq * block_size]", fn);
@@ -243,6 +243,7 @@ extern "C" int pkv_paged_attention_prefill_chunk(void* out, const void* q, const
   p.max_blocks = max_blocks_per_seq;
   p.num_blocks = num_blocks;
   p.block_size = block_size;
+  p.block_size_log2 = __builtin_ctz((unsigned)block_size);
   p.num_q_heads = num_q_heads;
   p.num_kv_heads = num_kv_heads;
   p.group = group;

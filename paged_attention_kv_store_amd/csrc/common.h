@@ -62,9 +62,11 @@ struct PrefillParams {
   int32_t num_seqs;
   int32_t total_q;
   int32_t max_q_len;
+  int32_t num_q_tiles;       // set by the launcher
   int32_t max_blocks;
   int32_t num_blocks;
   int32_t block_size;
+  int32_t block_size_log2;
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t group;

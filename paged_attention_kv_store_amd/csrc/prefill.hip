@@ -12,17 +12,19 @@
 // heads. Wave w owns M rows 32w .. 32w+31 as two 16-row tiles.
 //
 // The keys are walked in 64-token tiles gathered through the block table
-// into LDS (double-buffered: the next tile's global loads are in flight while
-// the current one is consumed), 16-byte pieces XOR-swizzled by row so that
-// both access patterns below are free of bank conflicts. Per 16 keys:
+// straight into LDS with direct-to-LDS loads (double-buffered: the next
+// tile's loads are in flight while the current one is consumed), 16-byte
+// pieces XOR-swizzled by row so that both access patterns below are free of
+// bank conflicts. Per 16 keys:
 //  * S^T = K Q^T on 16x16x32 bf16 MFMA (A = 16 K rows from LDS, B = the
 //    wave's Q rows kept in registers) gives each lane the scores of keys
 //    4*(l/16)+r for M row l%16;
 //  * causal / context mask, online softmax in fp32 (log2 domain, lazy
 //    rescaling), P rounded to bf16;
-//  * O += P V on 16x16x16 bf16 MFMA: P is already laid out as the A operand;
-//    the B operand (4 keys of one column per lane) comes from whole V rows
-//    read from LDS with two in-lane byte permutes.
+//  * O += P V on 16x16x32 bf16 MFMA over 32 keys at a time: the scores of
+//    two 16-key tiles are already laid out as the A operand (8 keys per
+//    lane); the B operand (the same 8 keys of one column per lane) comes from
+//    whole V rows read from LDS with four in-lane byte permutes.
 #include "common.h"
 #include "device_utils.h"
 
@@ -36,25 +38,34 @@ constexpr int kPThreads = 64 * kPW;
 constexpr int kMRows = 32 * kPW;      // M rows per workgroup
 constexpr int kKvTile = 64;           // keys per LDS tile
 constexpr int kRowPieces = kD * 2 / 16;   // 16-byte pieces per K/V row (16)
+constexpr int kXcds = 8;              // accelerator complex dies, each with its own L2
 
 // LDS position (in 16-byte units) of piece c of key row t in a tile.
 __device__ __forceinline__ int swz(int t, int c) { return t * kRowPieces + (c ^ (t & 15)); }
 
-struct KvStage {
-  uint4 k[4];
-  uint4 v[4];
-};
-
 }  // namespace
 
 template <int G>
-__global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_kernel(PrefillParams p) {
   constexpr int BQ = kMRows / G;      // query rows per workgroup
   __shared__ uint4 s_k[2][kKvTile * kRowPieces];
   __shared__ uint4 s_v[2][kKvTile * kRowPieces];
   __shared__ int s_bad;
 
-  const int qt = blockIdx.x, g = blockIdx.y, c = blockIdx.z;
+  // Work item of this workgroup. Workgroups are handed to the 8 XCDs round
+  // robin (id % 8), each XCD with its own L2. Item i = x * (items/8) + id/8
+  // for x = id % 8 gives every XCD a contiguous range of items, ordered with
+  // the kv-head slowest and the q-tiles of a chunk adjacent: all q-tiles that
+  // read the same chunk's K/V run on one XCD, close in time, and share its
+  // L2. Within a chunk the q-tiles with more keys go first.
+  const int nqt = p.num_q_tiles;
+  const int per_xcd = gridDim.x / kXcds;
+  const int item = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (item >= nqt * p.num_seqs * p.num_kv_heads) return;
+  const int qt = nqt - 1 - item % nqt;
+  const int c = (item / nqt) % p.num_seqs;
+  const int g = item / (nqt * p.num_seqs);
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, qg = lane >> 4;
@@ -72,7 +83,11 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
   const int64_t row_elems = (int64_t)p.num_kv_heads * kD;
   const int bs = p.block_size;
   const int32_t* bt = p.block_tables + (int64_t)c * p.max_blocks;
-  const float scale = p.scale_log2;
+  // A negative scale is applied as |scale| to negated q (exact in bf16), so
+  // the scale is >= 0 below and the row max of raw scores gives the max of
+  // scaled ones.
+  const float scale = fabsf(p.scale_log2);
+  const uint32_t qsign = p.scale_log2 < 0.f ? 0x80008000u : 0u;
 
   // ---- the wave's Q rows (B operand of S^T = K Q^T) ----------------------
   // tile t, lane l: M row mr = 32w + 16t + l%16 (query row r0 + mr/G, head
@@ -91,137 +106,184 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
     for (int s = 0; s < 4; ++s) {
       uint4 v = make_uint4(0, 0, 0, 0);
       if (live) v = load16(qrow + 32 * s);
+      v.x ^= qsign;
+      v.y ^= qsign;
+      v.z ^= qsign;
+      v.w ^= qsign;
       qf[t][s] = bit_cast_to<bf16x8_t>(v);
     }
   }
 
-  // ---- cooperative K/V tile gather (global -> registers -> LDS) ----------
-  // thread tid moves pieces f = i*256 + tid, i = 0..3: key row f/16, piece f%16
+  // ---- cooperative K/V tile gather, global memory straight into LDS -------
+  // A direct-to-LDS load puts lane j's 16 bytes at (wave's LDS base) + 16j.
+  // Load i of wave w fills LDS rows 16i + 4w .. +3 of the tile, so lane j
+  // fetches key row t = 16i + 4w + j/16, piece (j%16) ^ (t%16): the swizzled
+  // layout comes out of the choice of source addresses. Rows 16i .. 16i+15 of
+  // a tile lie in one block (block_size is a power of two >= 16), so a tile
+  // needs four block ids, all workgroup-uniform, scalar-loaded a tile ahead.
+  // Rows past the context are read from the last live row instead (finite
+  // values; their weight is zero), so no NaN from a dead row reaches P.V.
+  const int lbs = p.block_size_log2;
+  const int64_t row_bytes = row_elems * 2;
+  const int lrow = 4 * w + (lane >> 4);          // tile row of load 0, minus 16i
+  const char* kbase = reinterpret_cast<const char*>(p.k_cache) + g * kD * 2;
+  const char* vbase = reinterpret_cast<const char*>(p.v_cache) + g * kD * 2;
   bool bad = false;
-  auto gather = [&](int kt, KvStage& st) {
+  auto tile_blocks = [&](int kt, int (&ids)[4]) {
+    const int kv0 = min(kt, max(n_kv - 1, 0)) * kKvTile;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ids[i] = bt[min(kv0 + 16 * i, max(ctx - 1, 0)) >> lbs];
+  };
+  auto gather = [&](int kt, int buf, const int (&ids)[4]) {
     const int kv0 = kt * kKvTile;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int f = i * kPThreads + tid;
-      const int t = f / kRowPieces, piece = f % kRowPieces;
-      const int pos = kv0 + t;
-      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-      if (pos < ctx) {   // keys past the context read as zeros (never NaN garbage)
-        int blk = bt[pos / bs];
-        if ((unsigned)blk >= (unsigned)p.num_blocks) {
-          blk = 0;
-          bad = true;
-        }
-        const int64_t off = ((int64_t)blk * bs + pos % bs) * row_elems + g * kD + piece * 8;
-        kv = load16(reinterpret_cast<const uint16_t*>(p.k_cache) + off);
-        vv = load16(reinterpret_cast<const uint16_t*>(p.v_cache) + off);
+      int blk = ids[i];
+      if ((unsigned)blk >= (unsigned)p.num_blocks) {
+        blk = 0;
+        bad = true;
       }
-      st.k[i] = kv;
-      st.v[i] = vv;
+      const int t = 16 * i + lrow;
+      const int piece = (lane & 15) ^ (t & 15);
+      const int pos = min(kv0 + t, ctx - 1);
+      const int64_t off = (((int64_t)blk << lbs) + (pos & (bs - 1))) * row_bytes + piece * 16;
+      const int lds_pos = (16 * i + 4 * w) * kRowPieces;
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(kbase + off),
+                                       (void __attribute__((address_space(3)))*)(&s_k[buf][lds_pos]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(vbase + off),
+                                       (void __attribute__((address_space(3)))*)(&s_v[buf][lds_pos]), 16, 0, 0);
     }
   };
-  auto to_lds = [&](int buf, const KvStage& st) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int f = i * kPThreads + tid;
-      const int t = f / kRowPieces, piece = f % kRowPieces;
-      s_k[buf][swz(t, piece)] = st.k[i];
-      s_v[buf][swz(t, piece)] = st.v[i];
-    }
-  };
+  // all of this thread's direct-to-LDS loads have landed (vmcnt 0)
+  auto wait_loads = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };
 
-  float m_ref[2] = {neg_inf(), neg_inf()};   // per softmax row (lane's n)
-  float l_part[2] = {0.f, 0.f};
+  float m_ref[2] = {neg_inf(), neg_inf()};   // per softmax row (lane's n), scaled units
   f32x4_t acc[2][8];                          // acc[t][i][r] = O[row 16t + 4qg + r][8n + i]
+  f32x4_t lsum[2];                            // lsum[t][r]   = sum of P over row 16t + 4qg + r
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < 2; ++t) {
+    lsum[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[t][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  // bf16 ones: P times a ones column gives the row sums of the rounded weights
+  const bf16x8_t ones = bit_cast_to<bf16x8_t>(make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
+  // keys below this bound are visible to every row of the wave
+  const int lim_wave = p.causal ? min(P0 + r0 + (32 * w) / G + 1, ctx) : ctx;
 
   if (tid == 0) s_bad = 0;
-  KvStage stage;
+  int ids_next[4], ids_after[4];
   if (n_kv > 0) {
-    gather(0, stage);
-    to_lds(0, stage);
+    int ids0[4];
+    tile_blocks(0, ids0);
+    tile_blocks(1, ids_next);
+    gather(0, 0, ids0);
   }
+  wait_loads();
   __syncthreads();
 
   for (int kt = 0; kt < n_kv; ++kt) {
     const int buf = kt & 1;
     const bool more = kt + 1 < n_kv;
-    if (more) gather(kt + 1, stage);
+    tile_blocks(kt + 2, ids_after);
+    // the other buffer was last read before the previous barrier
+    if (more) gather(kt + 1, buf ^ 1, ids_next);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ids_next[i] = ids_after[i];
     const int kv0 = kt * kKvTile;
     const uint4* sk = s_k[buf];
     const uint4* sv = s_v[buf];
 
 #pragma unroll
-    for (int sub = 0; sub < kKvTile / 16; ++sub) {
-      const int tb = 16 * sub;              // first key of the sub-tile, tile-relative
+    for (int sub = 0; sub < kKvTile / 32; ++sub) {
+      const int tb = 32 * sub;              // first key of the 32-key block, tile-relative
       if (kv0 + tb >= kv_end) break;
-      // K rows tb + n, pieces 4s + qg (elements 32s + 8qg .. +8)
-      bf16x8_t kf[4];
+      // Slot u = 0..7 of a lane stands for key tb + 16*(u/4) + 4qg + u%4: the
+      // keys of two 16-key score tiles, in the order their scores arrive.
+      // K rows tb + 16h + n, pieces 4s + qg (elements 32s + 8qg .. +8)
+      bf16x8_t kf[2][4];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) kf[s] = bit_cast_to<bf16x8_t>(sk[swz(tb + n, 4 * s + qg)]);
-      // V rows tb + 4qg + st, piece n (columns 8n .. 8n+7)
-      uint32_t vd[4][4];
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const uint4 v = sv[swz(tb + 4 * qg + st, n)];
-        vd[st][0] = v.x;
-        vd[st][1] = v.y;
-        vd[st][2] = v.z;
-        vd[st][3] = v.w;
-      }
-      const int keyq = kv0 + tb + 4 * qg;   // key position of the lane's r = 0
-      short4_t pa[2];
+        for (int s = 0; s < 4; ++s) kf[h][s] = bit_cast_to<bf16x8_t>(sk[swz(tb + 16 * h + n, 4 * s + qg)]);
+      const int keyq = kv0 + tb + 4 * qg;   // key of slot 0
+      const bool full = kv0 + tb + 32 <= lim_wave;   // no key of the block is masked for this wave
+      bf16x8_t pa[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+        float x[8];   // raw scores q.k
 #pragma unroll
-        for (int s = 0; s < 4; ++s) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], qf[t][s], sc, 0, 0, 0);
-        const int lim = p.causal ? min(qpos[t] + 1, ctx) : ctx;   // visible keys < lim
-        float x[4];
+        for (int h = 0; h < 2; ++h) {
+          f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) x[r] = (keyq + r < lim) ? sc[r] * scale : neg_inf();
-        float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+          for (int s = 0; s < 4; ++s)
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[h][s], qf[t][s], sc, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) x[4 * h + r] = sc[r];
+        }
+        if (!full) {
+          const int lim = p.causal ? min(qpos[t] + 1, ctx) : ctx;   // visible keys < lim
+#pragma unroll
+          for (int u = 0; u < 8; ++u) x[u] = (keyq + 16 * (u / 4) + (u % 4) < lim) ? x[u] : neg_inf();
+        }
+        float mt = x[0];
+#pragma unroll
+        for (int u = 1; u < 8; ++u) mt = fmaxf(mt, x[u]);
         mt = fmaxf(mt, shfl_xor_f(mt, 16));
         mt = fmaxf(mt, shfl_xor_f(mt, 32));
+        mt = (mt == neg_inf()) ? mt : mt * scale;
         if (__any(mt > m_ref[t] + kRescaleThreshold)) {
           const float m_new = fmaxf(m_ref[t], mt);
           const float alpha = (m_new == neg_inf()) ? 1.f : fast_exp2(m_ref[t] - m_new);
-          l_part[t] *= alpha;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float a = __shfl(alpha, 4 * qg + r, 64);   // factor of row 4qg + r
+            lsum[t][r] *= a;
 #pragma unroll
             for (int i = 0; i < 8; ++i) acc[t][i][r] *= a;
           }
           m_ref[t] = m_new;
         }
-        const float mb = (m_ref[t] == neg_inf()) ? 0.f : m_ref[t];
-        uint32_t pw[2];
+        // weight 2^(scale*x - m); a masked score (-inf) gives 0
+        const float nm = (m_ref[t] == neg_inf()) ? 0.f : -m_ref[t];
+        uint32_t pw[4];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          pw[h] = pack_bf16x2(fast_exp2(x[2 * h] - mb), fast_exp2(x[2 * h + 1] - mb));
-          l_part[t] += bf16_lo(pw[h]) + bf16_hi(pw[h]);
+        for (int h = 0; h < 4; ++h) {
+          float e0 = fast_exp2(fmaf(x[2 * h], scale, nm));
+          float e1 = fast_exp2(fmaf(x[2 * h + 1], scale, nm));
+          if (!full) {
+            e0 = (x[2 * h] == neg_inf()) ? 0.f : e0;
+            e1 = (x[2 * h + 1] == neg_inf()) ? 0.f : e1;
+          }
+          pw[h] = pack_bf16x2(e0, e1);
         }
-        pa[t] = __builtin_bit_cast(short4_t, make_uint2(pw[0], pw[1]));
+        pa[t] = bit_cast_to<bf16x8_t>(make_uint4(pw[0], pw[1], pw[2], pw[3]));
+        lsum[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[t], ones, lsum[t], 0, 0, 0);
       }
+      // V rows of the lane's 8 keys, piece n (columns 8n .. 8n+7)
+      uint32_t vd[8][4];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint4 v = sv[swz(tb + 16 * (u / 4) + 4 * qg + (u % 4), n)];
+        vd[u][0] = v.x;
+        vd[u][1] = v.y;
+        vd[u][2] = v.z;
+        vd[u][3] = v.w;
+      }
+      // step i: B column n = V[the lane's 8 keys][8n + i]
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
-        const uint32_t b0 = __builtin_amdgcn_perm(vd[1][i / 2], vd[0][i / 2], sel);
-        const uint32_t b1 = __builtin_amdgcn_perm(vd[3][i / 2], vd[2][i / 2], sel);
-        const short4_t vb = __builtin_bit_cast(short4_t, make_uint2(b0, b1));
+        uint32_t b[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) b[h] = __builtin_amdgcn_perm(vd[2 * h + 1][i / 2], vd[2 * h][i / 2], sel);
+        const bf16x8_t vb = bit_cast_to<bf16x8_t>(make_uint4(b[0], b[1], b[2], b[3]));
 #pragma unroll
         for (int t = 0; t < 2; ++t)
-          acc[t][i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa[t], vb, acc[t][i], 0, 0, 0);
+          acc[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[t], vb, acc[t][i], 0, 0, 0);
       }
     }
-    if (more) {
-      // the other buffer was last read before the previous barrier
-      to_lds(buf ^ 1, stage);
-    }
+    wait_loads();
     __syncthreads();
   }
 
@@ -232,16 +294,12 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
   const bool poisoned = s_bad != 0;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    float l = l_part[t];
-    l += shfl_xor_f(l, 16);
-    l += shfl_xor_f(l, 32);          // row sum of M row 16t + n (all lanes with this n)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float lr = __shfl(l, 4 * qg + r, 64);   // sum of row 16t + 4qg + r
       const int mr = 32 * w + 16 * t + 4 * qg + r;
       const int qi = r0 + mr / G;
       if (qi >= L) continue;
-      const float inv = poisoned ? __builtin_nanf("") : 1.f / lr;
+      const float inv = poisoned ? __builtin_nanf("") : 1.f / lsum[t][r];
       uint32_t o[4];
 #pragma unroll
       for (int h = 0; h < 4; ++h) o[h] = pack_bf16x2(acc[t][2 * h][r] * inv, acc[t][2 * h + 1][r] * inv);
@@ -255,12 +313,16 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t stream) {
   if (head_dim != kD) return hipErrorInvalidValue;
   const int bq = kMRows / p.group;
-  const dim3 grid((p.max_q_len + bq - 1) / bq, p.num_kv_heads, p.num_seqs);
+  PrefillParams q = p;
+  q.num_q_tiles = (p.max_q_len + bq - 1) / bq;
+  const int64_t items = (int64_t)q.num_q_tiles * p.num_seqs * p.num_kv_heads;
+  if (items > 0x7fffffff - kXcds) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((items + kXcds - 1) / kXcds * kXcds));
   switch (p.group) {
-    case 1: hipLaunchKernelGGL(prefill_kernel<1>, grid, dim3(kPThreads), 0, stream, p); break;
-    case 2: hipLaunchKernelGGL(prefill_kernel<2>, grid, dim3(kPThreads), 0, stream, p); break;
-    case 4: hipLaunchKernelGGL(prefill_kernel<4>, grid, dim3(kPThreads), 0, stream, p); break;
-    case 8: hipLaunchKernelGGL(prefill_kernel<8>, grid, dim3(kPThreads), 0, stream, p); break;
+    case 1: hipLaunchKernelGGL(prefill_kernel<1>, grid, dim3(kPThreads), 0, stream, q); break;
+    case 2: hipLaunchKernelGGL(prefill_kernel<2>, grid, dim3(kPThreads), 0, stream, q); break;
+    case 4: hipLaunchKernelGGL(prefill_kernel<4>, grid, dim3(kPThreads), 0, stream, q); break;
+    case 8: hipLaunchKernelGGL(prefill_kernel<8>, grid, dim3(kPThreads), 0, stream, q); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
