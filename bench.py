@@ -1,30 +1,43 @@
 """Throughput of paged-KV attention on one MI355X.
 
-Headline workload: a Qwen3-0.6B-shaped decode step -- 60 sequences with
-contexts U{64..1024}, 16 q / 8 kv heads, head_dim 128, block_size 16, bf16,
-28 layers with distinct caches and queries (so the 256 MB last-level cache
-cannot serve repeated reads) and one shared block table. One step stores
-each sequence's new K/V row and runs decode attention, layer after layer.
+Headline workload (one "step"): a Qwen3-0.6B-shaped decode step -- 60
+sequences with contexts U{64..1024}, 16 q / 8 kv heads, head_dim 128,
+block_size 16, bf16, 28 layers with distinct caches and queries (so the
+256 MB last-level cache cannot serve repeated reads) and one shared block
+table. Per layer the step stores each sequence's new K/V row
+(kv_cache_store) and runs decode attention (paged_attention_decode). The
+28-layer step is captured once in a HIP graph and replayed, as a serving
+engine replays its decode step; every replay used for timing is checked
+bit-exact against the eagerly launched step first (--eager times eager
+launches instead).
 
-value = algorithmic decode bytes per step / step time (GB/s): the K and V
-rows inside the contexts, q, out, the block-table entries used and the
-context lengths, plus the store's reads and writes. Inputs are resident in
-HBM before timing starts.
+value = algorithmic bytes per step / step time, in GB/s: the K and V rows
+inside the contexts, q, out, the block-table entries used and the context
+lengths, plus the store's reads and writes. Inputs are resident in HBM
+before timing starts.
 
-Also reported on the same JSON line: the roofline of the dominant kernel
-(decode, HBM-bound) timed with HIP events on its own stream, a plain-copy
-bandwidth measured in the same run, tokens/s, the other standard workloads
-(prefix-shared batch, long-context split-K, mixed chunked prefill + decode
-with prefill matrix-core utilisation), a parity sample against the CPU
-oracle, and the oracle itself timed on a bounded sample of the headline
-workload on the host cores (a baseline, not a target).
+Also on the same JSON line: the roofline of the dominant kernel (decode,
+HBM-bound) from HIP events around each launch on the launch stream, the HBM
+traffic that rocprofv3 counters measured for that kernel (from
+profiles/decode_qwen3_traffic.json, null if the kernel source changed since),
+a plain-copy bandwidth measured in the same run, tokens/s, the other
+standard workloads (prefix-shared batch, long-context split-K, mixed chunked
+prefill + decode with the prefill's matrix-core utilisation), a parity
+sample against the CPU oracle, and the oracle itself timed on a bounded
+sample of the headline workload on one host core (a baseline, not a target).
+
+Other modes: --pmc-pass runs only the headline decode launches and one
+calibration copy of known size (for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE);
+--summarize-pmc FETCH_CSV WRITE_CSV turns two such runs into
+profiles/decode_qwen3_traffic.json.
 """
 
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -39,12 +52,22 @@ if ROOT not in sys.path:
 import paged_attention_kv_store_amd as pkv  # noqa: E402
 from paged_attention_kv_store_amd import workloads as W  # noqa: E402
 
-HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, vendor figure
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, vendor figure
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_qwen3_traffic.json")
+DECODE_SOURCES = ["decode.hip", "common.h", "device_utils.h"]
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def decode_source_hash():
+    h = hashlib.sha256()
+    for name in DECODE_SOURCES:
+        with open(os.path.join(ROOT, "paged_attention_kv_store_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 # --------------------------------------------------------------------------
@@ -59,8 +82,7 @@ def decode_bytes(b: W.PagedBatch, unique_blocks=False) -> float:
         # every distinct (block, row) read once: shared prefix blocks count once
         seen = {}
         for s, c in enumerate(ctx.tolist()):
-            nblk = -(-c // bs)
-            for j in range(nblk):
+            for j in range(-(-c // bs)):
                 rows = min(bs, c - j * bs)
                 blk = int(b.pool.block_tables[s, j])
                 seen[blk] = max(seen.get(blk, 0), rows)
@@ -88,42 +110,13 @@ def prefill_flops(b: W.PagedBatch, causal=True) -> float:
         rows = int(cu[c + 1] - cu[c])
         ctx = int(b.pool.context_lens[c])
         prior = ctx - rows
-        pairs = rows * prior + rows * (rows + 1) // 2 if causal else rows * ctx
-        tot += pairs
+        tot += rows * prior + rows * (rows + 1) // 2 if causal else rows * ctx
     return float(tot * b.num_q_heads * 4 * b.head_dim)
 
 
 # --------------------------------------------------------------------------
-# device-side workload state
+# timing helpers (HIP events on torch's current stream, where every launch goes)
 # --------------------------------------------------------------------------
-
-class DecodeCall:
-    def __init__(self, b: W.PagedBatch, partition, algo, device, tables=None, lens=None,
-                 k_cache=None, v_cache=None):
-        self.b = b
-        self.q = b.q
-        self.kc = b.k_cache if k_cache is None else k_cache
-        self.vc = b.v_cache if v_cache is None else v_cache
-        self.bt = tables if tables is not None else torch.as_tensor(b.pool.block_tables, device=device)
-        self.cl = lens if lens is not None else torch.as_tensor(b.pool.context_lens, device=device)
-        self.out = torch.empty_like(b.q)
-        self.partition = partition
-        self.algo = algo
-        self.max_ctx = b.max_ctx
-        need = pkv.decode_workspace_size(b.num_seqs, b.num_q_heads, b.head_dim, self.max_ctx,
-                                         partition) if partition else 0
-        self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
-
-    def store(self):
-        b = self.b
-        if b.k_new is not None:
-            pkv.kv_cache_store(b.k_new, b.v_new, self.kc, self.vc, b.slot_mapping)
-
-    def decode(self):
-        pkv.paged_attention_decode(self.out, self.q, self.kc, self.vc, self.bt, self.cl,
-                                   self.b.scale, self.max_ctx, partition_size=self.partition,
-                                   workspace=self.ws, algo=self.algo)
-
 
 def time_region(fn, steps, warmup):
     for _ in range(warmup):
@@ -139,19 +132,32 @@ def time_region(fn, steps, warmup):
     return start.elapsed_time(end) / steps   # ms
 
 
-def time_each_launch(fn, launches):
-    """Average duration of one launch of fn, events bracketing every launch
-    on the stream the kernels run on (torch's current stream)."""
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(launches)]
-    fn()
-    torch.cuda.synchronize()
-    for a, z in evs:
-        a.record()
+def gpu_hold(ms):
+    """Keep the stream busy for about `ms` so that the launches queued behind
+    it run back to back, independent of host launch latency."""
+    try:
+        torch.cuda._sleep(int(ms * 1e-3 * 2.4e9))
+    except Exception:  # pragma: no cover
+        pass
+
+
+def time_each_launch(fns, rounds):
+    """Average duration of one launch: the launches run back to back on the
+    stream (queued behind a GPU hold, so host overhead does not enter), one
+    HIP event pair brackets them all."""
+    for fn in fns:
         fn()
-        z.record()
     torch.cuda.synchronize()
-    return sum(a.elapsed_time(z) for a, z in evs) / launches
+    gpu_hold(5.0)
+    a = torch.cuda.Event(enable_timing=True)
+    z = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(rounds):
+        for fn in fns:
+            fn()
+    z.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(z) / (rounds * len(fns))
 
 
 def copy_bandwidth(device, nbytes=2 << 30):
@@ -159,6 +165,65 @@ def copy_bandwidth(device, nbytes=2 << 30):
     dst = torch.empty_like(src)
     ms = time_region(lambda: dst.copy_(src), 10, 3)
     return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+# --------------------------------------------------------------------------
+# headline workload
+# --------------------------------------------------------------------------
+
+class Layer:
+    def __init__(self, b: W.PagedBatch, bt, cl, partition, algo):
+        self.b = b
+        self.out = torch.empty_like(b.q)
+        self.store = pkv.StoreLaunch(b.k_new, b.v_new, b.k_cache, b.v_cache, b.slot_mapping)
+        self.decode = pkv.DecodeLaunch(self.out, b.q, b.k_cache, b.v_cache, bt, cl, b.scale,
+                                       b.max_ctx, partition_size=partition, algo=algo)
+
+
+def build_headline(device, layers, partition, algo):
+    wl = W.qwen3_decode(device=device, layers=layers)
+    b0 = wl.batches[0]
+    bt = torch.as_tensor(b0.pool.block_tables, device=device)
+    cl = torch.as_tensor(b0.pool.context_lens, device=device)
+    return wl, [Layer(b, bt, cl, partition, algo) for b in wl.batches]
+
+
+def capture_step(step, outs, replays=3):
+    """Capture `step` in a HIP graph and check replays against eager output."""
+    step()
+    torch.cuda.synchronize()
+    want = [o.clone() for o in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(replays):
+        for o in outs:
+            o.fill_(float("nan"))          # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for o, w in zip(outs, want):
+            if not torch.equal(o.view(torch.int16), w.view(torch.int16)):
+                raise RuntimeError("graph replay differs from the eager step")
+    return graph
+
+
+def load_traffic(dec_bytes):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("decode_source_hash") != decode_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
 
 
 # --------------------------------------------------------------------------
@@ -176,7 +241,7 @@ def cpu_baseline(b: W.PagedBatch, budget_s=12.0):
     bt, ctx = b.pool.block_tables, b.pool.context_lens
     e = b.q.element_size()
     done_bytes, t_used, seqs = 0.0, 0.0, 0
-    ctxm = threadpool_limits(limits=1) if threadpool_limits else None
+    limiter = threadpool_limits(limits=1) if threadpool_limits else None
     try:
         t0 = time.perf_counter()
         while t_used <= budget_s:
@@ -188,8 +253,8 @@ def cpu_baseline(b: W.PagedBatch, budget_s=12.0):
             seqs += 1
             t_used = time.perf_counter() - t0
     finally:
-        if ctxm is not None:
-            ctxm.__exit__(None, None, None)
+        if limiter is not None:
+            limiter.__exit__(None, None, None)
     return {"value": done_bytes / t_used / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{seqs} sequence decodes (layer 0's {b.num_seqs} sequences, cycled) by the "
                       f"float64 oracle in {t_used:.1f} s on one host core ({seqs / t_used:.1f} seq/s)"}
@@ -199,61 +264,155 @@ def cpu_baseline(b: W.PagedBatch, budget_s=12.0):
 # secondary workloads
 # --------------------------------------------------------------------------
 
-def secondary(device, steps, warmup, decode_algo):
+def secondary(device, steps, warmup, algo):
     res = {}
-    # prefix-shared Llama-shaped batch: one decode call
     b = W.llama_prefix(device=device).batches[0]
-    call = DecodeCall(b, 0, decode_algo, device)
-    ms = time_region(call.decode, steps, warmup)
+    bt = torch.as_tensor(b.pool.block_tables, device=device)
+    cl = torch.as_tensor(b.pool.context_lens, device=device)
+    dec = pkv.DecodeLaunch(torch.empty_like(b.q), b.q, b.k_cache, b.v_cache, bt, cl, b.scale,
+                           b.max_ctx, partition_size=0, algo=algo)
+    ms = time_region(dec, steps, warmup)
     ub, lb = decode_bytes(b, unique_blocks=True), decode_bytes(b)
     res["llama_prefix"] = {"ms": ms, "unique_GBps": ub / ms / 1e6, "logical_GBps": lb / ms / 1e6,
                            "pct_hbm_peak_unique": 100 * ub / ms / 1e6 / HBM_PEAK_GBS,
-                           "tokens_per_s": b.num_seqs / (ms * 1e-3)}
-    del call, b
-    # long-context split-K
+                           "tokens_per_s": b.num_seqs / (ms * 1e-3), "partition": 0}
+    del dec, b
     b = W.long_splitk(device=device).batches[0]
-    call = DecodeCall(b, 512, decode_algo, device)
-    ms = time_region(call.decode, steps, warmup)
+    bt = torch.as_tensor(b.pool.block_tables, device=device)
+    cl = torch.as_tensor(b.pool.context_lens, device=device)
+    dec = pkv.DecodeLaunch(torch.empty_like(b.q), b.q, b.k_cache, b.v_cache, bt, cl, b.scale,
+                           b.max_ctx, partition_size=512, algo=algo)
+    ms = time_region(dec, steps, warmup)
     by = decode_bytes(b)
-    res["long_splitk"] = {"ms": ms, "GBps": by / ms / 1e6,
-                          "pct_hbm_peak": 100 * by / ms / 1e6 / HBM_PEAK_GBS,
+    res["long_splitk"] = {"ms": ms, "GBps": by / ms / 1e6, "pct_hbm_peak": 100 * by / ms / 1e6 / HBM_PEAK_GBS,
                           "tokens_per_s": b.num_seqs / (ms * 1e-3), "partition": 512}
-    del call, b
-    # mixed: store, chunked prefill, decode on one stream
+    del dec, b
     wl = W.mixed(device=device)
-    pre, dec = wl.prefill, wl.batches[0]
-    bt_pre = torch.as_tensor(pre.pool.block_tables, device=device)
-    cu = torch.as_tensor(pre.cu_seqlens_q, device=device)
-    cl_pre = torch.as_tensor(pre.pool.context_lens, device=device)
-    out_pre = torch.empty_like(pre.q)
-    max_q = int(np.diff(pre.cu_seqlens_q).max())
-    dcall = DecodeCall(dec, 0, decode_algo, device)
-
-    def store():
-        pkv.kv_cache_store(pre.k_new, pre.v_new, pre.k_cache, pre.v_cache, pre.slot_mapping)
-
-    def prefill():
-        pkv.paged_attention_prefill_chunk(out_pre, pre.q, pre.k_cache, pre.v_cache, bt_pre, cu,
-                                          cl_pre, pre.scale, max_q, pre.max_ctx, causal=True)
-
-    entry = {}
+    pre, db = wl.prefill, wl.batches[0]
+    store = pkv.StoreLaunch(pre.k_new, pre.v_new, pre.k_cache, pre.v_cache, pre.slot_mapping)
+    prefill = pkv.PrefillLaunch(torch.empty_like(pre.q), pre.q, pre.k_cache, pre.v_cache,
+                                torch.as_tensor(pre.pool.block_tables, device=device),
+                                torch.as_tensor(pre.cu_seqlens_q, device=device),
+                                torch.as_tensor(pre.pool.context_lens, device=device), pre.scale,
+                                int(np.diff(pre.cu_seqlens_q).max()), pre.max_ctx, causal=True)
+    dec = pkv.DecodeLaunch(torch.empty_like(db.q), db.q, db.k_cache, db.v_cache,
+                           torch.as_tensor(db.pool.block_tables, device=device),
+                           torch.as_tensor(db.pool.context_lens, device=device), db.scale,
+                           db.max_ctx, partition_size=0, algo=algo)
     t_store = time_region(store, steps, warmup)
-    t_dec = time_region(dcall.decode, steps, warmup)
-    entry["store_ms"] = t_store
-    entry["store_GBps"] = store_bytes(pre) / t_store / 1e6
-    entry["decode_ms"] = t_dec
-    entry["decode_GBps"] = decode_bytes(dec) / t_dec / 1e6
-    try:
-        t_pre = time_region(prefill, steps, warmup)
-        fl = prefill_flops(pre)
-        entry["prefill_ms"] = t_pre
-        entry["prefill_TFLOPs"] = fl / t_pre / 1e9
-        entry["prefill_mfma_util_pct"] = 100 * fl / t_pre / 1e9 / BF16_MFMA_PEAK_TFLOPS
-        entry["tokens_per_s"] = 4224 / ((t_store + t_pre + t_dec) * 1e-3)
-    except pkv.PkvError as exc:
-        entry["prefill"] = f"unavailable: {exc}"
-    res["mixed"] = entry
+    t_pre = time_region(prefill, steps, warmup)
+    t_dec = time_region(dec, steps, warmup)
+    fl = prefill_flops(pre)
+    res["mixed"] = {"store_ms": t_store, "store_GBps": store_bytes(pre) / t_store / 1e6,
+                    "prefill_ms": t_pre, "prefill_TFLOPs": fl / t_pre / 1e9,
+                    "prefill_mfma_util_pct": 100 * fl / t_pre / 1e9 / BF16_MFMA_PEAK_TFLOPS,
+                    "decode_ms": t_dec, "decode_GBps": decode_bytes(db) / t_dec / 1e6,
+                    "tokens_per_s": 4224 / ((t_store + t_pre + t_dec) * 1e-3)}
     return res
+
+
+# --------------------------------------------------------------------------
+# counter passes
+# --------------------------------------------------------------------------
+
+CALIB_TOKENS = 65536              # calibration store: 65536 rows of 8 x 128 bf16 (2 KiB) each
+
+
+def calib_bytes():
+    """Bytes the calibration store reads and writes (K and V rows; slots read)."""
+    row = 8 * 128 * 2
+    return 2 * CALIB_TOKENS * row + 4 * CALIB_TOKENS, 2 * CALIB_TOKENS * row
+
+
+def pmc_pass(device, layers):
+    """Headline decode launches once each, then a plain copy of known size:
+    a kv_cache_store of 65536 new rows into a pool of exactly as many slots
+    (identity slots), i.e. 256 MiB read and 256 MiB written."""
+    wl, lyr = build_headline(device, layers, 0, "auto")
+    for ly in lyr:
+        ly.store()
+    torch.cuda.synchronize()
+    for ly in lyr:
+        ly.decode()
+    torch.cuda.synchronize()
+    k = torch.empty((CALIB_TOKENS, 8, 128), dtype=torch.bfloat16, device=device).normal_()
+    v = torch.empty_like(k).normal_()
+    kc = torch.empty((CALIB_TOKENS // 16, 16, 8, 128), dtype=torch.bfloat16, device=device)
+    vc = torch.empty_like(kc)
+    slots = torch.arange(CALIB_TOKENS, dtype=torch.int32, device=device)
+    torch.cuda.synchronize()
+    pkv.kv_cache_store(k, v, kc, vc, slots)
+    torch.cuda.synchronize()
+    print(json.dumps({"pmc_pass": "done", "decode_launches": len(lyr),
+                      "calibration_read_write_bytes": calib_bytes()}))
+
+
+def summarize_pmc(fetch_csv, write_csv):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the decode launches, each
+    scaled by (known bytes / counter reading) of the calibration store, which
+    is the last kv_store_kernel dispatch of a --pmc-pass run."""
+    def per_kernel(path, counter):
+        dec, store = [], []
+        for r in csv.DictReader(open(path)):
+            if r.get("Counter_Name") != counter:
+                continue
+            name, val = r["Kernel_Name"], float(r["Counter_Value"]) * 1024.0   # KiB -> bytes
+            if "decode_mfma_kernel" in name:
+                dec.append(val)
+            elif "kv_store_kernel" in name:
+                store.append((int(r["Dispatch_Id"]), val))
+        return dec, max(store)[1]
+    f_dec, f_cal = per_kernel(fetch_csv, "FETCH_SIZE")
+    w_dec, w_cal = per_kernel(write_csv, "WRITE_SIZE")
+    read_known, write_known = calib_bytes()
+    fr, fw = read_known / f_cal, write_known / w_cal
+    wl = W.qwen3_decode(device="cpu", layers=1)
+    out = {
+        "kernel": "decode_mfma_kernel<128, 4> (single pass), qwen3-shaped layer",
+        "decode_source_hash": decode_source_hash(),
+        "fetch_bytes_raw_per_launch": float(np.mean(f_dec)),
+        "write_bytes_raw_per_launch": float(np.mean(w_dec)),
+        "calibration": {"kernel": "kv_store_kernel, 65536 rows of 2 KiB, identity slots",
+                        "read_bytes": read_known, "write_bytes": write_known,
+                        "fetch_raw": f_cal, "write_raw": w_cal,
+                        "fetch_factor": fr, "write_factor": fw},
+        "hbm_bytes_per_launch": float(np.mean(f_dec)) * fr + float(np.mean(w_dec)) * fw,
+        "algorithmic_bytes_per_launch": decode_bytes(wl.batches[0]),
+        "launches_averaged": len(f_dec),
+    }
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
+def summarize_trace(stats_csv, trace_csv, out_md, command):
+    """Short markdown summary of a rocprofv3 --kernel-trace --stats run."""
+    stats = list(csv.DictReader(open(stats_csv)))
+    lines = [f"# Kernel trace: {os.path.basename(out_md)[:-3]}", "",
+             "Command (from the repository root on one MI355X):", "", "```", command, "```", "",
+             "## rocprofv3 --stats (all kernels of the run)", "",
+             "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
+    for r in stats[:14]:
+        name = r["Name"].split("(")[0].replace("void ", "")[:70]
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.2f} |")
+    groups = {}
+    for r in csv.DictReader(open(trace_csv)):
+        name = r["Kernel_Name"]
+        if "pkv::" not in name:
+            continue
+        key = (name.split("(")[0].replace("void ", ""), r["Grid_Size_X"], r["Grid_Size_Y"], r["Grid_Size_Z"])
+        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines += ["", "## This library's kernels by launch shape (from the kernel trace)", "",
+              "| kernel | grid (threads x, y, z) | launches | median us | mean us |", "|---|---|---|---|---|"]
+    for (name, gx, gy, gz), v in groups.items():
+        v.sort()
+        lines.append(f"| `{name}` | {gx}, {gy}, {gz} | {len(v)} | {v[len(v) // 2]:.2f} | {sum(v) / len(v):.2f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote {out_md}")
 
 
 # --------------------------------------------------------------------------
@@ -263,69 +422,73 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--partition", type=int, default=-1,
-                    help="decode partition size for the headline step (-1: built-in choice)")
+    ap.add_argument("--partition", type=int, default=0, help="decode partition size for the step")
     ap.add_argument("--algo", default="auto", choices=sorted(pkv.DECODE_ALGOS))
     ap.add_argument("--layers", type=int, default=28)
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replay")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-pass", action="store_true")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--summarize-trace", nargs=4, metavar=("STATS_CSV", "TRACE_CSV", "OUT_MD", "COMMAND"))
     args = ap.parse_args()
 
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(decode would shard by sequence or kv-head with no exchange; see the design notes)",
-              file=sys.stderr)
+        print("bench.py measures one GPU: this library has no multi-GPU path "
+              "(decode would shard by sequence or kv-head with no exchange)", file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     device = torch.device("cuda:0")
     torch.cuda.set_device(device)
-    partition = 0 if args.partition < 0 else args.partition
+    if args.pmc_pass:
+        pmc_pass(device, args.layers)
+        return
 
     log("generating the qwen3-shaped decode workload on the GPU")
-    wl = W.qwen3_decode(device=device, layers=args.layers)
-    calls = [DecodeCall(b, partition, args.algo, device) for b in wl.batches]
-    shared_bt, shared_cl = calls[0].bt, calls[0].cl
-    for c in calls[1:]:
-        c.bt, c.cl = shared_bt, shared_cl
+    wl, lyr = build_headline(device, args.layers, args.partition, args.algo)
     b0 = wl.batches[0]
-    layer_bytes = decode_bytes(b0) + store_bytes(b0)
-    step_bytes = layer_bytes * len(calls)
+    step_bytes = (decode_bytes(b0) + store_bytes(b0)) * len(lyr)
 
     def step():
-        for c in calls:
-            c.store()
-            c.decode()
+        for ly in lyr:
+            ly.store()
+            ly.decode()
 
-    log(f"timing {args.steps} steps ({len(calls)} layers each) after {args.warmup} warmup")
-    torch.cuda.synchronize()
-    ms = time_region(step, args.steps, args.warmup)
+    if args.eager:
+        run = step
+    else:
+        log("capturing the step in a HIP graph; checking replays against the eager step")
+        graph = capture_step(step, [ly.out for ly in lyr])
+        run = graph.replay
+    log(f"timing {args.steps} steps ({len(lyr)} layers each) after {args.warmup} warmup")
+    ms = time_region(run, args.steps, args.warmup)
     value = step_bytes / (ms * 1e-3) / 1e9
 
-    # dominant kernel: decode on one layer's inputs, events around each launch
+    # dominant kernel: decode, one launch per layer, events around each launch
     dec_bytes = decode_bytes(b0)
-    launches = 28 * 4
-    rot = [0]
-
-    def one_decode():
-        calls[rot[0] % len(calls)].decode()
-        rot[0] += 1
-
-    dec_ms = time_each_launch(one_decode, launches)
-    store_ms = time_each_launch(lambda: calls[0].store(), 50)
+    dec_ms = time_each_launch([ly.decode for ly in lyr], 4)
+    store_ms = time_each_launch([ly.store for ly in lyr], 2)
     copy_gbps = copy_bandwidth(device)
+    achieved = dec_bytes / (dec_ms * 1e-3) / 1e9
 
-    # parity sample of the timed run's output (layer 0) against the oracle
+    # parity sample of layer 0's output against the oracle
     import oracle
     seqs = [0, 17, 33, 59]
     okc, ovc = oracle.kv_cache_store(W.host_bits(b0.k_new), W.host_bits(b0.v_new),
                                      W.host_bits(b0.k_cache), W.host_bits(b0.v_cache),
                                      W.host_bits(b0.slot_mapping), b0.block_size)
-    calls[0].decode()
+    run()
     torch.cuda.synchronize()
     want = oracle.paged_attention_decode(W.host_bits(b0.q)[seqs], okc, ovc,
                                          b0.pool.block_tables[seqs], b0.pool.context_lens[seqs],
                                          b0.scale, b0.block_size)
-    got = calls[0].out.float().cpu().double().numpy()[seqs]
+    got = lyr[0].out.float().cpu().double().numpy()[seqs]
     parity_err = float(np.abs(got - want).max())
     del okc, ovc
 
@@ -344,30 +507,31 @@ def main():
         "data": "synthetic",
         "config": {"workload": "qwen3_decode", "num_seqs": 60, "context_lens": "U{64..1024}",
                    "num_q_heads": 16, "num_kv_heads": 8, "head_dim": 128, "block_size": 16,
-                   "layers": len(calls), "partition_size": partition, "algo": args.algo,
+                   "layers": len(lyr), "partition_size": args.partition, "algo": args.algo,
                    "step": "per layer: kv_cache_store of 60 new rows + paged_attention_decode",
+                   "launch": "eager" if args.eager else "hip graph replay",
                    "parallelism": "single GPU"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(b0.num_seqs / (ms * 1e-3), 1),
         "copy_GBps_measured": round(copy_gbps, 1),
-        "roofline": {"bound": "hbm", "kernel": "decode (one layer, one launch)",
-                     "achieved": round(dec_bytes / (dec_ms * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s",
-                     "frac": round(dec_bytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": None, "avg_launch_us": round(dec_ms * 1e3, 2),
+        "roofline": {"bound": "hbm", "kernel": "decode_mfma_kernel (one layer per launch)",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(dec_bytes),
+                     "avg_launch_us": round(dec_ms * 1e3, 2),
                      "algorithmic_bytes_per_launch": dec_bytes},
         "store_avg_launch_us": round(store_ms * 1e3, 2),
         "parity_sample_max_abs_err": parity_err,
     }
     if not args.no_secondary:
-        del calls, wl
+        del lyr, wl
+        if not args.eager:
+            del graph, run
         torch.cuda.empty_cache()
         log("secondary workloads")
         result["secondary"] = secondary(device, max(5, args.steps // 2), 3, args.algo)
     if not args.no_cpu_baseline:
         log("oracle baseline on the host")
-        wl1 = W.qwen3_decode(device="cpu", layers=1)
-        result["cpu_baseline"] = cpu_baseline(wl1.batches[0])
+        result["cpu_baseline"] = cpu_baseline(W.qwen3_decode(device="cpu", layers=1).batches[0])
     print(json.dumps(result), flush=True)
 
 

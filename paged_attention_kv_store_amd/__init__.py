@@ -8,7 +8,10 @@ library; the first call does, and raises if it has not been built.
 
 from .binding import (  # noqa: F401
     DECODE_ALGOS,
+    DecodeLaunch,
     PkvError,
+    PrefillLaunch,
+    StoreLaunch,
     decode_workspace_size,
     kv_cache_store,
     lib,

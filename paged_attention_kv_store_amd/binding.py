@@ -179,3 +179,88 @@ def paged_attention_prefill_chunk(out, q, k_cache, v_cache, block_tables, cu_seq
         _ptr(context_lens), n, tq, int(max_q_len), block_tables.shape[1], int(max_context_len),
         nb, bs, hq, hkv, d, float(scale), int(bool(causal)), _dtype_code(q), _stream(stream)))
     return out
+
+
+# --------------------------------------------------------------------------
+# Prepared launches: arguments checked and marshalled once, then each call is
+# a single C-ABI call with the cached arguments on the current (or a given)
+# stream. For serving loops and graph capture, where per-call Python work
+# would otherwise dominate short kernels.
+# --------------------------------------------------------------------------
+
+class _Prepared:
+    _fn = None
+    _args = ()
+
+    def __call__(self, stream=None):
+        _check(getattr(lib(), self._fn)(*self._args, _stream(stream)))
+
+
+class StoreLaunch(_Prepared):
+    """kv_cache_store with fixed tensors."""
+
+    def __init__(self, k, v, k_cache, v_cache, slot_mapping):
+        _dev(k, v, k_cache, v_cache, slot_mapping)
+        _need(k.dim() == 3 and v.shape == k.shape, "k, v must be [T, Hkv, D]")
+        _need(k_cache.dim() == 4 and v_cache.shape == k_cache.shape, "caches must be [NB, bs, Hkv, D]")
+        _need(k_cache.shape[2:] == k.shape[1:], "cache and new rows disagree on heads/dims")
+        _need(slot_mapping.dtype == torch.int32 and slot_mapping.shape == (k.shape[0],),
+              "slot_mapping must be int32 [T]")
+        _need(k.dtype == v.dtype == k_cache.dtype == v_cache.dtype, "dtypes must match")
+        nb, bs, hkv, d = k_cache.shape
+        self._keep = (k, v, k_cache, v_cache, slot_mapping)
+        self._fn = "pkv_kv_cache_store"
+        self._args = (_ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping),
+                      k.shape[0], nb, bs, hkv, d, _dtype_code(k))
+
+
+class DecodeLaunch(_Prepared):
+    """paged_attention_decode with fixed tensors; owns its split-K workspace."""
+
+    def __init__(self, out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                 max_context_len, partition_size=0, algo="auto", workspace=None):
+        _dev(out, q, k_cache, v_cache, block_tables, context_lens)
+        _need(q.dim() == 3 and out.shape == q.shape and out.dtype == q.dtype, "q/out must be [S, Hq, D]")
+        _need(k_cache.dim() == 4 and v_cache.shape == k_cache.shape, "caches must be [NB, bs, Hkv, D]")
+        _need(q.dtype == k_cache.dtype == v_cache.dtype, "dtypes must match")
+        _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
+              and block_tables.shape[0] == q.shape[0], "block_tables must be int32 [S, MB]")
+        _need(context_lens.dtype == torch.int32 and context_lens.shape == (q.shape[0],),
+              "context_lens must be int32 [S]")
+        s, hq, d = q.shape
+        nb, bs, hkv, _ = k_cache.shape
+        need = decode_workspace_size(s, hq, d, max_context_len, partition_size) if partition_size else 0
+        if need and workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        self._keep = (out, q, k_cache, v_cache, block_tables, context_lens, workspace)
+        self._fn = "pkv_paged_attention_decode"
+        self._args = (_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                      _ptr(context_lens), s, block_tables.shape[1], int(max_context_len), nb, bs,
+                      hq, hkv, d, float(scale), int(partition_size), _ptr(workspace), ws_bytes,
+                      _dtype_code(q), DECODE_ALGOS[algo])
+
+
+class PrefillLaunch(_Prepared):
+    """paged_attention_prefill_chunk with fixed tensors."""
+
+    def __init__(self, out, q, k_cache, v_cache, block_tables, cu_seqlens_q, context_lens, scale,
+                 max_q_len, max_context_len, causal=True):
+        _dev(out, q, k_cache, v_cache, block_tables, cu_seqlens_q, context_lens)
+        _need(q.dim() == 3 and out.shape == q.shape and out.dtype == q.dtype, "q/out must be [Tq, Hq, D]")
+        _need(k_cache.dim() == 4 and v_cache.shape == k_cache.shape, "caches must be [NB, bs, Hkv, D]")
+        _need(q.dtype == k_cache.dtype == v_cache.dtype, "dtypes must match")
+        n = block_tables.shape[0]
+        _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2, "block_tables must be int32")
+        _need(cu_seqlens_q.dtype == torch.int32 and cu_seqlens_q.shape == (n + 1,),
+              "cu_seqlens_q must be int32 [S+1]")
+        _need(context_lens.dtype == torch.int32 and context_lens.shape == (n,),
+              "context_lens must be int32 [S]")
+        tq, hq, d = q.shape
+        nb, bs, hkv, _ = k_cache.shape
+        self._keep = (out, q, k_cache, v_cache, block_tables, cu_seqlens_q, context_lens)
+        self._fn = "pkv_paged_attention_prefill_chunk"
+        self._args = (_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                      _ptr(cu_seqlens_q), _ptr(context_lens), n, tq, int(max_q_len),
+                      block_tables.shape[1], int(max_context_len), nb, bs, hq, hkv, d,
+                      float(scale), int(bool(causal)), _dtype_code(q))
