@@ -178,6 +178,9 @@ class Layer:
         self.store = pkv.StoreLaunch(b.k_new, b.v_new, b.k_cache, b.v_cache, b.slot_mapping)
         self.decode = pkv.DecodeLaunch(self.out, b.q, b.k_cache, b.v_cache, bt, cl, b.scale,
                                        b.max_ctx, partition_size=partition, algo=algo)
+        self.fused = pkv.DecodeStoreLaunch(self.out, b.q, b.k_cache, b.v_cache, bt, cl, b.k_new,
+                                           b.v_new, b.slot_mapping, b.scale, b.max_ctx,
+                                           partition_size=partition, algo=algo)
 
 
 def build_headline(device, layers, partition, algo):
@@ -426,6 +429,8 @@ def main():
     ap.add_argument("--algo", default="auto", choices=sorted(pkv.DECODE_ALGOS))
     ap.add_argument("--layers", type=int, default=28)
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replay")
+    ap.add_argument("--unfused", action="store_true",
+                    help="store and decode as two launches per layer instead of the fused call")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-pass", action="store_true")
@@ -455,10 +460,15 @@ def main():
     b0 = wl.batches[0]
     step_bytes = (decode_bytes(b0) + store_bytes(b0)) * len(lyr)
 
-    def step():
-        for ly in lyr:
-            ly.store()
-            ly.decode()
+    if args.unfused:
+        def step():
+            for ly in lyr:
+                ly.store()
+                ly.decode()
+    else:
+        def step():
+            for ly in lyr:
+                ly.fused()
 
     if args.eager:
         run = step
@@ -470,9 +480,9 @@ def main():
     ms = time_region(run, args.steps, args.warmup)
     value = step_bytes / (ms * 1e-3) / 1e9
 
-    # dominant kernel: decode, one launch per layer, events around each launch
-    dec_bytes = decode_bytes(b0)
-    dec_ms = time_each_launch([ly.decode for ly in lyr], 4)
+    # dominant kernel: decode (fused with the store unless --unfused), one launch per layer
+    dec_bytes = decode_bytes(b0) + (0.0 if args.unfused else store_bytes(b0))
+    dec_ms = time_each_launch([ly.decode if args.unfused else ly.fused for ly in lyr], 4)
     store_ms = time_each_launch([ly.store for ly in lyr], 2)
     copy_gbps = copy_bandwidth(device)
     achieved = dec_bytes / (dec_ms * 1e-3) / 1e9
@@ -508,13 +518,17 @@ def main():
         "config": {"workload": "qwen3_decode", "num_seqs": 60, "context_lens": "U{64..1024}",
                    "num_q_heads": 16, "num_kv_heads": 8, "head_dim": 128, "block_size": 16,
                    "layers": len(lyr), "partition_size": args.partition, "algo": args.algo,
-                   "step": "per layer: kv_cache_store of 60 new rows + paged_attention_decode",
+                   "step": ("per layer: kv_cache_store of 60 new rows, then paged_attention_decode"
+                            if args.unfused else
+                            "per layer: paged_attention_decode_store (store of 60 new rows fused)"),
                    "launch": "eager" if args.eager else "hip graph replay",
                    "parallelism": "single GPU"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(b0.num_seqs / (ms * 1e-3), 1),
         "copy_GBps_measured": round(copy_gbps, 1),
-        "roofline": {"bound": "hbm", "kernel": "decode_mfma_kernel (one layer per launch)",
+        "roofline": {"bound": "hbm",
+                     "kernel": "decode_mfma_kernel (one layer per launch%s)" % (
+                         "" if args.unfused else ", store fused"),
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(dec_bytes),
                      "avg_launch_us": round(dec_ms * 1e3, 2),

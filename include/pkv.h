@@ -138,6 +138,31 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
                                pkv_dtype dtype, int32_t algo, void* stream);
 
 /*
+ * paged_attention_decode_store: kv_cache_store of one new row per sequence
+ * followed by paged_attention_decode, in one launch. For each sequence s
+ * with 0 <= slot_mapping[s] < num_blocks * block_size, k_new[s] and v_new[s]
+ * ([num_seqs, num_kv_heads, head_dim], the dtype of q) are written to that
+ * slot of k_cache / v_cache, and decode then sees them as the sequence's
+ * newest token. Precondition (the usual decode step): slot_mapping[s] is the
+ * slot of position context_lens[s] - 1 under block_tables[s]; the kernel
+ * uses the new row for that position straight from k_new / v_new. A negative
+ * slot stores nothing and leaves position ctx-1 as the cache holds it. The
+ * other arguments, the results and the errors are those of
+ * pkv_paged_attention_decode; k_new, v_new and slot_mapping must be non-null
+ * (slot_mapping 4-byte, the rows 16-byte aligned).
+ */
+int pkv_paged_attention_decode_store(void* out, const void* q, void* k_cache, void* v_cache,
+                                     const int32_t* block_tables, const int32_t* context_lens,
+                                     const void* k_new, const void* v_new,
+                                     const int32_t* slot_mapping, int32_t num_seqs,
+                                     int32_t max_blocks_per_seq, int32_t max_context_len,
+                                     int32_t num_blocks, int32_t block_size,
+                                     int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, float scale, int32_t partition_size,
+                                     void* workspace, size_t workspace_bytes,
+                                     pkv_dtype dtype, int32_t algo, void* stream);
+
+/*
  * paged_attention_prefill_chunk: attention of packed query chunks over their
  * paged contexts. Chunk c owns q rows cu_seqlens_q[c] .. cu_seqlens_q[c+1]-1
  * (L_c rows); context_lens[c] >= L_c counts its cached tokens plus its own

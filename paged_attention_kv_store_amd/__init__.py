@@ -9,6 +9,7 @@ library; the first call does, and raises if it has not been built.
 from .binding import (  # noqa: F401
     DECODE_ALGOS,
     DecodeLaunch,
+    DecodeStoreLaunch,
     PkvError,
     PrefillLaunch,
     StoreLaunch,
@@ -17,5 +18,6 @@ from .binding import (  # noqa: F401
     lib,
     library_path,
     paged_attention_decode,
+    paged_attention_decode_store,
     paged_attention_prefill_chunk,
 )

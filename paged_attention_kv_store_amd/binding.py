@@ -34,6 +34,9 @@ _SIGNATURES = {
     "pkv_paged_attention_decode": ([_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                     _i32, _i32, _i32, ctypes.c_float, _i32, _vp, ctypes.c_size_t,
                                     ctypes.c_int, _i32, _vp], ctypes.c_int),
+    "pkv_paged_attention_decode_store": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                          _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _i32,
+                                          _vp, ctypes.c_size_t, ctypes.c_int, _i32, _vp], ctypes.c_int),
     "pkv_paged_attention_prefill_chunk": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                                            _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                            ctypes.c_float, _i32, ctypes.c_int, _vp], ctypes.c_int),
@@ -158,6 +161,17 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     return out
 
 
+def paged_attention_decode_store(out, q, k_cache, v_cache, block_tables, context_lens, k_new,
+                                 v_new, slot_mapping, scale, max_context_len, partition_size=0,
+                                 workspace=None, algo="auto", stream=None):
+    """Store one new K/V row per sequence (at its slot, which must be position
+    context_lens[s]-1) and run decode, in one launch; writes out and the caches."""
+    DecodeStoreLaunch(out, q, k_cache, v_cache, block_tables, context_lens, k_new, v_new,
+                      slot_mapping, scale, max_context_len, partition_size, algo,
+                      workspace)(stream)
+    return out
+
+
 def paged_attention_prefill_chunk(out, q, k_cache, v_cache, block_tables, cu_seqlens_q,
                                   context_lens, scale, max_q_len, max_context_len, causal=True,
                                   stream=None):
@@ -264,3 +278,23 @@ class PrefillLaunch(_Prepared):
                       _ptr(cu_seqlens_q), _ptr(context_lens), n, tq, int(max_q_len),
                       block_tables.shape[1], int(max_context_len), nb, bs, hq, hkv, d,
                       float(scale), int(bool(causal)), _dtype_code(q))
+
+
+class DecodeStoreLaunch(_Prepared):
+    """paged_attention_decode_store with fixed tensors; owns its split-K workspace."""
+
+    def __init__(self, out, q, k_cache, v_cache, block_tables, context_lens, k_new, v_new,
+                 slot_mapping, scale, max_context_len, partition_size=0, algo="auto",
+                 workspace=None):
+        base = DecodeLaunch(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                            max_context_len, partition_size, algo, workspace)
+        _dev(k_new, v_new, slot_mapping)
+        s, _, d = q.shape
+        hkv = k_cache.shape[2]
+        _need(k_new.shape == (s, hkv, d) and v_new.shape == k_new.shape, "k_new, v_new must be [S, Hkv, D]")
+        _need(k_new.dtype == v_new.dtype == q.dtype, "dtypes must match")
+        _need(slot_mapping.dtype == torch.int32 and slot_mapping.shape == (s,), "slot_mapping must be int32 [S]")
+        a = base._args
+        self._keep = base._keep + (k_new, v_new, slot_mapping)
+        self._fn = "pkv_paged_attention_decode_store"
+        self._args = a[:6] + (_ptr(k_new), _ptr(v_new), _ptr(slot_mapping)) + a[6:]

@@ -8,6 +8,7 @@ Packed-fp32 instructions are disabled for the device code.
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -34,19 +35,38 @@ def sources():
                   if f.endswith((".hip", ".cpp")))
 
 
+def _scratch_users(remarks):
+    """Kernels whose resource-usage remarks report scratch (private) memory."""
+    users, name = [], None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and int(m.group(1)) > 0 and name:
+            users.append((name, int(m.group(1))))
+    return users
+
+
 def _compile(src, verbose):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, "-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the packed-fp32 feature; that warning is noise
     noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
+    lines = [l for l in res.stderr.splitlines() if noise not in l]
+    err = "\n".join(l for l in lines if "kernel-resource-usage" not in l)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{err}")
     if err.strip() and verbose:
         print(err, file=sys.stderr)
+    # A kernel that spills to or keeps arrays in scratch memory runs far
+    # slower than intended; treat it as a build error.
+    users = _scratch_users("\n".join(lines))
+    if users:
+        raise RuntimeError(f"kernels in {src} use scratch memory: {users}")
     return obj
 
 

@@ -102,16 +102,17 @@ extern "C" size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_head
   return (size_t)num_seqs * num_q_heads * nparts * (head_dim + 2) * sizeof(float);
 }
 
-extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
-                                          const void* v_cache, const int32_t* block_tables,
-                                          const int32_t* context_lens, int32_t num_seqs,
-                                          int32_t max_blocks_per_seq, int32_t max_context_len,
-                                          int32_t num_blocks, int32_t block_size,
-                                          int32_t num_q_heads, int32_t num_kv_heads,
-                                          int32_t head_dim, float scale, int32_t partition_size,
-                                          void* workspace, size_t workspace_bytes,
-                                          pkv_dtype dtype, int32_t algo, void* stream) {
-  const char* fn = "pkv_paged_attention_decode";
+namespace {
+
+// Shared by the plain and the store-fused decode entry points; k_new, v_new
+// and new_slots are null for the plain one.
+int decode_impl(const char* fn, void* out, const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* block_tables, const int32_t* context_lens, const void* k_new,
+                const void* v_new, const int32_t* new_slots, int32_t num_seqs,
+                int32_t max_blocks_per_seq, int32_t max_context_len, int32_t num_blocks,
+                int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                float scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
+                int dtype, int32_t algo, void* stream) {
   if (num_seqs < 0) return fail(PKV_EINVAL, "%s: num_seqs < 0", fn);
   if (int rc = check_common(fn, num_blocks, block_size, num_kv_heads, head_dim, dtype)) return rc;
   if (num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
@@ -147,6 +148,9 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* 
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 4) ||
       !aligned(block_tables, 4) || !aligned(context_lens, 4))
     return fail(PKV_EINVAL, "%s: q and caches must be 16-byte aligned; out and index arrays 4-byte", fn);
+  const bool fused = new_slots != nullptr;
+  if (fused && (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(new_slots, 4)))
+    return fail(PKV_EINVAL, "%s: k_new and v_new must be non-null and 16-byte aligned", fn);
 
   int32_t part;
   int64_t nparts;
@@ -171,6 +175,9 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* 
   p.partition_size = part;
   p.num_partitions = (int32_t)nparts;
   p.ws_m = p.ws_l = p.ws_o = nullptr;
+  p.k_new = fused ? k_new : nullptr;
+  p.v_new = fused ? v_new : nullptr;
+  p.new_slots = fused ? new_slots : nullptr;
   if (nparts > 1) {
     const size_t need = pkv_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len,
                                                   partition_size);
@@ -190,6 +197,43 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* 
   if (e != hipSuccess) return hip_status(e, fn);
   if (nparts > 1) return hip_status(pkv::launch_splitk_reduce(p, head_dim, dtype, st), fn);
   return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
+                                          const void* v_cache, const int32_t* block_tables,
+                                          const int32_t* context_lens, int32_t num_seqs,
+                                          int32_t max_blocks_per_seq, int32_t max_context_len,
+                                          int32_t num_blocks, int32_t block_size,
+                                          int32_t num_q_heads, int32_t num_kv_heads,
+                                          int32_t head_dim, float scale, int32_t partition_size,
+                                          void* workspace, size_t workspace_bytes,
+                                          pkv_dtype dtype, int32_t algo, void* stream) {
+  return decode_impl("pkv_paged_attention_decode", out, q, k_cache, v_cache, block_tables,
+                     context_lens, nullptr, nullptr, nullptr, num_seqs, max_blocks_per_seq,
+                     max_context_len, num_blocks, block_size, num_q_heads, num_kv_heads, head_dim,
+                     scale, partition_size, workspace, workspace_bytes, dtype, algo, stream);
+}
+
+extern "C" int pkv_paged_attention_decode_store(void* out, const void* q, void* k_cache,
+                                                void* v_cache, const int32_t* block_tables,
+                                                const int32_t* context_lens, const void* k_new,
+                                                const void* v_new, const int32_t* slot_mapping,
+                                                int32_t num_seqs, int32_t max_blocks_per_seq,
+                                                int32_t max_context_len, int32_t num_blocks,
+                                                int32_t block_size, int32_t num_q_heads,
+                                                int32_t num_kv_heads, int32_t head_dim, float scale,
+                                                int32_t partition_size, void* workspace,
+                                                size_t workspace_bytes, pkv_dtype dtype, int32_t algo,
+                                                void* stream) {
+  const char* fn = "pkv_paged_attention_decode_store";
+  if (num_seqs > 0 && (!k_new || !v_new || !slot_mapping))
+    return fail(PKV_EINVAL, "%s: null pointer", fn);
+  return decode_impl(fn, out, q, k_cache, v_cache, block_tables, context_lens, k_new, v_new,
+                     slot_mapping, num_seqs, max_blocks_per_seq, max_context_len, num_blocks,
+                     block_size, num_q_heads, num_kv_heads, head_dim, scale, partition_size,
+                     workspace, workspace_bytes, dtype, algo, stream);
 }
 
 extern "C" int pkv_paged_attention_prefill_chunk(void* out, const void* q, const void* k_cache,

@@ -49,6 +49,11 @@ struct DecodeParams {
   float* ws_m;               // [num_seqs, num_q_heads, num_partitions]
   float* ws_l;               // same
   float* ws_o;               // [num_seqs, num_q_heads, num_partitions, head_dim]
+  // Fused store of one new row per sequence at position ctx-1 (all null when
+  // not fused): k_new/v_new [num_seqs, num_kv_heads, head_dim], new_slots [num_seqs].
+  const void* k_new;
+  const void* v_new;
+  const int32_t* new_slots;
 };
 
 struct PrefillParams {

@@ -114,6 +114,28 @@ __device__ __forceinline__ int64_t tile_row0(const int32_t* bt, int tok0, int bs
   return (int64_t)blk * bs + (tok0 - lb * bs);
 }
 
+// The sequence's new row in a fused store + decode: stored at `slot` and
+// standing for logical position `pos` = ctx-1; `mine` marks the wave of the
+// workgroup whose tiles include that position (tile (pos - t0)/16 belongs to
+// wave tile % kWaves).
+struct NewRow {
+  bool mine;
+  int slot;
+  int pos;
+};
+
+__device__ __forceinline__ NewRow new_row_of(const DecodeParams& p, int s, int ctx, int t0, int t1,
+                                             int w) {
+  NewRow r{false, -1, ctx - 1};
+  if (p.new_slots == nullptr) return r;
+  const int slot = p.new_slots[s];
+  if (slot < 0 || (int64_t)slot >= (int64_t)p.num_blocks * p.block_size) return r;  // padding / outside
+  if (r.pos < t0 || r.pos >= t1) return r;                                            // another partition
+  r.slot = slot;
+  r.mine = ((r.pos - t0) / kTile) % kWaves == w;
+  return r;
+}
+
 // ---------------------------------------------------------------------------
 // Vector-ALU decode
 // ---------------------------------------------------------------------------
@@ -194,6 +216,21 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
   }
   bool poisoned = false;
 
+  // Fused store: the sequence's new row (position ctx-1) goes to its slot,
+  // and the wave that owns the tile holding ctx-1 uses it from registers.
+  const NewRow nr = new_row_of(p, s, ctx, t0, t1, w);
+  uint4 nk = make_uint4(0, 0, 0, 0), nv = make_uint4(0, 0, 0, 0);
+  if (nr.mine) {
+    const int64_t src = ((int64_t)s * p.num_kv_heads + g) * D + c * EPL;
+    nk = load16(reinterpret_cast<const T*>(p.k_new) + src);
+    nv = load16(reinterpret_cast<const T*>(p.v_new) + src);
+    if (rg == 0) {   // the LPR lanes of row group 0 cover the row
+      const int64_t dst = (int64_t)nr.slot * row_elems + g * D + c * EPL;
+      *reinterpret_cast<uint4*>(const_cast<T*>(reinterpret_cast<const T*>(p.k_cache)) + dst) = nk;
+      *reinterpret_cast<uint4*>(const_cast<T*>(reinterpret_cast<const T*>(p.v_cache)) + dst) = nv;
+    }
+  }
+
   for (int it = w; it < n_tiles; it += kWaves) {
     const int tok0 = t0 + it * kTile;
     const int64_t row0 = tile_row0(bt, tok0, bs, p.num_blocks, poisoned);
@@ -202,12 +239,16 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
     for (int i = 0; i < LOADS; ++i) kr[i] = load16(kc + (row0 + rg + RPI * i) * row_elems);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) vr[i] = load16(vc + (row0 + rg + RPI * i) * row_elems);
+    // in the tile holding the new row, that row comes from registers
+    const bool ov = nr.mine && tok0 <= nr.pos && nr.pos < tok0 + kTile;
 
     float x[LOADS][G];
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       float kf[EPL];
-      Widen<T>::run(kr[i], kf);
+      uint4 kq = kr[i];
+      if (ov && tok0 + rg + RPI * i == nr.pos) kq = nk;
+      Widen<T>::run(kq, kf);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float a = 0.f;
@@ -244,7 +285,9 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       float vf[EPL];
-      Widen<T>::run(vr[i], vf);
+      uint4 vq = vr[i];
+      if (ov && tok0 + rg + RPI * i == nr.pos) vq = nv;
+      Widen<T>::run(vq, vf);
       const bool live = tok0 + rg + RPI * i < t1;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) vf[e] = live ? vf[e] : 0.f;
@@ -374,6 +417,25 @@ void decode_mfma_kernel(DecodeParams p) {
   for (int e = 0; e < EPL; ++e) acc[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   bool bad = false;
 
+  // Fused store: the sequence's new row (position ctx-1) goes to its slot,
+  // and the wave that owns the tile holding ctx-1 uses it from registers.
+  const NewRow nr = new_row_of(p, s, ctx, t0, t1, w);
+  uint4 nk[KCH], nv = make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int c = 0; c < KCH; ++c) nk[c] = make_uint4(0, 0, 0, 0);
+  if (nr.mine) {
+    const uint16_t* kn = reinterpret_cast<const uint16_t*>(p.k_new) + ((int64_t)s * p.num_kv_heads + g) * D;
+    const uint16_t* vn = reinterpret_cast<const uint16_t*>(p.v_new) + ((int64_t)s * p.num_kv_heads + g) * D;
+#pragma unroll
+    for (int c = 0; c < KCH; ++c) nk[c] = load16(kn + 8 * qg + 32 * c);
+    if constexpr (EPL == 8) {
+      nv = load16(vn + EPL * n);
+    } else {
+      const uint2 h = load8(vn + EPL * n);
+      nv = make_uint4(h.x, h.y, 0, 0);
+    }
+  }
+
   // Logical position of the first token of the wave's j-th tile (j clamped
   // to the wave's last tile) and its physical block.
   auto tile_tok0 = [&](int j) { return t0 + (w + kWaves * min(j, my_tiles - 1)) * kTile; };
@@ -406,11 +468,17 @@ void decode_mfma_kernel(DecodeParams p) {
   // Scores, online softmax and P.V of the wave's j-th tile.
   auto compute = [&](int j, const MfmaTile<D>& t) {
     const int tok0 = tile_tok0(j);
+    // in the tile holding the new row, that row comes from registers
+    const bool ov = nr.mine && tok0 <= nr.pos && nr.pos < tok0 + kTile;
+    const int rn = nr.pos - tok0;
     // S[token 4*qg + r][head n] in sc[r]
     f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < KCH; ++c)
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bit_cast_to<bf16x8_t>(t.k[c]), qb[c], sc, 0, 0, 0);
+    for (int c = 0; c < KCH; ++c) {
+      uint4 kq = t.k[c];
+      if (ov && n == rn) kq = nk[c];
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bit_cast_to<bf16x8_t>(kq), qb[c], sc, 0, 0, 0);
+    }
 
     const int tokq = tok0 + 4 * qg;
     float x[4];
@@ -446,10 +514,12 @@ void decode_mfma_kernel(DecodeParams p) {
     uint32_t vd[4][4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      vd[st][0] = t.v[st].x;
-      vd[st][1] = t.v[st].y;
-      vd[st][2] = t.v[st].z;
-      vd[st][3] = t.v[st].w;
+      uint4 v = t.v[st];
+      if (ov && 4 * qg + st == rn) v = nv;
+      vd[st][0] = v.x;
+      vd[st][1] = v.y;
+      vd[st][2] = v.z;
+      vd[st][3] = v.w;
     }
     if (tok0 + kTile > t1) {
 #pragma unroll
@@ -489,6 +559,26 @@ void decode_mfma_kernel(DecodeParams p) {
         blk_ahead = block_of(j + u + kStages);
         issue(j + u + kStages - 1, b, buf[(u + kStages - 1) % kStages]);
         if (j + u < my_tiles) compute(j + u, buf[u]);
+      }
+    }
+  }
+
+  // The new row goes to its cache slot after the loop, so that no store is
+  // in flight while the loop's loads are being waited for.
+  if (nr.mine) {
+    uint16_t* kd = const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(p.k_cache)) +
+                   (int64_t)nr.slot * row_elems + g * D;
+    uint16_t* vd = const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(p.v_cache)) +
+                   (int64_t)nr.slot * row_elems + g * D;
+    if (n == 0) {   // lanes n == 0 (qg = 0..3) hold all K pieces of the row
+#pragma unroll
+      for (int c = 0; c < KCH; ++c) *reinterpret_cast<uint4*>(kd + 8 * qg + 32 * c) = nk[c];
+    }
+    if (qg == 0) {  // lanes qg == 0 (n = 0..15) hold all V columns
+      if constexpr (EPL == 8) {
+        *reinterpret_cast<uint4*>(vd + EPL * n) = nv;
+      } else {
+        *reinterpret_cast<uint2*>(vd + EPL * n) = make_uint2(nv.x, nv.y);
       }
     }
   }

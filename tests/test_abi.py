@@ -156,3 +156,16 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(binding, "_LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         binding.lib()
+
+
+@needs_lib
+def test_fused_store_rejects_missing_rows():
+    lib = pkv.lib()
+    rc = lib.pkv_paged_attention_decode_store(1024, 1024, 1024, 1024, 1024, 1024, None, 1024, 1024,
+                                              4, 16, 256, 64, 16, 8, 4, 64, 0.125, 0, None, 0, 0, 0,
+                                              None)
+    assert rc == binding.PKV_EINVAL and b"null" in lib.pkv_last_error()
+    rc = lib.pkv_paged_attention_decode_store(1024, 1024, 1024, 1024, 1024, 1024, 1032, 1024, 1024,
+                                              4, 16, 256, 64, 16, 8, 4, 64, 0.125, 0, None, 0, 0, 0,
+                                              None)
+    assert rc == binding.PKV_EINVAL

@@ -193,3 +193,53 @@ def test_mixed_decode_part_full():
     want = oracle_decode(dec, caches=caches, seqs=seqs)
     got = gpu_decode(dec, dev=ddev, algo="mfma", partition_size=0, store=False)
     assert_close(got[seqs], want, torch.bfloat16, "mixed decode")
+
+
+# --------------------------------------------------------------------------
+# store fused into decode
+# --------------------------------------------------------------------------
+
+FUSED = [
+    # (dtype, hq, hkv, d, max_ctx, algo, partition)
+    (torch.float32, 8, 4, 64, 300, "valu", 0),
+    (torch.float32, 8, 4, 64, 300, "valu", 32),
+    (torch.bfloat16, 16, 8, 128, 400, "valu", 64),
+    (torch.bfloat16, 16, 8, 128, 400, "mfma", 0),
+    (torch.bfloat16, 32, 8, 128, 700, "mfma", 128),
+    (torch.bfloat16, 32, 8, 128, 700, "mfma", 32),
+    (torch.bfloat16, 12, 4, 64, 250, "mfma", 0),
+]
+
+
+@pytest.mark.parametrize("case", FUSED, ids=lambda c: f"{str(c[0])[6:]}-{c[1]}x{c[2]}-d{c[3]}-{c[5]}-p{c[6]}")
+def test_decode_store_fused(case):
+    dtype, hq, hkv, d, max_ctx, algo, partition = case
+    b = W.random_decode_batch(hq * 17 + d + partition, 11, hq, hkv, d, dtype, max_ctx=max_ctx,
+                              min_ctx=0)
+    say(f"fused {case} ctx={b.pool.context_lens.tolist()}")
+    dev = to_device(b)
+    out = torch.empty_like(dev["q"])
+    pkv.paged_attention_decode_store(out, dev["q"], dev["k_cache"], dev["v_cache"],
+                                     dev["block_tables"], dev["context_lens"], dev["k_new"],
+                                     dev["v_new"], dev["slot_mapping"], b.scale, b.max_ctx,
+                                     partition_size=partition, algo=algo)
+    torch.cuda.synchronize()
+    kc, vc = oracle_caches(b)                      # the oracle's store, then its decode
+    assert W.host_bits(dev["k_cache"]).tobytes() == kc.tobytes()
+    assert W.host_bits(dev["v_cache"]).tobytes() == vc.tobytes()
+    want = oracle_decode(b, caches=(kc, vc))
+    assert_close(out.float().cpu().double().numpy(), want, dtype, f"fused {algo} p={partition}")
+
+
+def test_decode_store_fused_tiny_and_qwen3_layer():
+    for b in (W.tiny().batches[0], W.qwen3_decode(layers=1).batches[0]):
+        dev = to_device(b)
+        out = torch.empty_like(dev["q"])
+        pkv.paged_attention_decode_store(out, dev["q"], dev["k_cache"], dev["v_cache"],
+                                         dev["block_tables"], dev["context_lens"], dev["k_new"],
+                                         dev["v_new"], dev["slot_mapping"], b.scale, b.max_ctx)
+        torch.cuda.synchronize()
+        kc, vc = oracle_caches(b)
+        assert W.host_bits(dev["k_cache"]).tobytes() == kc.tobytes()
+        assert_close(out.float().cpu().double().numpy(), oracle_decode(b, caches=(kc, vc)),
+                     b.q.dtype, "fused workload")
