@@ -155,7 +155,9 @@ int decode_impl(const char* fn, void* out, const void* q, const void* k_cache, c
   int32_t part;
   int64_t nparts;
   partitioning(max_context_len, partition_size, &part, &nparts);
-  if (nparts > 0x7fffffff) return fail(PKV_EUNSUPPORTED, "%s: too many partitions", fn);
+  if ((int64_t)num_seqs * num_kv_heads * nparts > 0x7ffffff0)
+    return fail(PKV_EUNSUPPORTED, "%s: %lld work items exceed the grid; use a larger partition_size", fn,
+                (long long)num_seqs * num_kv_heads * nparts);
   pkv::DecodeParams p;
   p.out = out;
   p.q = q;

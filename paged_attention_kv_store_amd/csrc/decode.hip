@@ -1,6 +1,7 @@
 // Decode attention over a paged KV cache: one query row per (sequence, q-head).
 //
-// Work unit: one workgroup of 4 wavefronts per (partition, kv-head, sequence).
+// Work unit: one workgroup of 4 wavefronts per (kv-head, partition, sequence).
+// The grid is one-dimensional and decode_item maps a workgroup to its item.
 // It serves all G = Hq/Hkv q-heads that share the kv-head, so each K/V byte is
 // read once for the whole group. The partition's tokens are cut into 16-token
 // tiles; wave w takes tiles w, w+4, w+8, ... Every tile lies inside one
@@ -26,7 +27,10 @@
 
 namespace pkv {
 
-constexpr int kWaves = 4;
+#ifndef PKV_DECODE_WAVES
+#define PKV_DECODE_WAVES 4
+#endif
+constexpr int kWaves = PKV_DECODE_WAVES;   // wavefronts per decode workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 16;
 #ifndef PKV_DECODE_STAGES
@@ -136,6 +140,32 @@ __device__ __forceinline__ NewRow new_row_of(const DecodeParams& p, int s, int c
   return r;
 }
 
+// Work item of a decode workgroup. Items are numbered partition fastest,
+// then kv-head, then sequence: i = part + P * (g + Hkv * s). Workgroups go to
+// the XCDs round robin (id % 8), each XCD with its own L2.
+//  * One partition: item = workgroup id, so with 8 kv-heads each XCD serves
+//    one kv-head of every sequence; blocks shared by consecutive sequences
+//    are re-read from one L2.
+//  * Several partitions: within each run of 8 consecutive items the XCD that
+//    takes an item is rotated by the run index, so the partitions of a
+//    sequence still spread over all XCDs but no XCD is tied to one partition
+//    index (with 2 partitions and mostly short sequences, a fixed mapping
+//    would leave half the XCDs nearly idle).
+// Returns false for the grid's padding.
+constexpr int kXcds = 8;
+__device__ __forceinline__ bool decode_item(const DecodeParams& p, int& g, int& part, int& s) {
+  int64_t item = blockIdx.x;
+  if (p.num_partitions > 1) {
+    const int64_t x = item % kXcds, k = item / kXcds;
+    item = k * kXcds + (x + k) % kXcds;
+  }
+  if (item >= (int64_t)p.num_seqs * p.num_kv_heads * p.num_partitions) return false;
+  part = (int)(item % p.num_partitions);
+  g = (int)((item / p.num_partitions) % p.num_kv_heads);
+  s = (int)(item / ((int64_t)p.num_partitions * p.num_kv_heads));
+  return true;
+}
+
 // ---------------------------------------------------------------------------
 // Vector-ALU decode
 // ---------------------------------------------------------------------------
@@ -177,7 +207,8 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
   __shared__ float s_m[kWaves * 16], s_l[kWaves * 16];
   __shared__ float s_o[kWaves * G * D];
 
-  const int part = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  int g, part, s;
+  if (!decode_item(p, g, part, s)) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int c = lane % LPR, rg = lane / LPR;
   const int ctx = clamp_ctx(p.context_lens[s], p.max_ctx);
@@ -369,7 +400,8 @@ void decode_mfma_kernel(DecodeParams p) {
   __shared__ float s_o[kWaves * GP * D];
   __shared__ int s_poison;
 
-  const int part = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  int g, part, s;
+  if (!decode_item(p, g, part, s)) return;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, qg = lane >> 4;
@@ -671,9 +703,14 @@ __global__ __launch_bounds__(D) void splitk_reduce_kernel(DecodeParams p) {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+static dim3 decode_grid(const DecodeParams& p) {
+  const int64_t items = (int64_t)p.num_seqs * p.num_kv_heads * p.num_partitions;
+  return dim3((unsigned)((items + kXcds - 1) / kXcds * kXcds));
+}
+
 template <typename T, int D>
 static hipError_t launch_valu_g(const DecodeParams& p, hipStream_t stream) {
-  const dim3 grid(p.num_partitions, p.num_kv_heads, p.num_seqs);
+  const dim3 grid = decode_grid(p);
   switch (p.group) {
 #define PKV_G(GV) \
   case GV: hipLaunchKernelGGL((decode_valu_kernel<T, D, GV>), grid, dim3(kThreads), 0, stream, p); break;
@@ -692,7 +729,7 @@ hipError_t launch_decode_valu(const DecodeParams& p, int head_dim, int dtype, hi
 
 template <int D>
 static hipError_t launch_mfma_d(const DecodeParams& p, hipStream_t stream) {
-  const dim3 grid(p.num_partitions, p.num_kv_heads, p.num_seqs);
+  const dim3 grid = decode_grid(p);
   if (p.group <= 4)
     hipLaunchKernelGGL((decode_mfma_kernel<D, 4>), grid, dim3(kThreads), 0, stream, p);
   else if (p.group <= 8)
