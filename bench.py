@@ -22,7 +22,8 @@ traffic that rocprofv3 counters measured for that kernel (from
 profiles/decode_qwen3_traffic.json, null if the kernel source changed since),
 a plain-copy bandwidth measured in the same run, tokens/s, the other
 standard workloads (prefix-shared batch, long-context split-K, mixed chunked
-prefill + decode with the prefill's matrix-core utilisation), a parity
+prefill + decode with the prefill's matrix-core utilisation, verification
+of 4 drafted-token rows per sequence), a parity
 sample against the CPU oracle, and the oracle itself timed on a bounded
 sample of the headline workload on one host core (a baseline, not a target).
 
@@ -311,6 +312,19 @@ def secondary(device, steps, warmup, algo):
                     "prefill_mfma_util_pct": 100 * fl / t_pre / 1e9 / BF16_MFMA_PEAK_TFLOPS,
                     "decode_ms": t_dec, "decode_GBps": decode_bytes(db) / t_dec / 1e6,
                     "tokens_per_s": 4224 / ((t_store + t_pre + t_dec) * 1e-3)}
+    del store, prefill, dec, wl, pre, db
+    # verification of drafted tokens: 128 seqs x 4 causal rows, one chunk call
+    sv = W.spec_verify(device=device).prefill
+    pkv.kv_cache_store(sv.k_new, sv.v_new, sv.k_cache, sv.v_cache, sv.slot_mapping)
+    verify = pkv.PrefillLaunch(torch.empty_like(sv.q), sv.q, sv.k_cache, sv.v_cache,
+                               torch.as_tensor(sv.pool.block_tables, device=device),
+                               torch.as_tensor(sv.cu_seqlens_q, device=device),
+                               torch.as_tensor(sv.pool.context_lens, device=device), sv.scale,
+                               4, sv.max_ctx, causal=True)
+    ms = time_region(verify, steps, warmup)
+    by = decode_bytes(sv)
+    res["spec_verify"] = {"ms": ms, "GBps": by / ms / 1e6, "pct_hbm_peak": 100 * by / ms / 1e6 / HBM_PEAK_GBS,
+                          "rows_per_s": sv.q.shape[0] / (ms * 1e-3), "rows_per_seq": 4}
     return res
 
 

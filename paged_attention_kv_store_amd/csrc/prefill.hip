@@ -28,6 +28,8 @@
 #include "common.h"
 #include "device_utils.h"
 
+#include <type_traits>
+
 namespace pkv {
 
 namespace {
@@ -170,6 +172,12 @@ void prefill_kernel(PrefillParams p) {
   const bf16x8_t ones = bit_cast_to<bf16x8_t>(make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
   // keys below this bound are visible to every row of the wave
   const int lim_wave = p.causal ? min(P0 + r0 + (32 * w) / G + 1, ctx) : ctx;
+  // Whether M-row tile t of the wave holds a live query row (wave-uniform).
+  // Short chunks (a few query rows, as in verifying drafted tokens) leave
+  // most tiles empty; their matrix work is skipped, while the wave still
+  // takes its share of the cooperative gather and every barrier.
+  const bool live0 = r0 + (32 * w) / G < L;
+  const bool live1 = r0 + (32 * w + 16) / G < L;
 
   if (tid == 0) s_bad = 0;
   int ids_next[4], ids_after[4];
@@ -197,7 +205,7 @@ void prefill_kernel(PrefillParams p) {
 #pragma unroll
     for (int sub = 0; sub < kKvTile / 32; ++sub) {
       const int tb = 32 * sub;              // first key of the 32-key block, tile-relative
-      if (kv0 + tb >= kv_end) break;
+      if (kv0 + tb >= kv_end || !live0) break;
       // Slot u = 0..7 of a lane stands for key tb + 16*(u/4) + 4qg + u%4: the
       // keys of two 16-key score tiles, in the order their scores arrive.
       // K rows tb + 16h + n, pieces 4s + qg (elements 32s + 8qg .. +8)
@@ -211,6 +219,7 @@ void prefill_kernel(PrefillParams p) {
       bf16x8_t pa[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
+        if (t == 1 && !live1) break;
         float x[8];   // raw scores q.k
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -271,17 +280,21 @@ void prefill_kernel(PrefillParams p) {
         vd[u][3] = v.w;
       }
       // step i: B column n = V[the lane's 8 keys][8n + i]
+      auto pv = [&](auto both) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
-        uint32_t b[4];
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+          uint32_t b[4];
 #pragma unroll
-        for (int h = 0; h < 4; ++h) b[h] = __builtin_amdgcn_perm(vd[2 * h + 1][i / 2], vd[2 * h][i / 2], sel);
-        const bf16x8_t vb = bit_cast_to<bf16x8_t>(make_uint4(b[0], b[1], b[2], b[3]));
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-          acc[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[t], vb, acc[t][i], 0, 0, 0);
-      }
+          for (int h = 0; h < 4; ++h) b[h] = __builtin_amdgcn_perm(vd[2 * h + 1][i / 2], vd[2 * h][i / 2], sel);
+          const bf16x8_t vb = bit_cast_to<bf16x8_t>(make_uint4(b[0], b[1], b[2], b[3]));
+          acc[0][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[0], vb, acc[0][i], 0, 0, 0);
+          if constexpr (decltype(both)::value)
+            acc[1][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[1], vb, acc[1][i], 0, 0, 0);
+        }
+      };
+      if (live1) pv(std::true_type{});
+      else pv(std::false_type{});
     }
     wait_loads();
     __syncthreads();

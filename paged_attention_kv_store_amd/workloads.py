@@ -8,7 +8,7 @@ sides of a parity test see the very same bits.
 
 Shapes follow serving batches of the kind the pages describe (a small Qwen3
 decoding 60 batched prompts, Llama-class serving with prefix caching, chunked
-prefill mixed with decode); the sizes are this library's five standard
+prefill mixed with decode); the sizes are this library's six standard
 workloads:
 
   tiny          4 seqs, ctx {1,17,100,256}, 8 q / 4 kv heads, D 64, fp32,
@@ -22,6 +22,9 @@ workloads:
   mixed         8 prefill chunks of 512 rows after U{0..8192} cached tokens,
                 plus 128 decode seqs with ctx U{256..4096}; 32 q / 8 kv heads,
                 D 128, bf16; all 4224 new tokens stored first
+  spec_verify   128 seqs, each 4 causal query rows (one accepted and three
+                drafted tokens) after U{256..4096} cached tokens; 32 q / 8 kv
+                heads, D 128, bf16; the 512 new rows stored first
 
 Recipe: the metadata comes from numpy PCG64 streams spawned from
 SeedSequence(seed); values come from a torch generator (on the target device)
@@ -242,7 +245,7 @@ def decode_store_slots(pool: Pool, block_size=BLOCK_SIZE) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
-# The five standard workloads.
+# The six standard workloads.
 # --------------------------------------------------------------------------
 
 def tiny(seed: int = 0, device="cpu") -> Workload:
@@ -328,12 +331,33 @@ def mixed(seed: int = 4, device="cpu") -> Workload:
                     notes="store 4224 tokens, prefill 8x512 causal, decode 128 seqs")
 
 
+def spec_verify(seed: int = 5, device="cpu", rows: int = 4) -> Workload:
+    """Verification of drafted tokens: 128 seqs x `rows` causal query rows.
+
+    Each sequence has U{256..4096} cached tokens before the rows (the last
+    accepted token plus rows-1 drafted ones); the rows' own K/V are stored
+    first, so context = prior + rows. Shapes as the decode half of `mixed`.
+    """
+    (rng,) = _streams(seed, 1)
+    prior = rng.integers(256, 4096, size=128, endpoint=True).astype(np.int32)
+    ctx = (prior + rows).astype(np.int32)
+    pool = make_pool(rng, ctx)
+    slots = np.concatenate([_slots_of(pool, c, np.arange(prior[c], ctx[c]), BLOCK_SIZE)
+                            for c in range(len(ctx))]).astype(np.int32)
+    batch = build_batch(pool, 32, 8, 128, torch.bfloat16, seed, 0, device,
+                        num_queries=rows * len(ctx), store_slots=slots)
+    batch.cu_seqlens_q = np.arange(0, rows * len(ctx) + 1, rows, dtype=np.int32)
+    return Workload("spec_verify", [], prefill=batch,
+                    notes=f"128 seqs x {rows} causal query rows after U{{256..4096}} cached")
+
+
 WORKLOADS = {
     "tiny": tiny,
     "qwen3_decode": qwen3_decode,
     "llama_prefix": llama_prefix,
     "long_splitk": long_splitk,
     "mixed": mixed,
+    "spec_verify": spec_verify,
 }
 
 

@@ -134,3 +134,55 @@ def test_mixed_prefill_full_sampled_rows():
                                                  b.pool.block_tables[c:c + 1],
                                                  np.array([prior + i + 1]), b.scale, 16)
             assert_close(got[cu[c] + i][None], want, torch.bfloat16, f"chunk {c} row {i}")
+
+
+SHORT = [
+    # (hq, hkv, rows): verification of rows-1 drafted tokens, every GQA group
+    (32, 8, 2), (32, 8, 4), (32, 8, 8), (16, 8, 3), (8, 8, 5), (32, 4, 7), (8, 1, 6),
+]
+
+
+@pytest.mark.parametrize("case", SHORT, ids=lambda c: f"{c[0]}x{c[1]}-L{c[2]}")
+def test_short_chunks_match_decode_over_each_prefix(case):
+    """Multi-query decode: row i of an L-row chunk after P0 cached tokens is
+    single-query decode over the first P0 + i + 1 keys."""
+    hq, hkv, rows = case
+    b = W.random_prefill_batch(hq + 13 * rows, 9, hq, hkv, 128, torch.bfloat16,
+                               max_rows=rows, min_rows=rows, max_prior=1500)
+    say(f"short chunks {case} ctx={b.pool.context_lens.tolist()}")
+    dev = to_device(b)
+    got = gpu_prefill(b, dev=dev)
+    kc, vc = oracle_caches(b)
+    assert_close(got, oracle_prefill(b, caches=(kc, vc)), torch.bfloat16, f"L={rows}")
+    # the same rows through the decode kernel, one context length per row
+    cu, ctx = b.cu_seqlens_q, b.pool.context_lens
+    seq = np.repeat(np.arange(len(ctx)), rows)
+    row_ctx = np.concatenate([ctx[c] - rows + 1 + np.arange(rows) for c in range(len(ctx))])
+    bt = np.ascontiguousarray(b.pool.block_tables[seq])
+    out = torch.empty_like(dev["q"])
+    pkv.paged_attention_decode(out, dev["q"], dev["k_cache"], dev["v_cache"],
+                               torch.as_tensor(bt, device="cuda"),
+                               torch.as_tensor(row_ctx.astype(np.int32), device="cuda"),
+                               b.scale, int(row_ctx.max()))
+    torch.cuda.synchronize()
+    dec = out.float().cpu().double().numpy()
+    want = oracle.paged_attention_decode(W.host_bits(b.q), kc, vc, bt, row_ctx, b.scale, 16)
+    assert_close(dec, want, torch.bfloat16, "decode per row")
+    assert_close(got, want, torch.bfloat16, "chunk vs per-row decode oracle")
+    assert cu[-1] == len(row_ctx)
+
+
+@pytest.mark.slow
+def test_spec_verify_full_sampled_seqs():
+    b = W.spec_verify().prefill
+    say(f"spec_verify: {b.num_seqs} seqs x 4 rows")
+    got = gpu_prefill(b)
+    kc, vc = oracle_caches(b)
+    q = W.host_bits(b.q)
+    cu, ctx = b.cu_seqlens_q, b.pool.context_lens
+    for c in sorted({0, 1, 63, 127} | set(range(5, 128, 11))):
+        want = oracle.paged_attention_prefill_chunk(q[cu[c]:cu[c + 1]], kc, vc,
+                                                    b.pool.block_tables[c:c + 1],
+                                                    np.array([0, 4], np.int32),
+                                                    ctx[c:c + 1], b.scale, 16)
+        assert_close(got[cu[c]:cu[c + 1]], want, torch.bfloat16, f"seq {c}")

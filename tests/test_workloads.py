@@ -70,3 +70,18 @@ def test_random_prefill_batch_slots_cover_the_chunks():
     out = oracle.paged_attention_prefill_chunk(bits(b.q), kc, vc, b.pool.block_tables, cu,
                                                b.pool.context_lens, b.scale, 16)
     assert np.isfinite(out).all()
+
+
+def test_spec_verify_rows_follow_their_prefix():
+    wl = W.spec_verify()
+    b = wl.prefill
+    ctx, cu = b.pool.context_lens, b.cu_seqlens_q
+    assert ctx.shape == (128,) and (ctx >= 260).all() and (ctx <= 4100).all()
+    assert (np.diff(cu) == 4).all() and b.q.shape == (512, 32, 128)
+    # the store fills exactly positions ctx-4 .. ctx-1 of each sequence
+    slots = b.slot_mapping.numpy().reshape(128, 4)
+    for s in range(0, 128, 17):
+        pos = np.arange(ctx[s] - 4, ctx[s])
+        want = b.pool.block_tables[s][pos // 16].astype(np.int64) * 16 + pos % 16
+        np.testing.assert_array_equal(slots[s], want)
+    assert len(np.unique(slots)) == slots.size
