@@ -268,6 +268,13 @@ def cpu_baseline(b: W.PagedBatch, budget_s=12.0):
 # secondary workloads
 # --------------------------------------------------------------------------
 
+def balanced_ms(b, bt, cl, steps, warmup):
+    """The same decode with the work-balanced kernel (one launch, in-kernel merge)."""
+    dec = pkv.DecodeLaunch(torch.empty_like(b.q), b.q, b.k_cache, b.v_cache, bt, cl, b.scale,
+                           b.max_ctx, partition_size="balanced", algo="mfma")
+    return time_region(dec, steps, warmup)
+
+
 def secondary(device, steps, warmup, algo):
     res = {}
     b = W.llama_prefix(device=device).batches[0]
@@ -279,7 +286,8 @@ def secondary(device, steps, warmup, algo):
     ub, lb = decode_bytes(b, unique_blocks=True), decode_bytes(b)
     res["llama_prefix"] = {"ms": ms, "unique_GBps": ub / ms / 1e6, "logical_GBps": lb / ms / 1e6,
                            "pct_hbm_peak_unique": 100 * ub / ms / 1e6 / HBM_PEAK_GBS,
-                           "tokens_per_s": b.num_seqs / (ms * 1e-3), "partition": 0}
+                           "tokens_per_s": b.num_seqs / (ms * 1e-3), "partition": 0,
+                           "balanced_ms": balanced_ms(b, bt, cl, steps, warmup)}
     del dec, b
     b = W.long_splitk(device=device).batches[0]
     bt = torch.as_tensor(b.pool.block_tables, device=device)
@@ -289,7 +297,8 @@ def secondary(device, steps, warmup, algo):
     ms = time_region(dec, steps, warmup)
     by = decode_bytes(b)
     res["long_splitk"] = {"ms": ms, "GBps": by / ms / 1e6, "pct_hbm_peak": 100 * by / ms / 1e6 / HBM_PEAK_GBS,
-                          "tokens_per_s": b.num_seqs / (ms * 1e-3), "partition": 512}
+                          "tokens_per_s": b.num_seqs / (ms * 1e-3), "partition": 512,
+                          "balanced_ms": balanced_ms(b, bt, cl, steps, warmup)}
     del dec, b
     wl = W.mixed(device=device)
     pre, db = wl.prefill, wl.batches[0]
@@ -306,11 +315,14 @@ def secondary(device, steps, warmup, algo):
     t_store = time_region(store, steps, warmup)
     t_pre = time_region(prefill, steps, warmup)
     t_dec = time_region(dec, steps, warmup)
+    t_dec_bal = balanced_ms(db, torch.as_tensor(db.pool.block_tables, device=device),
+                            torch.as_tensor(db.pool.context_lens, device=device), steps, warmup)
     fl = prefill_flops(pre)
     res["mixed"] = {"store_ms": t_store, "store_GBps": store_bytes(pre) / t_store / 1e6,
                     "prefill_ms": t_pre, "prefill_TFLOPs": fl / t_pre / 1e9,
                     "prefill_mfma_util_pct": 100 * fl / t_pre / 1e9 / BF16_MFMA_PEAK_TFLOPS,
                     "decode_ms": t_dec, "decode_GBps": decode_bytes(db) / t_dec / 1e6,
+                    "decode_balanced_ms": t_dec_bal,
                     "tokens_per_s": 4224 / ((t_store + t_pre + t_dec) * 1e-3)}
     del store, prefill, dec, wl, pre, db
     # verification of drafted tokens: 128 seqs x 4 causal rows, one chunk call
@@ -438,7 +450,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--partition", type=int, default=0, help="decode partition size for the step")
+    ap.add_argument("--partition", type=int, default=0, help="decode partition size for the step (-1: work-balanced)")
     ap.add_argument("--algo", default="auto", choices=sorted(pkv.DECODE_ALGOS))
     ap.add_argument("--layers", type=int, default=28)
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replay")

@@ -74,6 +74,10 @@ typedef enum {
   PKV_DECODE_MFMA = 2     /* GQA group packed into matrix-core tiles (bf16 only) */
 } pkv_decode_algo;
 
+/* partition_size value selecting the work-balanced decode (see
+ * pkv_paged_attention_decode). */
+enum { PKV_PARTITION_BALANCED = -1 };
+
 /* Library version as major*10000 + minor*100 + patch. */
 int pkv_version(void);
 
@@ -97,15 +101,22 @@ int pkv_kv_cache_store(const void* k, const void* v, void* k_cache, void* v_cach
                        int32_t head_dim, pkv_dtype dtype, void* stream);
 
 /*
- * Bytes of split-K workspace needed by pkv_paged_attention_decode for the
- * same num_seqs, num_q_heads, head_dim, max_context_len and partition_size:
- * fp32 running max, sum and unnormalised output for every (sequence, q-head,
- * partition). 0 when partition_size is 0 (single pass). Layout inside:
- *   m [num_seqs, num_q_heads, P], l [num_seqs, num_q_heads, P],
- *   o [num_seqs, num_q_heads, P, head_dim],  P = ceil(max_context_len / partition_size).
+ * Bytes of workspace needed by pkv_paged_attention_decode for the same
+ * num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len and
+ * partition_size (0 for invalid sizes).
+ *  - partition_size > 0 (split-K): fp32 running max, sum and unnormalised
+ *    output for every (sequence, q-head, partition); 0 when one partition
+ *    covers max_context_len. Layout: m [num_seqs, num_q_heads, P],
+ *    l [num_seqs, num_q_heads, P], o [num_seqs, num_q_heads, P, head_dim],
+ *    P = ceil(max_context_len / partition_size).
+ *  - PKV_PARTITION_BALANCED: 4096 int32 arrival counters (16 KiB, at the
+ *    start whatever the sizes), then fp32 pieces of the partial results, two
+ *    per wave of the largest grid (4096 waves).
+ *  - 0 (single pass): 0.
  */
-size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                 int32_t max_context_len, int32_t partition_size);
+size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_context_len,
+                                 int32_t partition_size);
 
 /*
  * paged_attention_decode: out[s, h] = softmax_j(scale * q[s, h] . K_s[j, g])
@@ -120,8 +131,20 @@ size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *     sum, unnormalised output) go to `workspace`, and a second launch merges
  *     them (log-sum-exp). Sequences that fit in one partition are written
  *     directly.
+ *     PKV_PARTITION_BALANCED (MFMA kernel, bf16, at most 8192 sequences,
+ *     fewer than 2^30 16-token tiles): one launch whose grid fills the GPU
+ *     once; every wave takes an equal share of all (kv-head, sequence,
+ *     16-token tile) work, so the time no longer follows the longest
+ *     context. A (sequence, kv-head) split between waves is merged
+ *     (log-sum-exp) in the same launch by the wave that finishes its part
+ *     last, found with atomic counters in the first 16 KiB of `workspace`.
+ *     Those must be zero before the first call (e.g. a zero-filled
+ *     workspace); every call leaves them zero, so one workspace serves calls
+ *     of any sizes in turn, but calls that run at the same time must not
+ *     share it. out must be 16-byte aligned.
  *   workspace / workspace_bytes: device buffer of at least
- *     pkv_decode_workspace_size(...) bytes (may be NULL when that is 0).
+ *     pkv_decode_workspace_size(...) bytes (may be NULL when that is 0),
+ *     256-byte aligned for PKV_PARTITION_BALANCED.
  *   algo: pkv_decode_algo. The MFMA kernel needs bf16 and
  *     num_q_heads / num_kv_heads <= 16.
  * Supported: head_dim in {64, 128}; block_size a multiple of 16 up to 256;

@@ -22,6 +22,7 @@ _lib = None
 PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EWORKSPACE, PKV_EHIP = 0, -1, -2, -3, -4
 PKV_F32, PKV_BF16 = 0, 1
 DECODE_ALGOS = {"auto": 0, "valu": 1, "mfma": 2}
+PARTITION_BALANCED = -1      # partition_size selecting the work-balanced decode
 
 _i32 = ctypes.c_int32
 _vp = ctypes.c_void_p
@@ -30,7 +31,7 @@ _SIGNATURES = {
     "pkv_last_error": ([], ctypes.c_char_p),
     "pkv_kv_cache_store": ([_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _vp],
                            ctypes.c_int),
-    "pkv_decode_workspace_size": ([_i32, _i32, _i32, _i32, _i32], ctypes.c_size_t),
+    "pkv_decode_workspace_size": ([_i32, _i32, _i32, _i32, _i32, _i32], ctypes.c_size_t),
     "pkv_paged_attention_decode": ([_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                     _i32, _i32, _i32, ctypes.c_float, _i32, _vp, ctypes.c_size_t,
                                     ctypes.c_int, _i32, _vp], ctypes.c_int),
@@ -124,9 +125,24 @@ def kv_cache_store(k, v, k_cache, v_cache, slot_mapping, stream=None):
                                     _dtype_code(k), _stream(stream)))
 
 
-def decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len, partition_size):
-    return int(lib().pkv_decode_workspace_size(num_seqs, num_q_heads, head_dim,
-                                               max_context_len, partition_size))
+def _partition(partition_size):
+    return PARTITION_BALANCED if partition_size == "balanced" else int(partition_size)
+
+
+def decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                          partition_size):
+    return int(lib().pkv_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                               max_context_len, _partition(partition_size)))
+
+
+def _decode_workspace(workspace, s, hq, hkv, d, max_context_len, partition, device):
+    """The caller's workspace, or a new one when the call needs it: zero-filled
+    (the work-balanced decode requires zero counters before its first call)."""
+    need = decode_workspace_size(s, hq, hkv, d, max_context_len, partition) if partition else 0
+    if need and workspace is None:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    return workspace, ws_bytes
 
 
 def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale,
@@ -135,8 +151,11 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     """One query row per sequence over its paged context; writes out [S, Hq, D].
 
     max_context_len is a host-side bound on context_lens (it sizes the grid).
-    With partition_size > 0 the split-K workspace is taken from `workspace`
-    (a uint8 device tensor) or allocated here through torch when omitted.
+    partition_size: 0 (one pass per sequence and kv-head), a positive multiple
+    of 16 (split-K), or "balanced" / PARTITION_BALANCED (work-balanced decode).
+    The workspace those need is taken from `workspace` (a uint8 device
+    tensor; zero-filled before its first work-balanced use) or allocated here
+    through torch when omitted.
     """
     _dev(out, q, k_cache, v_cache, block_tables, context_lens)
     _need(q.dim() == 3 and out.shape == q.shape and out.dtype == q.dtype, "q/out must be [S, Hq, D]")
@@ -149,14 +168,12 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     _need(k_cache.shape[3] == q.shape[2], "head_dim mismatch")
     s, hq, d = q.shape
     nb, bs, hkv, _ = k_cache.shape
-    need = decode_workspace_size(s, hq, d, max_context_len, partition_size) if partition_size else 0
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    part = _partition(partition_size)
+    workspace, ws_bytes = _decode_workspace(workspace, s, hq, hkv, d, max_context_len, part, q.device)
     _check(lib().pkv_paged_attention_decode(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
         s, block_tables.shape[1], int(max_context_len), nb, bs, hq, hkv, d, float(scale),
-        int(partition_size), _ptr(workspace), ws_bytes, _dtype_code(q), DECODE_ALGOS[algo],
+        part, _ptr(workspace), ws_bytes, _dtype_code(q), DECODE_ALGOS[algo],
         _stream(stream)))
     return out
 
@@ -229,7 +246,7 @@ class StoreLaunch(_Prepared):
 
 
 class DecodeLaunch(_Prepared):
-    """paged_attention_decode with fixed tensors; owns its split-K workspace."""
+    """paged_attention_decode with fixed tensors; owns its workspace."""
 
     def __init__(self, out, q, k_cache, v_cache, block_tables, context_lens, scale,
                  max_context_len, partition_size=0, algo="auto", workspace=None):
@@ -243,15 +260,14 @@ class DecodeLaunch(_Prepared):
               "context_lens must be int32 [S]")
         s, hq, d = q.shape
         nb, bs, hkv, _ = k_cache.shape
-        need = decode_workspace_size(s, hq, d, max_context_len, partition_size) if partition_size else 0
-        if need and workspace is None:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        part = _partition(partition_size)
+        workspace, ws_bytes = _decode_workspace(workspace, s, hq, hkv, d, max_context_len, part,
+                                                q.device)
         self._keep = (out, q, k_cache, v_cache, block_tables, context_lens, workspace)
         self._fn = "pkv_paged_attention_decode"
         self._args = (_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                       _ptr(context_lens), s, block_tables.shape[1], int(max_context_len), nb, bs,
-                      hq, hkv, d, float(scale), int(partition_size), _ptr(workspace), ws_bytes,
+                      hq, hkv, d, float(scale), part, _ptr(workspace), ws_bytes,
                       _dtype_code(q), DECODE_ALGOS[algo])
 
 
@@ -281,7 +297,7 @@ class PrefillLaunch(_Prepared):
 
 
 class DecodeStoreLaunch(_Prepared):
-    """paged_attention_decode_store with fixed tensors; owns its split-K workspace."""
+    """paged_attention_decode_store with fixed tensors; owns its workspace."""
 
     def __init__(self, out, q, k_cache, v_cache, block_tables, context_lens, k_new, v_new,
                  slot_mapping, scale, max_context_len, partition_size=0, algo="auto",

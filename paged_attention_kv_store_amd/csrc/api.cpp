@@ -91,10 +91,20 @@ extern "C" int pkv_kv_cache_store(const void* k, const void* v, void* k_cache, v
   return hip_status(pkv::launch_store(p, (hipStream_t)stream), fn);
 }
 
-extern "C" size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                            int32_t max_context_len, int32_t partition_size) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0 || partition_size <= 0)
+
+extern "C" size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                            int32_t head_dim, int32_t max_context_len,
+                                            int32_t partition_size) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_context_len < 0 ||
+      num_q_heads % num_kv_heads != 0)
     return 0;
+  if (partition_size == PKV_PARTITION_BALANCED) {
+    // one arrival counter per wave, then two pieces per wave, for the largest grid
+    const int64_t stride = pkv::bal_piece_stride(num_q_heads / num_kv_heads, head_dim);
+    return (size_t)(pkv::kBalMaxWaves * (int64_t)sizeof(int32_t) +
+                    2 * (int64_t)pkv::kBalMaxWaves * stride * (int64_t)sizeof(float));
+  }
+  if (partition_size <= 0) return 0;
   int32_t part;
   int64_t nparts;
   partitioning(max_context_len, partition_size, &part, &nparts);
@@ -127,9 +137,10 @@ int decode_impl(const char* fn, void* out, const void* q, const void* k_cache, c
   if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
     return fail(PKV_EINVAL, "%s: max_context_len %d outside [0, max_blocks_per_seq * block_size = %lld]", fn,
                 max_context_len, (long long)max_blocks_per_seq * block_size);
-  if (partition_size < 0 || partition_size % 16 != 0)
-    return fail(PKV_EINVAL, "%s: partition_size %d must be 0 or a positive multiple of 16", fn,
-                partition_size);
+  const bool balanced = partition_size == PKV_PARTITION_BALANCED;
+  if (!balanced && (partition_size < 0 || partition_size % 16 != 0))
+    return fail(PKV_EINVAL, "%s: partition_size %d must be 0, a positive multiple of 16 or "
+                "PKV_PARTITION_BALANCED", fn, partition_size);
   if (!std::isfinite(scale)) return fail(PKV_EINVAL, "%s: scale is not finite", fn);
   if (algo == PKV_DECODE_AUTO) algo = dtype == PKV_BF16 ? PKV_DECODE_MFMA : PKV_DECODE_VALU;
   if (algo == PKV_DECODE_MFMA) {
@@ -142,9 +153,20 @@ int decode_impl(const char* fn, void* out, const void* q, const void* k_cache, c
   }
   if (num_seqs > 65535 || num_kv_heads > 65535)
     return fail(PKV_EUNSUPPORTED, "%s: num_seqs and num_kv_heads are limited to 65535", fn);
+  if (balanced) {
+    if (algo != PKV_DECODE_MFMA)
+      return fail(PKV_EUNSUPPORTED, "%s: the work-balanced decode runs on the MFMA kernel (bf16)", fn);
+    if (num_seqs > pkv::kBalMaxSeqs)
+      return fail(PKV_EUNSUPPORTED, "%s: the work-balanced decode takes at most %d sequences", fn,
+                  pkv::kBalMaxSeqs);
+    if ((int64_t)num_seqs * num_kv_heads * ceil_div(max_context_len, 16) >= ((int64_t)1 << 30))
+      return fail(PKV_EUNSUPPORTED, "%s: more than 2^30 tiles for the work-balanced decode", fn);
+  }
   if (num_seqs == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
     return fail(PKV_EINVAL, "%s: null pointer", fn);
+  if (balanced && !aligned(out, 16))
+    return fail(PKV_EINVAL, "%s: the work-balanced decode needs a 16-byte aligned out", fn);
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 4) ||
       !aligned(block_tables, 4) || !aligned(context_lens, 4))
     return fail(PKV_EINVAL, "%s: q and caches must be 16-byte aligned; out and index arrays 4-byte", fn);
@@ -154,7 +176,7 @@ int decode_impl(const char* fn, void* out, const void* q, const void* k_cache, c
 
   int32_t part;
   int64_t nparts;
-  partitioning(max_context_len, partition_size, &part, &nparts);
+  partitioning(max_context_len, balanced ? 0 : partition_size, &part, &nparts);
   if ((int64_t)num_seqs * num_kv_heads * nparts > 0x7ffffff0)
     return fail(PKV_EUNSUPPORTED, "%s: %lld work items exceed the grid; use a larger partition_size", fn,
                 (long long)num_seqs * num_kv_heads * nparts);
@@ -180,9 +202,26 @@ int decode_impl(const char* fn, void* out, const void* q, const void* k_cache, c
   p.k_new = fused ? k_new : nullptr;
   p.v_new = fused ? v_new : nullptr;
   p.new_slots = fused ? new_slots : nullptr;
+  p.bal_counters = nullptr;
+  p.bal_pieces = nullptr;
+  p.bal_piece_stride = 0;
+  hipStream_t st = (hipStream_t)stream;
+  if (balanced) {
+    const size_t need = pkv_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                  max_context_len, partition_size);
+    if (!workspace || workspace_bytes < need)
+      return fail(PKV_EWORKSPACE, "%s: the work-balanced decode needs %zu workspace bytes, got %zu", fn,
+                  need, workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 256)) return fail(PKV_EINVAL, "%s: workspace must be 256-byte aligned", fn);
+    p.bal_counters = reinterpret_cast<int32_t*>(workspace);
+    p.bal_pieces = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
+                                            pkv::kBalMaxWaves * sizeof(int32_t));
+    p.bal_piece_stride = (int32_t)pkv::bal_piece_stride(group, head_dim);
+    return hip_status(pkv::launch_decode_balanced(p, head_dim, st), fn);
+  }
   if (nparts > 1) {
-    const size_t need = pkv_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len,
-                                                  partition_size);
+    const size_t need = pkv_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                  max_context_len, partition_size);
     if (!workspace || workspace_bytes < need)
       return fail(PKV_EWORKSPACE, "%s: split-K needs %zu workspace bytes, got %zu", fn, need,
                   workspace ? workspace_bytes : (size_t)0);
@@ -193,7 +232,6 @@ int decode_impl(const char* fn, void* out, const void* q, const void* k_cache, c
     p.ws_l = ws + cells;
     p.ws_o = ws + 2 * cells;
   }
-  hipStream_t st = (hipStream_t)stream;
   hipError_t e = algo == PKV_DECODE_MFMA ? pkv::launch_decode_mfma(p, head_dim, st)
                                          : pkv::launch_decode_valu(p, head_dim, dtype, st);
   if (e != hipSuccess) return hip_status(e, fn);

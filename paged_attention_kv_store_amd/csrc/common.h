@@ -54,7 +54,26 @@ struct DecodeParams {
   const void* k_new;
   const void* v_new;
   const int32_t* new_slots;
+  // Work-balanced decode only: arrival counters [kBalMaxWaves] (zero between
+  // calls) and per-wave pieces [2 * kBalMaxWaves][piece_stride].
+  int32_t* bal_counters;
+  float* bal_pieces;
+  int32_t bal_piece_stride;  // floats per piece
 };
+
+// Work-balanced decode limits. Every workgroup keeps the per-sequence tile
+// prefix sums in LDS, which bounds the batch; the piece area is sized for
+// the largest grid the launcher uses.
+constexpr int kBalMaxSeqs = 8192;
+constexpr int kBalMaxWorkgroups = 1024;
+constexpr int kBalWavesPerWorkgroup = 4;
+constexpr int kBalMaxWaves = kBalMaxWorkgroups * kBalWavesPerWorkgroup;
+
+// Floats of one piece: unnormalised output [G][D], then max [G] and sum [G],
+// rounded up to 16 bytes.
+inline int64_t bal_piece_stride(int group, int head_dim) {
+  return ((int64_t)group * head_dim + 2 * group + 3) / 4 * 4;
+}
 
 struct PrefillParams {
   void* out;
@@ -84,6 +103,7 @@ struct PrefillParams {
 hipError_t launch_store(const StoreParams& p, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeParams& p, int head_dim, int dtype, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_decode_balanced(const DecodeParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_splitk_reduce(const DecodeParams& p, int head_dim, int dtype, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t stream);
 

@@ -25,6 +25,9 @@
 #include "common.h"
 #include "device_utils.h"
 
+#include <algorithm>
+#include <atomic>
+
 namespace pkv {
 
 #ifndef PKV_DECODE_WAVES
@@ -38,6 +41,14 @@ constexpr int kTile = 16;
 #endif
 // Tiles in flight per wave in the matrix-core decode (register ring depth).
 constexpr int kStages = PKV_DECODE_STAGES;
+// Work-balanced decode: resident workgroups per compute unit (= waves per
+// SIMD) and tiles in flight per wave.
+#ifndef PKV_BAL_WG_PER_CU
+#define PKV_BAL_WG_PER_CU 1
+#endif
+#ifndef PKV_BAL_STAGES
+#define PKV_BAL_STAGES 3
+#endif
 #ifndef PKV_DECODE_WAVES_PER_SIMD
 #define PKV_DECODE_WAVES_PER_SIMD 2
 #endif
@@ -701,6 +712,439 @@ __global__ __launch_bounds__(D) void splitk_reduce_kernel(DecodeParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Work-balanced matrix-core decode (bf16)
+// ---------------------------------------------------------------------------
+// The batch's 16-token tiles form one list, kv-head slowest, then sequence,
+// then tile: kv-head g's tiles are a contiguous run of C = sum_s ceil(ctx_s/16)
+// tiles. A grid sized to fill the GPU once gives every wave an equal,
+// contiguous share of the list, so waves finish together however unequal the
+// context lengths are. A wave walks its share with the register ring of the
+// per-item kernel, switching sequence and kv-head as it crosses items (each
+// ring slot carries its own q rows). An item that lies wholly inside one
+// share is finished by that wave. An item cut by share boundaries leaves one
+// piece (max, sum, unnormalised output) per wave that touched it; the wave
+// that completes its piece last, as counted by an arrival counter (one per
+// wave index: that of the item's first wave), merges the pieces and writes
+// the output. No wave ever waits for another.
+// Waves are numbered contiguously per XCD (workgroups go to the 8 XCDs round
+// robin), so each XCD walks a contiguous part of the list: with 8 kv-heads,
+// one kv-head per XCD, and blocks shared between sequences are re-read from
+// one L2.
+namespace {
+constexpr int kBalThreads = 64 * kBalWavesPerWorkgroup;
+constexpr int kBalMinShare = 4;         // fewest tiles a wave is given
+constexpr int kInfoRows = 31;           // tile descriptor: live rows (1..16)
+constexpr int kInfoLast = 1 << 5;       //   last tile of its item
+constexpr int kInfoNewRow = 1 << 6;     //   its last row comes from the new K/V rows
+constexpr int kInfoBad = 1 << 7;        //   block id outside the pool
+
+// Relaxed agent-scope atomic accesses of the pieces: written through to, and
+// read from, the point where all XCDs see the same memory (each XCD has its
+// own L2), without a whole-cache write-back or invalidation.
+__device__ __forceinline__ void coherent_store(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float coherent_load(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int D>
+struct BalSlot {
+  uint4 k[D / 32];
+  uint4 v[4];
+  uint4 q[D / 32];
+  int s, g, t, info;
+};
+}  // namespace
+
+template <int D>
+__global__ __launch_bounds__(kBalThreads) __attribute__((amdgpu_waves_per_eu(PKV_BAL_WG_PER_CU, PKV_BAL_WG_PER_CU)))
+void decode_balanced_kernel(DecodeParams p) {
+  constexpr int kStages = PKV_BAL_STAGES;
+  constexpr int KCH = D / 32;
+  constexpr int EPL = D / 16;
+  __shared__ int s_cum[kBalMaxSeqs + 1];     // tiles of sequences before s
+  __shared__ uint8_t s_last[kBalMaxSeqs];    // rows in a sequence's last tile
+  __shared__ int s_wsum[kBalWavesPerWorkgroup];
+
+  const int S = p.num_seqs, Hkv = p.num_kv_heads, Hq = p.num_q_heads, G = p.group;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, qg = lane >> 4;
+  const int bs = p.block_size;
+  const int64_t row_elems = (int64_t)Hkv * D;
+  const int64_t num_slots = (int64_t)p.num_blocks * bs;
+
+  // Wave position in the list order: XCD-contiguous.
+  const int nwg = gridDim.x;   // a multiple of kXcds
+  const int pos = ((int)(blockIdx.x % kXcds) * (nwg / kXcds) + (int)(blockIdx.x / kXcds)) *
+                      kBalWavesPerWorkgroup + w;
+  const int NW = nwg * kBalWavesPerWorkgroup;
+
+  // New rows of the fused store: kRowLanes lanes move one item's K and V
+  // rows, 16 bytes each; the first pass is loaded now and stored at the end.
+  constexpr int kRowLanes = D / 4;              // 16-byte pieces of a K row and a V row
+  constexpr int kRowsPerPass = 64 / kRowLanes;
+  const int row_sub = lane % kRowLanes;
+  const bool row_is_v = row_sub >= kRowLanes / 2;
+  const int row_piece = row_sub % (kRowLanes / 2);
+  int new_item = pos * kRowsPerPass + lane / kRowLanes;
+  int new_slot = -1;
+  uint4 new_data = make_uint4(0, 0, 0, 0);
+  auto load_new_row = [&](int item) {
+    const int s = item / Hkv, g = item - (item / Hkv) * Hkv;
+    const int64_t off = ((int64_t)s * Hkv + g) * D + 8 * row_piece;
+    new_data = load16(reinterpret_cast<const uint16_t*>(row_is_v ? p.v_new : p.k_new) + off);
+    new_slot = p.new_slots[s];
+  };
+  auto store_new_row = [&](int item) {
+    const int s = item / Hkv, g = item - (item / Hkv) * Hkv;
+    // a sequence with an empty context has no new row in it
+    if (new_slot < 0 || new_slot >= num_slots || s_cum[s + 1] == s_cum[s]) return;
+    uint16_t* dst = const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(row_is_v ? p.v_cache : p.k_cache)) +
+                    (int64_t)new_slot * row_elems + g * D + 8 * row_piece;
+    *reinterpret_cast<uint4*>(dst) = new_data;
+  };
+  const bool fused = p.new_slots != nullptr;
+  if (fused && new_item < S * Hkv) load_new_row(new_item);
+
+  // ---- tiles per sequence and their exclusive prefix sums ------------------
+  for (int i = tid; i < S; i += kBalThreads) {
+    const int c = clamp_ctx(p.context_lens[i], p.max_ctx);
+    const int nt = (c + kTile - 1) / kTile;
+    s_cum[i] = nt;
+    s_last[i] = (uint8_t)(nt > 0 ? c - (nt - 1) * kTile : 0);
+  }
+  __syncthreads();
+  {
+    const int per = (S + kBalThreads - 1) / kBalThreads;
+    const int lo = min(tid * per, S), hi = min(lo + per, S);
+    int run = 0;
+    for (int i = lo; i < hi; ++i) run += s_cum[i];
+    int incl = run;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += o;
+    }
+    if (lane == 63) s_wsum[w] = incl;
+    __syncthreads();
+    int base = incl - run;
+    for (int i = 0; i < w; ++i) base += s_wsum[i];
+    for (int i = lo; i < hi; ++i) {
+      const int nt = s_cum[i];
+      s_cum[i] = base;
+      base += nt;
+    }
+    if (tid == kBalThreads - 1) s_cum[S] = base;   // the last thread's running sum is the total
+    __syncthreads();
+  }
+  const int C = s_cum[S];          // tiles per kv-head
+  const int T = C * Hkv;           // the host bounds this below 2^30
+  const int share = max((T + NW - 1) / NW, kBalMinShare);
+  const int a = min(pos * share, T);
+  const int cnt = min(T - a, share);
+
+  // ---- tile descriptors: lane l describes tile `base + l` of the share -----
+  int d_s = 0, d_g = 0, d_t = 0, d_info = 0, d_blk = 0;
+  auto describe = [&](int base) {
+    const int x = a + min(base + lane, cnt - 1);
+    const int g = x / C;
+    const int r = x - g * C;
+    int lo = 0, hi = S - 1;   // last sequence whose first tile is <= r (never an empty one)
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_cum[mid] <= r) lo = mid;
+      else hi = mid - 1;
+    }
+    const int s = lo, t = r - s_cum[s];
+    const bool last = t == s_cum[s + 1] - s_cum[s] - 1;
+    int info = last ? (int)s_last[s] | kInfoLast : kTile;
+    if (last && fused) {
+      const int slot = p.new_slots[s];
+      if (slot >= 0 && slot < num_slots) info |= kInfoNewRow;
+    }
+    d_blk = p.block_tables[(int64_t)s * p.max_blocks + (t * kTile) / bs];
+    d_s = s;
+    d_g = g;
+    d_t = t;
+    d_info = info;
+  };
+
+  const uint16_t* kc = reinterpret_cast<const uint16_t*>(p.k_cache);
+  const uint16_t* vc = reinterpret_cast<const uint16_t*>(p.v_cache);
+  const uint16_t* qbase = reinterpret_cast<const uint16_t*>(p.q);
+  const int head_in_group = n % G;   // padding columns repeat a real head (finite, never written)
+
+  // Loads of the share's j-th tile (j clamped to the last one) into a slot.
+  auto issue = [&](int j, BalSlot<D>& sl) {
+    if (j < cnt && j > 0 && (j & 63) == 0) describe(j);
+    const int idx = min(j, cnt - 1) & 63;
+    const int s = __builtin_amdgcn_readlane(d_s, idx);
+    const int g = __builtin_amdgcn_readlane(d_g, idx);
+    const int t = __builtin_amdgcn_readlane(d_t, idx);
+    int info = __builtin_amdgcn_readlane(d_info, idx);
+    int blk = __builtin_amdgcn_readlane(d_blk, idx);
+    if ((unsigned)blk >= (unsigned)p.num_blocks) {
+      blk = 0;
+      info |= kInfoBad;
+    }
+    sl.s = s;
+    sl.g = g;
+    sl.t = t;
+    sl.info = info;
+    const int64_t row0 = (int64_t)blk * bs + (t * kTile) % bs;
+    const uint16_t* kp = kc + (row0 + n) * row_elems + g * D + 8 * qg;
+    const uint16_t* vp = vc + (row0 + 4 * qg) * row_elems + g * D + EPL * n;
+    // the tile's last row is the new token: read it from the new rows
+    const int rn = (info & kInfoRows) - 1;
+    const bool ovr = (info & kInfoNewRow) != 0;
+    const int64_t nrow = ((int64_t)s * Hkv + g) * D;
+    if (ovr && n == rn) kp = reinterpret_cast<const uint16_t*>(p.k_new) + nrow + 8 * qg;
+    const uint16_t* qp = qbase + ((int64_t)s * Hq + g * G + head_in_group) * D + 8 * qg;
+#pragma unroll
+    for (int c = 0; c < KCH; ++c) sl.k[c] = load16(kp + 32 * c);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const uint16_t* src = (ovr && 4 * qg + st == rn)
+                                ? reinterpret_cast<const uint16_t*>(p.v_new) + nrow + EPL * n
+                                : vp + st * row_elems;
+      if constexpr (EPL == 8) {
+        sl.v[st] = load16(src);
+      } else {
+        const uint2 h = load8(src);
+        sl.v[st] = make_uint4(h.x, h.y, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < KCH; ++c) sl.q[c] = load16(qp + 32 * c);
+  };
+
+  // softmax state of the current item
+  float m_ref = neg_inf(), l_part = 0.f;
+  f32x4_t acc[EPL];
+  bool item_bad = false, seg_full = false, seg_first = true;
+  // items this wave left a piece of (at most its first and its last)
+  int pend_s0 = 0, pend_g0 = 0, pend_s1 = 0, pend_g1 = 0, npend = 0;
+  float* pieces = p.bal_pieces;
+  const int stride = p.bal_piece_stride;
+
+  auto flush = [&](int s, int g, bool complete) {
+    float l_tot = l_part;
+    l_tot += shfl_xor_f(l_tot, 16);
+    l_tot += shfl_xor_f(l_tot, 32);
+    if (complete) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int h = 4 * qg + r;
+        const float l = __shfl(l_tot, h, 64);
+        const float inv = item_bad ? __builtin_nanf("") : 1.f / l;
+        if (h < G) {
+          uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + ((int64_t)s * Hq + g * G + h) * D + EPL * n;
+          if constexpr (EPL == 8) {
+            uint32_t pk[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pk[e] = pack_bf16x2(acc[2 * e][r] * inv, acc[2 * e + 1][r] * inv);
+            *reinterpret_cast<uint4*>(o) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+          } else {
+            *reinterpret_cast<uint2*>(o) = make_uint2(pack_bf16x2(acc[0][r] * inv, acc[1][r] * inv),
+                                                     pack_bf16x2(acc[2][r] * inv, acc[3][r] * inv));
+          }
+        }
+      }
+    } else {
+      // agent-coherent stores: complete means visible to every XCD
+      float* pc = pieces + (int64_t)(2 * pos + (seg_first ? 0 : 1)) * stride;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int h = 4 * qg + r;
+        if (h < G) {
+          float* o = pc + h * D + EPL * n;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) coherent_store(o + e, acc[e][r]);
+        }
+      }
+      if (qg == 0 && n < G) {
+        coherent_store(pc + G * D + n, m_ref);
+        coherent_store(pc + G * D + G + n, item_bad ? __builtin_nanf("") : l_tot);
+      }
+      if (npend == 0) {
+        pend_s0 = s;
+        pend_g0 = g;
+      } else {
+        pend_s1 = s;
+        pend_g1 = g;
+      }
+      ++npend;
+    }
+    seg_first = false;
+  };
+
+  // Scores, online softmax and P.V of one tile (the same arithmetic as the
+  // per-item kernel), then the end-of-item bookkeeping.
+  auto compute = [&](int j, const BalSlot<D>& sl) {
+    const int info = sl.info;
+    if (j == 0 || sl.t == 0) {
+      m_ref = neg_inf();
+      l_part = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      item_bad = false;
+      seg_full = sl.t == 0;
+    }
+    item_bad |= (info & kInfoBad) != 0;
+    const int valid = info & kInfoRows;
+    f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < KCH; ++c)
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bit_cast_to<bf16x8_t>(sl.k[c]), bit_cast_to<bf16x8_t>(sl.q[c]),
+                                                   sc, 0, 0, 0);
+    float x[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x[r] = (4 * qg + r < valid) ? sc[r] * p.scale_log2 : neg_inf();
+    float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    mt = fmaxf(mt, shfl_xor_f(mt, 16));
+    mt = fmaxf(mt, shfl_xor_f(mt, 32));
+    if (__any(mt > m_ref + kRescaleThreshold)) {
+      const float m_new = fmaxf(m_ref, mt);
+      const float alpha = fast_exp2(m_ref - m_new);
+      l_part *= alpha;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float f = __shfl(alpha, 4 * qg + r, 64);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e][r] *= f;
+      }
+      m_ref = m_new;
+    }
+    uint32_t pw[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      pw[h] = pack_bf16x2(fast_exp2(x[2 * h] - m_ref), fast_exp2(x[2 * h + 1] - m_ref));
+      l_part += bf16_lo(pw[h]) + bf16_hi(pw[h]);
+    }
+    const short4_t pa = __builtin_bit_cast(short4_t, make_uint2(pw[0], pw[1]));
+    uint32_t vd[4][4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const bool live = 4 * qg + st < valid;   // rows past the context may hold anything
+      vd[st][0] = live ? sl.v[st].x : 0u;
+      vd[st][1] = live ? sl.v[st].y : 0u;
+      vd[st][2] = live ? sl.v[st].z : 0u;
+      vd[st][3] = live ? sl.v[st].w : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+      const uint32_t b0 = __builtin_amdgcn_perm(vd[1][i / 2], vd[0][i / 2], sel);
+      const uint32_t b1 = __builtin_amdgcn_perm(vd[3][i / 2], vd[2][i / 2], sel);
+      acc[i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, __builtin_bit_cast(short4_t, make_uint2(b0, b1)),
+                                                         acc[i], 0, 0, 0);
+    }
+    if ((info & kInfoLast) || j == cnt - 1) flush(sl.s, sl.g, seg_full && (info & kInfoLast));
+  };
+
+  if (cnt > 0) {
+    describe(0);
+    BalSlot<D> buf[kStages];
+#pragma unroll
+    for (int i = 0; i < kStages - 1; ++i) issue(i, buf[i]);
+    for (int j = 0; j < cnt; j += kStages) {
+#pragma unroll
+      for (int u = 0; u < kStages; ++u) {
+        issue(j + u + kStages - 1, buf[(u + kStages - 1) % kStages]);
+        if (j + u < cnt) compute(j + u, buf[u]);
+      }
+    }
+  }
+
+  // ---- items cut by share boundaries: arrive, and merge if last ------------
+  for (int i = 0; i < npend; ++i) {
+    const int s = i == 0 ? pend_s0 : pend_s1, g = i == 0 ? pend_g0 : pend_g1;
+    const int A = g * C + s_cum[s];
+    const int B = A + (s_cum[s + 1] - s_cum[s]);
+    const int np = (B - 1) / share - A / share + 1;
+    // The item's first wave holds the item's start and, the item running past
+    // its share, ends with it: no other cut item starts in that wave, so the
+    // wave's index names the item's counter.
+    int* counter = p.bal_counters + A / share;
+    // The piece's stores have completed (at the agent coherence point) before
+    // the arrival is counted; the memory clobber keeps the compiler from
+    // moving memory accesses across.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    int old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __builtin_amdgcn_readfirstlane(old);
+    if (old != np - 1) continue;
+    // Last arrival: every other piece completed before its arrival was counted,
+    // and the coherent loads below are issued after this one's count returned.
+    asm volatile("" ::: "memory");
+    const int w0 = A / share;
+    for (int idx = lane; idx < G * (D / 4); idx += 64) {
+      const int h = idx / (D / 4), d4 = idx - h * (D / 4);
+      float M = neg_inf(), L = 0.f;
+      float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+      // eight pieces' loads in flight at a time, then their online merge
+      constexpr int kBatch = 8;
+      for (int k0 = 0; k0 < np; k0 += kBatch) {
+        float mv[kBatch], lv[kBatch];
+        float4 ov[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int pw = w0 + min(k0 + u, np - 1);
+          const float* pc = pieces + (int64_t)(2 * pw + (pw * share < A ? 1 : 0)) * stride;
+          const float* po = pc + h * D + 4 * d4;
+          mv[u] = coherent_load(pc + G * D + h);
+          lv[u] = coherent_load(pc + G * D + G + h);
+          ov[u] = make_float4(coherent_load(po), coherent_load(po + 1), coherent_load(po + 2),
+                              coherent_load(po + 3));
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          if (k0 + u >= np) break;   // clamped repeats of the last piece are not counted
+          const float m = mv[u];
+          if (m > M) {
+            const float f = (M == neg_inf()) ? 0.f : fast_exp2(M - m);
+            L *= f;
+            O.x *= f;
+            O.y *= f;
+            O.z *= f;
+            O.w *= f;
+            M = m;
+          }
+          const float f = (m == neg_inf()) ? 0.f : fast_exp2(m - M);
+          L += f * lv[u];
+          O.x += f * ov[u].x;
+          O.y += f * ov[u].y;
+          O.z += f * ov[u].z;
+          O.w += f * ov[u].w;
+        }
+      }
+      const float inv = 1.f / L;
+      uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + ((int64_t)s * Hq + g * G + h) * D + 4 * d4;
+      *reinterpret_cast<uint2*>(o) = make_uint2(pack_bf16x2(O.x * inv, O.y * inv), pack_bf16x2(O.z * inv, O.w * inv));
+    }
+    if (lane == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // for the next call
+  }
+
+  // ---- sequences with an empty context: zero output rows -------------------
+  for (int s = pos; s < S; s += NW) {
+    if (s_cum[s + 1] != s_cum[s]) continue;
+    uint4* o = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.out) + (int64_t)s * Hq * D);
+    for (int i = lane; i < Hq * D / 8; i += 64) o[i] = make_uint4(0, 0, 0, 0);
+  }
+
+  // ---- fused store: the new rows go to their cache slots --------------------
+  if (fused) {
+    if (new_item < S * Hkv) store_new_row(new_item);
+    for (new_item += NW * kRowsPerPass; new_item < S * Hkv; new_item += NW * kRowsPerPass) {
+      load_new_row(new_item);
+      store_new_row(new_item);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 static dim3 decode_grid(const DecodeParams& p) {
@@ -741,6 +1185,37 @@ static hipError_t launch_mfma_d(const DecodeParams& p, hipStream_t stream) {
 
 hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, hipStream_t stream) {
   return head_dim == 64 ? launch_mfma_d<64>(p, stream) : launch_mfma_d<128>(p, stream);
+}
+
+// Compute units of the current device (queried once per device).
+static int device_compute_units() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+  int cus = cache[dev].load(std::memory_order_relaxed);
+  if (cus > 0) return cus;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+// PKV_BAL_WG_PER_CU workgroups per compute unit (at most the kernel's
+// occupancy of two), so the whole grid is resident at once; fewer when the
+// batch has too few tiles to give every wave kBalMinShare of them.
+hipError_t launch_decode_balanced(const DecodeParams& p, int head_dim, hipStream_t stream) {
+  const int64_t tiles = (int64_t)p.num_seqs * p.num_kv_heads * ((p.max_ctx + kTile - 1) / kTile);
+  const int64_t per_wg = (int64_t)kBalMinShare * kBalWavesPerWorkgroup;
+  int64_t nwg = std::min<int64_t>(PKV_BAL_WG_PER_CU * (int64_t)device_compute_units(), kBalMaxWorkgroups);
+  nwg = std::min<int64_t>(nwg, std::max<int64_t>((tiles + per_wg - 1) / per_wg, 1));
+  nwg = std::min<int64_t>((nwg + kXcds - 1) / kXcds * kXcds, kBalMaxWorkgroups);
+  const dim3 grid((unsigned)nwg);
+  if (head_dim == 64)
+    hipLaunchKernelGGL(decode_balanced_kernel<64>, grid, dim3(kBalThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(decode_balanced_kernel<128>, grid, dim3(kBalThreads), 0, stream, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_splitk_reduce(const DecodeParams& p, int head_dim, int dtype, hipStream_t stream) {

@@ -71,6 +71,13 @@ def _decode(lib, **over):
     (dict(q=1028), binding.PKV_EINVAL),
     (dict(scale=float("nan")), binding.PKV_EINVAL),
     (dict(S=70000), binding.PKV_EUNSUPPORTED),
+    (dict(part=-1), binding.PKV_EUNSUPPORTED),                       # balanced needs bf16
+    (dict(part=-1, dtype=1, algo=1), binding.PKV_EUNSUPPORTED),      # ... and the MFMA kernel
+    (dict(part=-1, dtype=1, S=9000), binding.PKV_EUNSUPPORTED),      # at most 8192 sequences
+    (dict(part=-1, dtype=1), binding.PKV_EWORKSPACE),
+    (dict(part=-1, dtype=1, ws=1040, ws_bytes=1 << 30), binding.PKV_EINVAL),   # 256-byte alignment
+    (dict(part=-1, dtype=1, out=1032), binding.PKV_EINVAL),          # out 16-byte aligned
+    (dict(part=-2), binding.PKV_EINVAL),
 ])
 def test_decode_rejects(over, code):
     lib = pkv.lib()
@@ -87,10 +94,20 @@ def test_decode_empty_batch_is_a_no_op():
 def test_workspace_size():
     lib = pkv.lib()
     # 32 seqs x 32 heads x ceil(32768/512)=64 partitions x (128 + 2) floats
-    assert pkv.decode_workspace_size(32, 32, 128, 32768, 512) == 32 * 32 * 64 * 130 * 4
-    assert pkv.decode_workspace_size(32, 32, 128, 512, 512) == 0      # one partition
-    assert pkv.decode_workspace_size(32, 32, 128, 513, 512) == 32 * 32 * 2 * 130 * 4
-    assert lib.pkv_decode_workspace_size(4, 8, 64, 100, 0) == 0
+    assert pkv.decode_workspace_size(32, 32, 8, 128, 32768, 512) == 32 * 32 * 64 * 130 * 4
+    assert pkv.decode_workspace_size(32, 32, 8, 128, 512, 512) == 0      # one partition
+    assert pkv.decode_workspace_size(32, 32, 8, 128, 513, 512) == 32 * 32 * 2 * 130 * 4
+    assert lib.pkv_decode_workspace_size(4, 8, 4, 64, 100, 0) == 0
+    assert lib.pkv_decode_workspace_size(4, 8, 3, 64, 100, 0) == 0       # Hq not a multiple of Hkv
+    # work-balanced: 4096 int32 counters, then 2 pieces per wave of the largest
+    # grid (4096 waves), each G*D + 2G floats rounded up to 4; no dependence on
+    # num_seqs or max_context_len
+    counters = 4096 * 4
+    assert pkv.decode_workspace_size(32, 32, 8, 128, 4096, "balanced") == \
+        counters + 2 * 4096 * (4 * 128 + 8) * 4
+    assert pkv.decode_workspace_size(60, 16, 8, 128, 1024, -1) == counters + 2 * 4096 * 260 * 4
+    assert pkv.decode_workspace_size(7000, 16, 8, 128, 9, -1) == counters + 2 * 4096 * 260 * 4
+    assert pkv.decode_workspace_size(3, 3, 1, 64, 10, -1) == counters + 2 * 4096 * 200 * 4
 
 
 def _store(lib, **over):
