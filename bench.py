@@ -411,7 +411,47 @@ def summarize_pmc(fetch_csv, write_csv):
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1)
+    with open(TRAFFIC_FILE[:-5] + ".md", "w") as f:
+        f.write(traffic_markdown(out))
     print(json.dumps(out))
+
+
+def traffic_markdown(t):
+    c = t["calibration"]
+    return f"""# HBM traffic of the decode kernel, Qwen3-shaped layer
+
+Kernel: `decode_mfma_kernel<128, 4>` (single pass, the store of the 60 new K/V rows fused into it,
+as the benchmark's step launches it), one layer of the Qwen3-0.6B-shaped decode step
+(60 sequences, contexts U{{64..1024}}, 16 q / 8 kv heads, head_dim 128, block_size 16, bf16),
+{t['launches_averaged']} launches on distinct layer caches (4.7 GB in total, so the 256 MB last-level cache
+cannot hold them).
+
+Commands (from the repository root on one MI355X):
+
+```
+rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch_out> -o run -- python3 bench.py --pmc-pass
+rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write_out> -o run -- python3 bench.py --pmc-pass
+python3 bench.py --summarize-pmc <fetch_out>/run_counter_collection.csv <write_out>/run_counter_collection.csv
+```
+
+Calibration: the last dispatch of each pass is a plain copy of known size, a `kv_store_kernel`
+moving 65536 rows of 2 KiB with identity slots ({c['read_bytes']:,} bytes read including the slot
+array, {c['write_bytes']:,} bytes written). The counters read {int(c['fetch_raw']):,} bytes fetched
+(factor {c['fetch_factor']:.3f}) and {int(c['write_raw']):,} bytes written (factor {c['write_factor']:.3f}) for it;
+the decode readings are scaled by the same factors.
+
+| quantity | bytes per launch |
+|---|---|
+| FETCH_SIZE, raw (mean of {t['launches_averaged']} launches) | {int(t['fetch_bytes_raw_per_launch']):,} |
+| WRITE_SIZE, raw (mean of {t['launches_averaged']} launches) | {int(t['write_bytes_raw_per_launch']):,} |
+| HBM bytes, calibrated | {int(t['hbm_bytes_per_launch']):,} |
+| algorithmic bytes (K/V rows in context, q, out, table entries, lengths, the fused store's rows and slots) | {int(t['algorithmic_bytes_per_launch']):,} |
+| traffic / algorithmic | {t['hbm_bytes_per_launch'] / t['algorithmic_bytes_per_launch']:.3f} |
+
+The written bytes are the output (60 x 16 x 128 bf16 = 245,760) plus the 60 stored K and V rows
+(245,760). Machine-readable values: `decode_qwen3_traffic.json` (bench.py reports them as
+`traffic` only while the decode kernel's source hash, {t['decode_source_hash']}, matches).
+"""
 
 
 def summarize_trace(stats_csv, trace_csv, out_md, command):
