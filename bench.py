@@ -64,10 +64,15 @@ def log(msg):
 
 
 def decode_source_hash():
+    """Hash of the decode kernel's code: the sources with // comments and
+    whitespace removed, so that editing a comment keeps measured counters."""
     h = hashlib.sha256()
     for name in DECODE_SOURCES:
-        with open(os.path.join(ROOT, "paged_attention_kv_store_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "paged_attention_kv_store_amd", "csrc", name)) as f:
+            for line in f:
+                code = line.split("//", 1)[0].strip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

@@ -1,6 +1,7 @@
 // Decode attention over a paged KV cache: one query row per (sequence, q-head).
 //
-// Work unit: one workgroup of 4 wavefronts per (kv-head, partition, sequence).
+// Per-item kernels (decode_valu_kernel, decode_mfma_kernel):
+// one workgroup of 4 wavefronts per (kv-head, partition, sequence).
 // The grid is one-dimensional and decode_item maps a workgroup to its item.
 // It serves all G = Hq/Hkv q-heads that share the kv-head, so each K/V byte is
 // read once for the whole group. The partition's tokens are cut into 16-token
@@ -19,9 +20,12 @@
 //    a row; P.V is vector FMAs. Any dtype, G <= 8.
 //  * decode_mfma_kernel (bf16): q.k for the 16 tile tokens x the G heads is a
 //    16x16x32 bf16 matrix-core product per 32 dims of head_dim (the G heads
-//    are padded to 16 columns); P.V is 16x16x4 fp32 matrix-core steps whose
-//    B operand is V read in plain row order (4 tokens x 16 column groups), so
-//    no transposition of V is needed and P stays in fp32.
+//    are padded to 16 columns); P.V is 16x16x16 bf16 matrix-core steps with
+//    P rounded to bf16 and the B operand built in-lane from whole V rows, so
+//    no transposition of V is needed.
+//
+// decode_balanced_kernel (bf16) computes the same with the work spread
+// evenly over a grid that fills the GPU once (see its own comment).
 #include "common.h"
 #include "device_utils.h"
 
