@@ -23,9 +23,10 @@ profiles/decode_qwen3_traffic.json, null if the kernel source changed since),
 a plain-copy bandwidth measured in the same run, tokens/s, the other
 standard workloads (prefix-shared batch, long-context split-K, mixed chunked
 prefill + decode with the prefill's matrix-core utilisation, verification
-of 4 drafted-token rows per sequence), a parity
-sample against the CPU oracle, and the oracle itself timed on a bounded
-sample of the headline workload on one host core (a baseline, not a target).
+of 4 drafted-token rows per sequence, the headline step over an E4M3
+cache), a parity sample against the CPU oracle, and the oracle itself timed
+on a bounded sample of the headline workload on one host core (a baseline,
+not a target).
 
 Other modes: --pmc-pass runs only the headline decode launches and one
 calibration copy of known size (for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE);
@@ -81,7 +82,7 @@ def decode_source_hash():
 # --------------------------------------------------------------------------
 
 def decode_bytes(b: W.PagedBatch, unique_blocks=False) -> float:
-    e = b.q.element_size()
+    e = b.k_cache.element_size()        # 1 for E4M3 caches
     hkv, d, bs = b.num_kv_heads, b.head_dim, b.block_size
     ctx = b.pool.context_lens.astype(np.int64)
     if unique_blocks:
@@ -96,7 +97,7 @@ def decode_bytes(b: W.PagedBatch, unique_blocks=False) -> float:
     else:
         kv_rows = int(ctx.sum())
     kv = kv_rows * hkv * d * e * 2
-    qo = 2 * b.q.numel() * e
+    qo = 2 * b.q.numel() * b.q.element_size()
     tables = int((-(-ctx // bs)).sum()) * 4 + len(ctx) * 4
     return float(kv + qo + tables)
 
@@ -105,8 +106,9 @@ def store_bytes(b: W.PagedBatch) -> float:
     if b.k_new is None:
         return 0.0
     t = int((b.slot_mapping >= 0).sum().item())
-    row = b.num_kv_heads * b.head_dim * b.q.element_size()
-    return float(2 * 2 * t * row + 4 * len(b.slot_mapping))
+    row_in = b.num_kv_heads * b.head_dim * b.k_new.element_size()
+    row_out = b.num_kv_heads * b.head_dim * b.k_cache.element_size()
+    return float(2 * t * (row_in + row_out) + 4 * len(b.slot_mapping))
 
 
 def prefill_flops(b: W.PagedBatch, causal=True) -> float:
@@ -280,8 +282,36 @@ def balanced_ms(b, bt, cl, steps, warmup):
     return time_region(dec, steps, warmup)
 
 
-def secondary(device, steps, warmup, algo):
-    res = {}
+def fp8_step(device, steps, warmup, bf16_step_ms):
+    """The headline step over E4M3 caches: per layer, decode with the
+    quantising store of the 60 new rows fused in, 28 layers, one graph replay."""
+    wl = W.qwen3_decode_fp8(device=device)
+    b0 = wl.batches[0]
+    bt = torch.as_tensor(b0.pool.block_tables, device=device)
+    cl = torch.as_tensor(b0.pool.context_lens, device=device)
+    calls, outs = [], []
+    for b in wl.batches:
+        out = torch.empty_like(b.q)
+        outs.append(out)
+        calls.append(pkv.DecodeStoreFp8Launch(out, b.q, b.k_cache, b.v_cache, b.k_scale, b.v_scale, bt,
+                                              cl, b.k_new, b.v_new, b.slot_mapping, b.scale, b.max_ctx))
+
+    def step():
+        for c in calls:
+            c()
+    graph = capture_step(step, outs)
+    ms = time_region(graph.replay, steps, warmup)
+    per_launch = decode_bytes(b0) + store_bytes(b0)
+    dec_ms = time_each_launch(calls, 4)
+    return {"ms_per_step": ms, "GBps": per_launch * len(calls) / ms / 1e6,
+            "tokens_per_s": b0.num_seqs / (ms * 1e-3), "speedup_vs_bf16_step": bf16_step_ms / ms,
+            "decode_avg_launch_us": dec_ms * 1e3, "decode_GBps": per_launch / dec_ms / 1e6,
+            "cache": "E4M3 codes, per-kv-head scales; store fused into decode"}
+
+
+def secondary(device, steps, warmup, algo, bf16_step_ms):
+    res = {"qwen3_fp8": fp8_step(device, steps, warmup, bf16_step_ms)}
+    torch.cuda.empty_cache()
     b = W.llama_prefix(device=device).batches[0]
     bt = torch.as_tensor(b.pool.block_tables, device=device)
     cl = torch.as_tensor(b.pool.context_lens, device=device)
@@ -612,7 +642,7 @@ def main():
             del graph, run
         torch.cuda.empty_cache()
         log("secondary workloads")
-        result["secondary"] = secondary(device, max(5, args.steps // 2), 3, args.algo)
+        result["secondary"] = secondary(device, max(5, args.steps // 2), 3, args.algo, ms)
     if not args.no_cpu_baseline:
         log("oracle baseline on the host")
         result["cpu_baseline"] = cpu_baseline(W.qwen3_decode(device="cpu", layers=1).batches[0])

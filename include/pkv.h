@@ -186,6 +186,65 @@ int pkv_paged_attention_decode_store(void* out, const void* q, void* k_cache, vo
                                      pkv_dtype dtype, int32_t algo, void* stream);
 
 /*
+ * E4M3 KV cache. The pages list support for quantized models among the
+ * engine's features ("A vLLM engine small enough to read in one sitting",
+ * section "Key highlights"); the format and scaling are this library's
+ * reading. Cache elements are OCP FP8 E4M3 codes (1 sign, 4 exponent bits
+ * with bias 7, 3 mantissa bits, no infinity, 0x7f/0xff NaN, largest finite
+ * 448) in the same [num_blocks, block_size, num_kv_heads, head_dim] layout,
+ * one byte each. k_scale and v_scale are device float32 arrays
+ * [num_kv_heads]: a code c of kv-head g stands for value(c) * scale[g].
+ *
+ * kv_cache_store_fp8: like pkv_kv_cache_store, but each element x of k / v
+ * (src_dtype bf16 or fp32, [num_tokens, num_kv_heads, head_dim], 16-byte
+ * aligned) is stored as the code of t = x / scale[g] (one IEEE float32
+ * division), rounded to nearest with ties to the even code, saturated to
+ * +-448; a NaN is stored as 0x7f. The result is bit-exact. Slots as in
+ * pkv_kv_cache_store (negative: no write; past the pool: skipped).
+ * head_dim must be a multiple of 8; caches 8-byte aligned.
+ */
+int pkv_kv_cache_store_fp8(const void* k, const void* v, void* k_cache, void* v_cache,
+                           const int32_t* slot_mapping, const float* k_scale, const float* v_scale,
+                           int32_t num_tokens, int32_t num_blocks, int32_t block_size,
+                           int32_t num_kv_heads, int32_t head_dim, pkv_dtype src_dtype,
+                           void* stream);
+
+/*
+ * paged_attention_decode_fp8: pkv_paged_attention_decode over E4M3 caches
+ * (values dequantised with k_scale / v_scale), q and out bf16, on the MFMA
+ * kernel. partition_size 0 or a positive multiple of 16 (split-K, with the
+ * same workspace); the work-balanced mode is not offered here. The other
+ * arguments, results and errors are those of pkv_paged_attention_decode.
+ */
+int pkv_paged_attention_decode_fp8(void* out, const void* q, const void* k_cache,
+                                   const void* v_cache, const float* k_scale, const float* v_scale,
+                                   const int32_t* block_tables, const int32_t* context_lens,
+                                   int32_t num_seqs, int32_t max_blocks_per_seq,
+                                   int32_t max_context_len, int32_t num_blocks, int32_t block_size,
+                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   float scale, int32_t partition_size, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/*
+ * paged_attention_decode_store_fp8: pkv_kv_cache_store_fp8 of one new row
+ * per sequence (bf16 k_new / v_new [num_seqs, num_kv_heads, head_dim],
+ * quantised exactly as that call does) followed by
+ * pkv_paged_attention_decode_fp8, in one launch, under the precondition and
+ * slot rules of pkv_paged_attention_decode_store. The codes of the new row
+ * are used for position ctx-1 straight from the quantisation.
+ */
+int pkv_paged_attention_decode_store_fp8(void* out, const void* q, void* k_cache, void* v_cache,
+                                         const float* k_scale, const float* v_scale,
+                                         const int32_t* block_tables, const int32_t* context_lens,
+                                         const void* k_new, const void* v_new,
+                                         const int32_t* slot_mapping, int32_t num_seqs,
+                                         int32_t max_blocks_per_seq, int32_t max_context_len,
+                                         int32_t num_blocks, int32_t block_size,
+                                         int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, float scale, int32_t partition_size,
+                                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * paged_attention_prefill_chunk: attention of packed query chunks over their
  * paged contexts. Chunk c owns q rows cu_seqlens_q[c] .. cu_seqlens_q[c+1]-1
  * (L_c rows); context_lens[c] >= L_c counts its cached tokens plus its own

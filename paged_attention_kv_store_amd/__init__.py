@@ -8,16 +8,23 @@ library; the first call does, and raises if it has not been built.
 
 from .binding import (  # noqa: F401
     DECODE_ALGOS,
+    PARTITION_BALANCED,
+    DecodeFp8Launch,
     DecodeLaunch,
+    DecodeStoreFp8Launch,
     DecodeStoreLaunch,
     PkvError,
     PrefillLaunch,
+    StoreFp8Launch,
     StoreLaunch,
     decode_workspace_size,
     kv_cache_store,
+    kv_cache_store_fp8,
     lib,
     library_path,
     paged_attention_decode,
+    paged_attention_decode_fp8,
     paged_attention_decode_store,
+    paged_attention_decode_store_fp8,
     paged_attention_prefill_chunk,
 )

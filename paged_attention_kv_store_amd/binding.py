@@ -38,6 +38,15 @@ _SIGNATURES = {
     "pkv_paged_attention_decode_store": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
                                           _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _i32,
                                           _vp, ctypes.c_size_t, ctypes.c_int, _i32, _vp], ctypes.c_int),
+    "pkv_kv_cache_store_fp8": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                ctypes.c_int, _vp], ctypes.c_int),
+    "pkv_paged_attention_decode_fp8": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                        _i32, _i32, _i32, _i32, ctypes.c_float, _i32, _vp,
+                                        ctypes.c_size_t, _vp], ctypes.c_int),
+    "pkv_paged_attention_decode_store_fp8": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                              _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                              ctypes.c_float, _i32, _vp, ctypes.c_size_t, _vp],
+                                             ctypes.c_int),
     "pkv_paged_attention_prefill_chunk": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                                            _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                            ctypes.c_float, _i32, ctypes.c_int, _vp], ctypes.c_int),
@@ -189,6 +198,41 @@ def paged_attention_decode_store(out, q, k_cache, v_cache, block_tables, context
     return out
 
 
+def _check_fp8_cache(k_cache, v_cache, k_scale, v_scale):
+    _need(k_cache.dtype == v_cache.dtype == torch.uint8 and k_cache.dim() == 4
+          and v_cache.shape == k_cache.shape, "E4M3 caches must be uint8 [NB, bs, Hkv, D]")
+    hkv = k_cache.shape[2]
+    _need(k_scale.dtype == v_scale.dtype == torch.float32 and k_scale.shape == (hkv,)
+          and v_scale.shape == (hkv,), "k_scale, v_scale must be float32 [Hkv]")
+
+
+def kv_cache_store_fp8(k, v, k_cache, v_cache, slot_mapping, k_scale, v_scale, stream=None):
+    """Quantise new K/V rows (bf16 or fp32 [T, Hkv, D]) to E4M3 codes with one
+    scale per kv-head and write them into uint8 caches [NB, bs, Hkv, D]."""
+    StoreFp8Launch(k, v, k_cache, v_cache, slot_mapping, k_scale, v_scale)(stream)
+
+
+def paged_attention_decode_fp8(out, q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                               context_lens, scale, max_context_len, partition_size=0,
+                               workspace=None, stream=None):
+    """Decode over E4M3 caches (uint8 [NB, bs, Hkv, D], scales float32 [Hkv]);
+    q and out bf16 [S, Hq, D]."""
+    DecodeFp8Launch(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, scale,
+                    max_context_len, partition_size, workspace)(stream)
+    return out
+
+
+def paged_attention_decode_store_fp8(out, q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                                     context_lens, k_new, v_new, slot_mapping, scale,
+                                     max_context_len, partition_size=0, workspace=None, stream=None):
+    """Quantise and store one new row per sequence (bf16 k_new / v_new
+    [S, Hkv, D], at the slot of position context_lens[s]-1) and decode over
+    the E4M3 caches, in one launch."""
+    DecodeStoreFp8Launch(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, k_new,
+                         v_new, slot_mapping, scale, max_context_len, partition_size, workspace)(stream)
+    return out
+
+
 def paged_attention_prefill_chunk(out, q, k_cache, v_cache, block_tables, cu_seqlens_q,
                                   context_lens, scale, max_q_len, max_context_len, causal=True,
                                   stream=None):
@@ -314,3 +358,66 @@ class DecodeStoreLaunch(_Prepared):
         self._keep = base._keep + (k_new, v_new, slot_mapping)
         self._fn = "pkv_paged_attention_decode_store"
         self._args = a[:6] + (_ptr(k_new), _ptr(v_new), _ptr(slot_mapping)) + a[6:]
+
+
+class StoreFp8Launch(_Prepared):
+    """kv_cache_store_fp8 with fixed tensors."""
+
+    def __init__(self, k, v, k_cache, v_cache, slot_mapping, k_scale, v_scale):
+        _dev(k, v, k_cache, v_cache, slot_mapping, k_scale, v_scale)
+        _check_fp8_cache(k_cache, v_cache, k_scale, v_scale)
+        _need(k.dim() == 3 and v.shape == k.shape and k.dtype == v.dtype, "k, v must be [T, Hkv, D]")
+        _need(k_cache.shape[2:] == k.shape[1:], "cache and new rows disagree on heads/dims")
+        _need(slot_mapping.dtype == torch.int32 and slot_mapping.shape == (k.shape[0],),
+              "slot_mapping must be int32 [T]")
+        nb, bs, hkv, d = k_cache.shape
+        self._keep = (k, v, k_cache, v_cache, slot_mapping, k_scale, v_scale)
+        self._fn = "pkv_kv_cache_store_fp8"
+        self._args = (_ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping),
+                      _ptr(k_scale), _ptr(v_scale), k.shape[0], nb, bs, hkv, d, _dtype_code(k))
+
+
+class DecodeFp8Launch(_Prepared):
+    """paged_attention_decode_fp8 with fixed tensors; owns its split-K workspace."""
+
+    def __init__(self, out, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
+                 scale, max_context_len, partition_size=0, workspace=None):
+        _dev(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens)
+        _check_fp8_cache(k_cache, v_cache, k_scale, v_scale)
+        _need(q.dim() == 3 and out.shape == q.shape and q.dtype == out.dtype == torch.bfloat16,
+              "q/out must be bf16 [S, Hq, D]")
+        _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
+              and block_tables.shape[0] == q.shape[0], "block_tables must be int32 [S, MB]")
+        _need(context_lens.dtype == torch.int32 and context_lens.shape == (q.shape[0],),
+              "context_lens must be int32 [S]")
+        _need(k_cache.shape[3] == q.shape[2], "head_dim mismatch")
+        s, hq, d = q.shape
+        nb, bs, hkv, _ = k_cache.shape
+        part = int(partition_size)
+        workspace, ws_bytes = _decode_workspace(workspace, s, hq, hkv, d, max_context_len, part,
+                                                q.device)
+        self._keep = (out, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, workspace)
+        self._fn = "pkv_paged_attention_decode_fp8"
+        self._args = (_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                      _ptr(block_tables), _ptr(context_lens), s, block_tables.shape[1],
+                      int(max_context_len), nb, bs, hq, hkv, d, float(scale), part,
+                      _ptr(workspace), ws_bytes)
+
+
+class DecodeStoreFp8Launch(_Prepared):
+    """paged_attention_decode_store_fp8 with fixed tensors; owns its split-K workspace."""
+
+    def __init__(self, out, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, k_new,
+                 v_new, slot_mapping, scale, max_context_len, partition_size=0, workspace=None):
+        base = DecodeFp8Launch(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
+                               scale, max_context_len, partition_size, workspace)
+        _dev(k_new, v_new, slot_mapping)
+        s, _, d = q.shape
+        hkv = k_cache.shape[2]
+        _need(k_new.shape == (s, hkv, d) and v_new.shape == k_new.shape, "k_new, v_new must be [S, Hkv, D]")
+        _need(k_new.dtype == v_new.dtype == torch.bfloat16, "k_new, v_new must be bf16")
+        _need(slot_mapping.dtype == torch.int32 and slot_mapping.shape == (s,), "slot_mapping must be int32 [S]")
+        a = base._args
+        self._keep = base._keep + (k_new, v_new, slot_mapping)
+        self._fn = "pkv_paged_attention_decode_store_fp8"
+        self._args = a[:8] + (_ptr(k_new), _ptr(v_new), _ptr(slot_mapping)) + a[8:]

@@ -122,7 +122,8 @@ int decode_impl(const char* fn, void* out, const void* q, const void* k_cache, c
                 int32_t max_blocks_per_seq, int32_t max_context_len, int32_t num_blocks,
                 int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                 float scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
-                int dtype, int32_t algo, void* stream) {
+                int dtype, int32_t algo, void* stream, bool fp8 = false,
+                const float* k_scale = nullptr, const float* v_scale = nullptr) {
   if (num_seqs < 0) return fail(PKV_EINVAL, "%s: num_seqs < 0", fn);
   if (int rc = check_common(fn, num_blocks, block_size, num_kv_heads, head_dim, dtype)) return rc;
   if (num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
@@ -143,6 +144,13 @@ int decode_impl(const char* fn, void* out, const void* q, const void* k_cache, c
                 "PKV_PARTITION_BALANCED", fn, partition_size);
   if (!std::isfinite(scale)) return fail(PKV_EINVAL, "%s: scale is not finite", fn);
   if (algo == PKV_DECODE_AUTO) algo = dtype == PKV_BF16 ? PKV_DECODE_MFMA : PKV_DECODE_VALU;
+  if (fp8) {
+    if (dtype != PKV_BF16) return fail(PKV_EUNSUPPORTED, "%s: q and out must be bf16", fn);
+    if (algo != PKV_DECODE_MFMA)
+      return fail(PKV_EUNSUPPORTED, "%s: E4M3 caches are read by the MFMA kernel only", fn);
+    if (balanced)
+      return fail(PKV_EUNSUPPORTED, "%s: no work-balanced decode over E4M3 caches", fn);
+  }
   if (algo == PKV_DECODE_MFMA) {
     if (dtype != PKV_BF16) return fail(PKV_EUNSUPPORTED, "%s: the MFMA kernel needs bf16", fn);
     if (group > 16) return fail(PKV_EUNSUPPORTED, "%s: GQA group %d > 16", fn, group);
@@ -171,6 +179,8 @@ int decode_impl(const char* fn, void* out, const void* q, const void* k_cache, c
       !aligned(block_tables, 4) || !aligned(context_lens, 4))
     return fail(PKV_EINVAL, "%s: q and caches must be 16-byte aligned; out and index arrays 4-byte", fn);
   const bool fused = new_slots != nullptr;
+  if (fp8 && (!k_scale || !v_scale || !aligned(k_scale, 4) || !aligned(v_scale, 4)))
+    return fail(PKV_EINVAL, "%s: k_scale and v_scale must be non-null, 4-byte aligned", fn);
   if (fused && (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(new_slots, 4)))
     return fail(PKV_EINVAL, "%s: k_new and v_new must be non-null and 16-byte aligned", fn);
 
@@ -202,6 +212,8 @@ int decode_impl(const char* fn, void* out, const void* q, const void* k_cache, c
   p.k_new = fused ? k_new : nullptr;
   p.v_new = fused ? v_new : nullptr;
   p.new_slots = fused ? new_slots : nullptr;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
   p.bal_counters = nullptr;
   p.bal_pieces = nullptr;
   p.bal_piece_stride = 0;
@@ -232,8 +244,9 @@ int decode_impl(const char* fn, void* out, const void* q, const void* k_cache, c
     p.ws_l = ws + cells;
     p.ws_o = ws + 2 * cells;
   }
-  hipError_t e = algo == PKV_DECODE_MFMA ? pkv::launch_decode_mfma(p, head_dim, st)
-                                         : pkv::launch_decode_valu(p, head_dim, dtype, st);
+  hipError_t e = fp8 ? pkv::launch_decode_mfma_fp8(p, head_dim, st)
+                 : algo == PKV_DECODE_MFMA ? pkv::launch_decode_mfma(p, head_dim, st)
+                                           : pkv::launch_decode_valu(p, head_dim, dtype, st);
   if (e != hipSuccess) return hip_status(e, fn);
   if (nparts > 1) return hip_status(pkv::launch_splitk_reduce(p, head_dim, dtype, st), fn);
   return PKV_OK;
@@ -274,6 +287,72 @@ extern "C" int pkv_paged_attention_decode_store(void* out, const void* q, void* 
                      slot_mapping, num_seqs, max_blocks_per_seq, max_context_len, num_blocks,
                      block_size, num_q_heads, num_kv_heads, head_dim, scale, partition_size,
                      workspace, workspace_bytes, dtype, algo, stream);
+}
+
+extern "C" int pkv_kv_cache_store_fp8(const void* k, const void* v, void* k_cache, void* v_cache,
+                                      const int32_t* slot_mapping, const float* k_scale,
+                                      const float* v_scale, int32_t num_tokens, int32_t num_blocks,
+                                      int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                                      pkv_dtype src_dtype, void* stream) {
+  const char* fn = "pkv_kv_cache_store_fp8";
+  if (num_tokens < 0) return fail(PKV_EINVAL, "%s: num_tokens < 0", fn);
+  if (int rc = check_common(fn, num_blocks, block_size, num_kv_heads, head_dim, src_dtype)) return rc;
+  if (head_dim % 8 != 0)
+    return fail(PKV_EUNSUPPORTED, "%s: head_dim %d must be a multiple of 8", fn, head_dim);
+  if ((int64_t)num_kv_heads * head_dim > 0x7fffffff)
+    return fail(PKV_EUNSUPPORTED, "%s: token row too long", fn);
+  if (num_tokens == 0) return PKV_OK;
+  if (!k || !v || !k_cache || !v_cache || !slot_mapping || !k_scale || !v_scale)
+    return fail(PKV_EINVAL, "%s: null pointer", fn);
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_cache, 8) || !aligned(v_cache, 8) ||
+      !aligned(slot_mapping, 4) || !aligned(k_scale, 4) || !aligned(v_scale, 4))
+    return fail(PKV_EINVAL, "%s: new rows must be 16-byte aligned, caches 8-byte, slots and scales 4-byte",
+                fn);
+  pkv::StoreFp8Params p;
+  p.k = k;
+  p.v = v;
+  p.k_cache = reinterpret_cast<uint8_t*>(k_cache);
+  p.v_cache = reinterpret_cast<uint8_t*>(v_cache);
+  p.slot_mapping = slot_mapping;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.num_tokens = num_tokens;
+  p.num_slots = (int64_t)num_blocks * block_size;
+  p.row_elems = num_kv_heads * head_dim;
+  p.head_dim = head_dim;
+  p.src_f32 = src_dtype == PKV_F32 ? 1 : 0;
+  return hip_status(pkv::launch_store_fp8(p, (hipStream_t)stream), fn);
+}
+
+extern "C" int pkv_paged_attention_decode_fp8(void* out, const void* q, const void* k_cache,
+                                              const void* v_cache, const float* k_scale,
+                                              const float* v_scale, const int32_t* block_tables,
+                                              const int32_t* context_lens, int32_t num_seqs,
+                                              int32_t max_blocks_per_seq, int32_t max_context_len,
+                                              int32_t num_blocks, int32_t block_size,
+                                              int32_t num_q_heads, int32_t num_kv_heads,
+                                              int32_t head_dim, float scale, int32_t partition_size,
+                                              void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "pkv_paged_attention_decode_fp8";
+  return decode_impl(fn, out, q, k_cache, v_cache, block_tables, context_lens, nullptr, nullptr,
+                     nullptr, num_seqs, max_blocks_per_seq, max_context_len, num_blocks, block_size,
+                     num_q_heads, num_kv_heads, head_dim, scale, partition_size, workspace,
+                     workspace_bytes, PKV_BF16, PKV_DECODE_MFMA, stream, true, k_scale, v_scale);
+}
+
+extern "C" int pkv_paged_attention_decode_store_fp8(
+    void* out, const void* q, void* k_cache, void* v_cache, const float* k_scale, const float* v_scale,
+    const int32_t* block_tables, const int32_t* context_lens, const void* k_new, const void* v_new,
+    const int32_t* slot_mapping, int32_t num_seqs, int32_t max_blocks_per_seq, int32_t max_context_len,
+    int32_t num_blocks, int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    float scale, int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "pkv_paged_attention_decode_store_fp8";
+  if (num_seqs > 0 && (!k_new || !v_new || !slot_mapping))
+    return fail(PKV_EINVAL, "%s: null pointer", fn);
+  return decode_impl(fn, out, q, k_cache, v_cache, block_tables, context_lens, k_new, v_new,
+                     slot_mapping, num_seqs, max_blocks_per_seq, max_context_len, num_blocks, block_size,
+                     num_q_heads, num_kv_heads, head_dim, scale, partition_size, workspace,
+                     workspace_bytes, PKV_BF16, PKV_DECODE_MFMA, stream, true, k_scale, v_scale);
 }
 
 extern "C" int pkv_paged_attention_prefill_chunk(void* out, const void* q, const void* k_cache,

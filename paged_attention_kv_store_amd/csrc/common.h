@@ -28,6 +28,22 @@ struct StoreParams {
   int32_t row_vec16;     // bytes of one token row (kv_heads * head_dim * elt) / 16
 };
 
+// E4M3 store: new rows (bf16 or fp32) quantised with one scale per kv-head.
+struct StoreFp8Params {
+  const void* k;
+  const void* v;
+  uint8_t* k_cache;
+  uint8_t* v_cache;
+  const int32_t* slot_mapping;
+  const float* k_scale;      // [num_kv_heads]
+  const float* v_scale;
+  int32_t num_tokens;
+  int64_t num_slots;
+  int32_t row_elems;         // num_kv_heads * head_dim (a multiple of 8)
+  int32_t head_dim;
+  int32_t src_f32;           // 1: fp32 rows, 0: bf16 rows
+};
+
 struct DecodeParams {
   void* out;
   const void* q;
@@ -54,6 +70,9 @@ struct DecodeParams {
   const void* k_new;
   const void* v_new;
   const int32_t* new_slots;
+  // E4M3 caches only (null otherwise): dequantisation scales [num_kv_heads].
+  const float* k_scale;
+  const float* v_scale;
   // Work-balanced decode only: arrival counters [kBalMaxWaves] (zero between
   // calls) and per-wave pieces [2 * kBalMaxWaves][piece_stride].
   int32_t* bal_counters;
@@ -101,8 +120,10 @@ struct PrefillParams {
 
 // dtype codes match pkv_dtype
 hipError_t launch_store(const StoreParams& p, hipStream_t stream);
+hipError_t launch_store_fp8(const StoreFp8Params& p, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeParams& p, int head_dim, int dtype, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_decode_mfma_fp8(const DecodeParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_decode_balanced(const DecodeParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_splitk_reduce(const DecodeParams& p, int head_dim, int dtype, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t stream);

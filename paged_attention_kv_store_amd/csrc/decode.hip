@@ -45,6 +45,10 @@ constexpr int kTile = 16;
 #endif
 // Tiles in flight per wave in the matrix-core decode (register ring depth).
 constexpr int kStages = PKV_DECODE_STAGES;
+// The same for E4M3 caches, whose tiles are half as many bytes.
+#ifndef PKV_DECODE_STAGES_FP8
+#define PKV_DECODE_STAGES_FP8 2
+#endif
 // Work-balanced decode: resident workgroups per compute unit (= waves per
 // SIMD) and tiles in flight per wave.
 #ifndef PKV_BAL_WG_PER_CU
@@ -397,19 +401,53 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
 // reads its 4 V rows whole (lane n holds columns EPL*n .. EPL*n+EPL-1 of all
 // 4 tokens), so step i of P.V takes column EPL*n+i of the 4 rows with two
 // in-lane byte permutes: no lane exchange, and every V load reads full rows.
+//
+// E4M3 caches (FP8): a lane holds the D/4 contiguous bytes [qg*D/4, +D/4) of
+// its K row, so step c of q.k pairs elements qg*D/4 + 8c .. +7 (q is loaded
+// in the same order), and EPL bytes of each of its 4 V rows. Codes become
+// bf16 at the point of use (exact: every E4M3 value is a bf16 value); the K
+// scale joins the logit multiplier and the V scale the accumulator.
+template <int D, bool FP8>
+struct MfmaTile;
 template <int D>
-struct MfmaTile {
+struct MfmaTile<D, false> {
   static constexpr int KCH = D / 32;   // 16-byte K pieces per lane
   static constexpr int EPL = D / 16;   // V columns per lane
   uint4 k[KCH];
   uint4 v[4];                          // rows 4*qg + 0..3 (EPL bf16 each, rest unused)
 };
+template <int D>
+struct MfmaTile<D, true> {
+  static constexpr int KCH = D / 32;
+  static constexpr int EPL = D / 16;
+  uint4 k[D / 64];                     // D/4 bytes of the K row
+  uint2 v[4];                          // EPL bytes of each V row (D = 64: .x only)
+};
 
-template <int D, int GP>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PKV_DECODE_WAVES_PER_SIMD, PKV_DECODE_WAVES_PER_SIMD)))
+// Two bf16 words holding the exact values of the four E4M3 codes of w.
+__device__ __forceinline__ uint2 e4m3x4_to_bf16(uint32_t w) {
+  const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  return make_uint2(pack_bf16x2(lo.x, lo.y), pack_bf16x2(hi.x, hi.y));
+}
+
+__device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+#ifndef PKV_DECODE_WAVES_PER_SIMD_FP8
+#define PKV_DECODE_WAVES_PER_SIMD_FP8 2
+#endif
+template <bool FP8>
+constexpr int kMfmaWavesPerSimd = FP8 ? PKV_DECODE_WAVES_PER_SIMD_FP8 : PKV_DECODE_WAVES_PER_SIMD;
+
+template <int D, int GP, bool FP8>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kMfmaWavesPerSimd<FP8>, kMfmaWavesPerSimd<FP8>)))
 void decode_mfma_kernel(DecodeParams p) {
-  constexpr int KCH = MfmaTile<D>::KCH;
-  constexpr int EPL = MfmaTile<D>::EPL;   // also the number of 16x16x16 P.V steps
+  using Tile = MfmaTile<D, FP8>;
+  constexpr int kStages = FP8 ? PKV_DECODE_STAGES_FP8 : ::pkv::kStages;
+  constexpr int KCH = Tile::KCH;
+  constexpr int EPL = Tile::EPL;   // also the number of 16x16x16 P.V steps
 
   __shared__ float s_m[kWaves * 16], s_l[kWaves * 16];
   __shared__ float s_o[kWaves * GP * D];
@@ -440,21 +478,25 @@ void decode_mfma_kernel(DecodeParams p) {
   // so the four lanes of a K row read 64 contiguous bytes per load. The K
   // operand uses the same element order, so the contraction pairs matching
   // elements whatever order the hardware sums them in.
+  // (E4M3 caches: elements qg*D/4 + 8c .. +7 instead, see MfmaTile.)
   bf16x8_t qb[KCH];
   {
     const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) +
-                           ((int64_t)s * p.num_q_heads + g * G + n) * D + 8 * qg;
+                           ((int64_t)s * p.num_q_heads + g * G + n) * D + (FP8 ? qg * (D / 4) : 8 * qg);
 #pragma unroll
     for (int j = 0; j < KCH; ++j) {
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (n < G) v = load16(qrow + 32 * j);
+      if (n < G) v = load16(qrow + (FP8 ? 8 : 32) * j);
       qb[j] = bit_cast_to<bf16x8_t>(v);
     }
   }
+  // logit multiplier (with the K scale for E4M3 caches) and V scale
+  const float logit_scale = FP8 ? p.scale_log2 * p.k_scale[g] : p.scale_log2;
 
-  const uint16_t* kc = reinterpret_cast<const uint16_t*>(p.k_cache) + g * D + 8 * qg;
+  constexpr int kElt = FP8 ? 1 : 2;   // bytes per cache element
+  const char* kc = reinterpret_cast<const char*>(p.k_cache) + (g * D + (FP8 ? qg * (D / 4) : 8 * qg)) * kElt;
   // V: lane reads rows 4*qg + st (st = 0..3), columns EPL*n .. EPL*n+EPL-1
-  const uint16_t* vc = reinterpret_cast<const uint16_t*>(p.v_cache) + g * D + EPL * n;
+  const char* vc = reinterpret_cast<const char*>(p.v_cache) + (g * D + EPL * n) * kElt;
   const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks;
 
   float m_ref = neg_inf();   // reference max of head n (replicated over qg)
@@ -466,20 +508,43 @@ void decode_mfma_kernel(DecodeParams p) {
 
   // Fused store: the sequence's new row (position ctx-1) goes to its slot,
   // and the wave that owns the tile holding ctx-1 uses it from registers.
+  // E4M3 caches: the new row is quantised here exactly as the store kernel
+  // does, and its codes stand in for the cache's.
   const NewRow nr = new_row_of(p, s, ctx, t0, t1, w);
-  uint4 nk[KCH], nv = make_uint4(0, 0, 0, 0);
+  uint4 nk[KCH], nv = make_uint4(0, 0, 0, 0);     // bf16 new row pieces
+  uint4 nk8[D / 64];                               // E4M3: codes of elements qg*D/4 ..
+  uint2 nv8 = make_uint2(0u, 0u);                  // E4M3: codes of columns EPL*n ..
 #pragma unroll
   for (int c = 0; c < KCH; ++c) nk[c] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int c = 0; c < D / 64; ++c) nk8[c] = make_uint4(0, 0, 0, 0);
   if (nr.mine) {
     const uint16_t* kn = reinterpret_cast<const uint16_t*>(p.k_new) + ((int64_t)s * p.num_kv_heads + g) * D;
     const uint16_t* vn = reinterpret_cast<const uint16_t*>(p.v_new) + ((int64_t)s * p.num_kv_heads + g) * D;
+    if constexpr (FP8) {
+      const float ks = p.k_scale[g], vs = p.v_scale[g];
 #pragma unroll
-    for (int c = 0; c < KCH; ++c) nk[c] = load16(kn + 8 * qg + 32 * c);
-    if constexpr (EPL == 8) {
-      nv = load16(vn + EPL * n);
+      for (int c = 0; c < D / 64; ++c) {
+        const uint2 a = quantize8_bf16(load16(kn + qg * (D / 4) + 16 * c), ks);
+        const uint2 b = quantize8_bf16(load16(kn + qg * (D / 4) + 16 * c + 8), ks);
+        nk8[c] = make_uint4(a.x, a.y, b.x, b.y);
+      }
+      if constexpr (EPL == 8) {
+        nv8 = quantize8_bf16(load16(vn + EPL * n), vs);
+      } else {
+        const uint2 h = load8(vn + EPL * n);
+        const float x[4] = {bf16_lo(h.x), bf16_hi(h.x), bf16_lo(h.y), bf16_hi(h.y)};
+        nv8 = make_uint2(quantize4(x, vs), 0u);
+      }
     } else {
-      const uint2 h = load8(vn + EPL * n);
-      nv = make_uint4(h.x, h.y, 0, 0);
+#pragma unroll
+      for (int c = 0; c < KCH; ++c) nk[c] = load16(kn + 8 * qg + 32 * c);
+      if constexpr (EPL == 8) {
+        nv = load16(vn + EPL * n);
+      } else {
+        const uint2 h = load8(vn + EPL * n);
+        nv = make_uint4(h.x, h.y, 0, 0);
+      }
     }
   }
 
@@ -490,30 +555,41 @@ void decode_mfma_kernel(DecodeParams p) {
 
   // Issue the loads of the wave's j-th tile, whose physical block is blk (an
   // id outside the pool reads block 0 and poisons the result).
-  auto issue = [&](int j, int blk, MfmaTile<D>& t) {
+  auto issue = [&](int j, int blk, Tile& t) {
     if ((unsigned)blk >= (unsigned)p.num_blocks) {
       blk = 0;
       bad = true;
     }
     const int tok0 = tile_tok0(j);
     const int64_t row0 = (int64_t)blk * bs + (tok0 % bs);
-    const uint16_t* kp = kc + (row0 + n) * row_elems;
-    const uint16_t* vp = vc + (row0 + 4 * qg) * row_elems;
+    const int64_t row_bytes = row_elems * kElt;
+    const char* kp = kc + (row0 + n) * row_bytes;
+    const char* vp = vc + (row0 + 4 * qg) * row_bytes;
+    if constexpr (FP8) {
 #pragma unroll
-    for (int c = 0; c < KCH; ++c) t.k[c] = load16(kp + 32 * c);
+      for (int c = 0; c < D / 64; ++c) t.k[c] = load16(kp + 16 * c);
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      if constexpr (EPL == 8) {
-        t.v[st] = load16(vp + st * row_elems);
-      } else {
-        const uint2 h = load8(vp + st * row_elems);
-        t.v[st] = make_uint4(h.x, h.y, 0, 0);
+      for (int st = 0; st < 4; ++st) {
+        if constexpr (EPL == 8) t.v[st] = load8(vp + st * row_bytes);
+        else t.v[st] = make_uint2(*reinterpret_cast<const uint32_t*>(vp + st * row_bytes), 0u);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < KCH; ++c) t.k[c] = load16(kp + 64 * c);
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        if constexpr (EPL == 8) {
+          t.v[st] = load16(vp + st * row_bytes);
+        } else {
+          const uint2 h = load8(vp + st * row_bytes);
+          t.v[st] = make_uint4(h.x, h.y, 0, 0);
+        }
       }
     }
   };
 
   // Scores, online softmax and P.V of the wave's j-th tile.
-  auto compute = [&](int j, const MfmaTile<D>& t) {
+  auto compute = [&](int j, const Tile& t) {
     const int tok0 = tile_tok0(j);
     // in the tile holding the new row, that row comes from registers
     const bool ov = nr.mine && tok0 <= nr.pos && nr.pos < tok0 + kTile;
@@ -522,15 +598,28 @@ void decode_mfma_kernel(DecodeParams p) {
     f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < KCH; ++c) {
-      uint4 kq = t.k[c];
-      if (ov && n == rn) kq = nk[c];
+      uint4 kq;
+      if constexpr (FP8) {
+        uint32_t w0 = word_of(t.k[(2 * c) / 4], (2 * c) % 4);
+        uint32_t w1 = word_of(t.k[(2 * c + 1) / 4], (2 * c + 1) % 4);
+        if (ov && n == rn) {
+          w0 = word_of(nk8[(2 * c) / 4], (2 * c) % 4);
+          w1 = word_of(nk8[(2 * c + 1) / 4], (2 * c + 1) % 4);
+        }
+        const uint2 lo = e4m3x4_to_bf16(w0);
+        const uint2 hi = e4m3x4_to_bf16(w1);
+        kq = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      } else {
+        kq = t.k[c];
+        if (ov && n == rn) kq = nk[c];
+      }
       sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bit_cast_to<bf16x8_t>(kq), qb[c], sc, 0, 0, 0);
     }
 
     const int tokq = tok0 + 4 * qg;
     float x[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) x[r] = (tokq + r < t1) ? sc[r] * p.scale_log2 : neg_inf();
+    for (int r = 0; r < 4; ++r) x[r] = (tokq + r < t1) ? sc[r] * logit_scale : neg_inf();
     float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     mt = fmaxf(mt, shfl_xor_f(mt, 16));
     mt = fmaxf(mt, shfl_xor_f(mt, 32));
@@ -561,12 +650,23 @@ void decode_mfma_kernel(DecodeParams p) {
     uint32_t vd[4][4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      uint4 v = t.v[st];
-      if (ov && 4 * qg + st == rn) v = nv;
-      vd[st][0] = v.x;
-      vd[st][1] = v.y;
-      vd[st][2] = v.z;
-      vd[st][3] = v.w;
+      if constexpr (FP8) {
+        uint2 c8 = t.v[st];
+        if (ov && 4 * qg + st == rn) c8 = nv8;
+        const uint2 a = e4m3x4_to_bf16(c8.x);
+        const uint2 b = EPL == 8 ? e4m3x4_to_bf16(c8.y) : make_uint2(0u, 0u);
+        vd[st][0] = a.x;
+        vd[st][1] = a.y;
+        vd[st][2] = b.x;
+        vd[st][3] = b.y;
+      } else {
+        uint4 v = t.v[st];
+        if (ov && 4 * qg + st == rn) v = nv;
+        vd[st][0] = v.x;
+        vd[st][1] = v.y;
+        vd[st][2] = v.z;
+        vd[st][3] = v.w;
+      }
     }
     if (tok0 + kTile > t1) {
 #pragma unroll
@@ -591,7 +691,7 @@ void decode_mfma_kernel(DecodeParams p) {
     // kStages register buffers in a ring; the loop is unrolled by the ring
     // size so every buffer index is a compile-time constant and no register
     // copy (which would wait on its pending load) is needed.
-    MfmaTile<D> buf[kStages];
+    Tile buf[kStages];
     int blk_ahead = block_of(0);
 #pragma unroll
     for (int i = 0; i < kStages - 1; ++i) {
@@ -612,7 +712,23 @@ void decode_mfma_kernel(DecodeParams p) {
 
   // The new row goes to its cache slot after the loop, so that no store is
   // in flight while the loop's loads are being waited for.
-  if (nr.mine) {
+  if (FP8 && nr.mine) {
+    uint8_t* kd = const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(p.k_cache)) +
+                  (int64_t)nr.slot * row_elems + g * D;
+    uint8_t* vd = const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(p.v_cache)) +
+                  (int64_t)nr.slot * row_elems + g * D;
+    if (n == 0) {   // lanes n == 0 (qg = 0..3) hold the codes of the whole K row
+#pragma unroll
+      for (int c = 0; c < D / 64; ++c) *reinterpret_cast<uint4*>(kd + qg * (D / 4) + 16 * c) = nk8[c];
+    }
+    if (qg == 0) {  // lanes qg == 0 (n = 0..15) hold the codes of all V columns
+      if constexpr (EPL == 8) {
+        *reinterpret_cast<uint2*>(vd + EPL * n) = nv8;
+      } else {
+        *reinterpret_cast<uint32_t*>(vd + EPL * n) = nv8.x;
+      }
+    }
+  } else if (nr.mine) {
     uint16_t* kd = const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(p.k_cache)) +
                    (int64_t)nr.slot * row_elems + g * D;
     uint16_t* vd = const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(p.v_cache)) +
@@ -636,12 +752,13 @@ void decode_mfma_kernel(DecodeParams p) {
     s_m[w * 16 + lane] = m_ref;
     s_l[w * 16 + lane] = l_part;
   }
+  const float v_scale = FP8 ? p.v_scale[g] : 1.f;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int h = 4 * qg + r;
     if (h < G) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) s_o[(w * GP + h) * D + EPL * n + e] = acc[e][r];
+      for (int e = 0; e < EPL; ++e) s_o[(w * GP + h) * D + EPL * n + e] = acc[e][r] * v_scale;
     }
   }
   const bool poisoned = __any(bad);
@@ -1175,20 +1292,24 @@ hipError_t launch_decode_valu(const DecodeParams& p, int head_dim, int dtype, hi
   return head_dim == 64 ? launch_valu_g<uint16_t, 64>(p, stream) : launch_valu_g<uint16_t, 128>(p, stream);
 }
 
-template <int D>
+template <int D, bool FP8>
 static hipError_t launch_mfma_d(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid = decode_grid(p);
   if (p.group <= 4)
-    hipLaunchKernelGGL((decode_mfma_kernel<D, 4>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((decode_mfma_kernel<D, 4, FP8>), grid, dim3(kThreads), 0, stream, p);
   else if (p.group <= 8)
-    hipLaunchKernelGGL((decode_mfma_kernel<D, 8>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((decode_mfma_kernel<D, 8, FP8>), grid, dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((decode_mfma_kernel<D, 16>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((decode_mfma_kernel<D, 16, FP8>), grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
 hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, hipStream_t stream) {
-  return head_dim == 64 ? launch_mfma_d<64>(p, stream) : launch_mfma_d<128>(p, stream);
+  return head_dim == 64 ? launch_mfma_d<64, false>(p, stream) : launch_mfma_d<128, false>(p, stream);
+}
+
+hipError_t launch_decode_mfma_fp8(const DecodeParams& p, int head_dim, hipStream_t stream) {
+  return head_dim == 64 ? launch_mfma_d<64, true>(p, stream) : launch_mfma_d<128, true>(p, stream);
 }
 
 // Compute units of the current device (queried once per device).

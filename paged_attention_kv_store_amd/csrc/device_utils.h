@@ -48,4 +48,34 @@ __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 __device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ uint2 load8(const void* p) { return *reinterpret_cast<const uint2*>(p); }
 
+// ---- E4M3 quantisation (the cache format's reading) ------------------------
+// t = x / scale as one IEEE float32 division, clamped to +-448 (a NaN passes
+// through), rounded to the nearest E4M3 code with ties to even by the
+// hardware conversion; a NaN becomes the canonical code 0x7f (the conversion
+// would set the sign bit). Used by the store and by the store fused into
+// decode, so both write the same bytes.
+__device__ __forceinline__ float clamp_e4m3(float t) {
+  return t > 448.f ? 448.f : (t < -448.f ? -448.f : t);
+}
+
+// codes of x[0..3] / s, packed little-endian
+__device__ __forceinline__ uint32_t quantize4(const float* x, float s) {
+  float t[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) t[i] = clamp_e4m3(x[i] / s);
+  uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
+  w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], (int)w, true);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (t[i] != t[i]) w = (w & ~(0xffu << (8 * i))) | (0x7fu << (8 * i));
+  return w;
+}
+
+// codes of the 8 bf16 values in v, divided by s
+__device__ __forceinline__ uint2 quantize8_bf16(const uint4& v, float s) {
+  const float x[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                      bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+  return make_uint2(quantize4(x, s), quantize4(x + 4, s));
+}
+
 }  // namespace pkv

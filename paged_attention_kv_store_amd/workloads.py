@@ -26,6 +26,11 @@ workloads:
                 drafted tokens) after U{256..4096} cached tokens; 32 q / 8 kv
                 heads, D 128, bf16; the 512 new rows stored first
 
+E4M3 variants (qwen3_decode_fp8, random_decode_batch_fp8) keep the shapes and
+draw the caches as codes: N(0,1) values divided by per-kv-head scales drawn
+U(0.008, 0.016), kept inside +-448 and cast by torch's float8_e4m3fn; dead
+rows hold the NaN code 0x7f. q and the new rows stay bf16.
+
 Recipe: the metadata comes from numpy PCG64 streams spawned from
 SeedSequence(seed); values come from a torch generator (on the target device)
 seeded from the same SeedSequence, drawn in fp32 and rounded to nearest-even
@@ -49,11 +54,12 @@ BLOCK_SIZE = 16
 
 
 def host_bits(t: torch.Tensor) -> np.ndarray:
-    """Raw storage of a CPU tensor as numpy: float32 as is, bf16 as uint16 bits."""
+    """Raw storage of a tensor as host numpy: float32 and integer types as they
+    are (uint8 for E4M3 codes), bf16 as uint16 bits."""
     t = t.detach().to("cpu").contiguous()
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16)
-    if t.dtype in (torch.float32, torch.float64, torch.int32, torch.int64):
+    if t.dtype in (torch.float32, torch.float64, torch.int32, torch.int64, torch.uint8):
         return t.numpy()
     raise TypeError(f"unsupported dtype {t.dtype}")
 
@@ -85,6 +91,9 @@ class PagedBatch:
     slot_mapping: Optional[torch.Tensor] = None   # int32 [T]
     # prefill chunks only
     cu_seqlens_q: Optional[np.ndarray] = None      # int32 [S+1]
+    # E4M3 caches only: the caches hold uint8 codes; one scale per kv-head
+    k_scale: Optional[torch.Tensor] = None          # float32 [Hkv]
+    v_scale: Optional[torch.Tensor] = None
 
     @property
     def num_seqs(self) -> int:
@@ -207,6 +216,51 @@ def _poisoned_cache(num_blocks, block_size, num_kv_heads, head_dim, dtype, gen,
         idx = torch.as_tensor(dead_rows, dtype=torch.long, device=device)
         flat.index_fill_(0, idx, float("nan"))
     return cache
+
+
+E4M3_NAN = 0x7F
+
+
+def _e4m3_cache(num_blocks, block_size, num_kv_heads, head_dim, scale, gen, device, dead_rows):
+    """Cache of E4M3 codes standing for N(0,1) values at the given per-head
+    scales: the draws divided by the scale, kept inside the format's +-448 and
+    cast by torch's float8_e4m3fn; dead rows hold the NaN code."""
+    x = torch.randn((num_blocks, block_size, num_kv_heads, head_dim), generator=gen, device=device,
+                    dtype=torch.float32)
+    x = (x / scale.view(1, 1, -1, 1)).clamp_(-448.0, 448.0)
+    codes = x.to(torch.float8_e4m3fn).view(torch.uint8)
+    if len(dead_rows):
+        flat = codes.view(num_blocks * block_size, num_kv_heads * head_dim)
+        flat[torch.as_tensor(dead_rows, dtype=torch.long, device=device)] = E4M3_NAN
+    return codes
+
+
+def build_batch_fp8(pool: Pool, num_q_heads, num_kv_heads, head_dim, seed, salt, device,
+                    num_queries=None, store_slots=None, block_size=BLOCK_SIZE,
+                    scale=None) -> PagedBatch:
+    """Like build_batch with E4M3 caches: q and the new rows are bf16, the
+    caches uint8 codes, k_scale / v_scale drawn U(0.008, 0.016) per kv-head
+    (about max|x| / 448 for N(0,1) rows)."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(_torch_seed(seed, salt))
+    n_q = pool.context_lens.shape[0] if num_queries is None else num_queries
+    store_slots = None if store_slots is None else np.asarray(store_slots, np.int32)
+    live_store = () if store_slots is None else store_slots[store_slots >= 0]
+    dead = _dead_rows(pool, block_size, live_store)
+    q = _normal((n_q, num_q_heads, head_dim), torch.bfloat16, gen, device)
+    k_scale = torch.empty(num_kv_heads, device=device).uniform_(0.008, 0.016, generator=gen)
+    v_scale = torch.empty(num_kv_heads, device=device).uniform_(0.008, 0.016, generator=gen)
+    kc = _e4m3_cache(pool.num_blocks, block_size, num_kv_heads, head_dim, k_scale, gen, device, dead)
+    vc = _e4m3_cache(pool.num_blocks, block_size, num_kv_heads, head_dim, v_scale, gen, device, dead)
+    batch = PagedBatch(pool=pool, q=q, k_cache=kc, v_cache=vc,
+                       scale=(1.0 / math.sqrt(head_dim)) if scale is None else scale,
+                       block_size=block_size, k_scale=k_scale, v_scale=v_scale)
+    if store_slots is not None:
+        t = len(store_slots)
+        batch.k_new = _normal((t, num_kv_heads, head_dim), torch.bfloat16, gen, device)
+        batch.v_new = _normal((t, num_kv_heads, head_dim), torch.bfloat16, gen, device)
+        batch.slot_mapping = torch.as_tensor(store_slots, dtype=torch.int32, device=device)
+    return batch
 
 
 def build_batch(pool: Pool, num_q_heads, num_kv_heads, head_dim, dtype, seed,
@@ -377,6 +431,32 @@ def random_decode_batch(seed, num_seqs, num_q_heads, num_kv_heads, head_dim,
     slots = decode_store_slots(pool, block_size) if store else None
     return build_batch(pool, num_q_heads, num_kv_heads, head_dim, dtype, seed, 7,
                        device, store_slots=slots, block_size=block_size, scale=scale)
+
+
+def random_decode_batch_fp8(seed, num_seqs, num_q_heads, num_kv_heads, head_dim, max_ctx,
+                            min_ctx=0, block_size=BLOCK_SIZE, device="cpu", store=True,
+                            scale=None) -> PagedBatch:
+    """random_decode_batch with E4M3 caches (bf16 q and new rows)."""
+    (rng,) = _streams(seed, 1)
+    ctx = rng.integers(min_ctx, max_ctx, size=num_seqs, endpoint=True).astype(np.int32)
+    pool = make_pool(rng, ctx, block_size=block_size,
+                     max_blocks=max(1, -(-int(max(max_ctx, ctx.max())) // block_size)), reserve=2)
+    slots = decode_store_slots(pool, block_size) if store else None
+    return build_batch_fp8(pool, num_q_heads, num_kv_heads, head_dim, seed, 8, device,
+                           store_slots=slots, block_size=block_size, scale=scale)
+
+
+def qwen3_decode_fp8(seed: int = 1, device="cpu", layers: int = 28) -> Workload:
+    """The Qwen3-shaped decode step over E4M3 caches: the same lengths,
+    tables and new-row slots as qwen3_decode (same seed), bf16 q."""
+    (rng,) = _streams(seed, 1)
+    ctx = rng.integers(64, 1024, size=60, endpoint=True).astype(np.int32)
+    pool = make_pool(rng, ctx)
+    slots = decode_store_slots(pool)
+    batches = [build_batch_fp8(pool, 16, 8, 128, seed, 101 + layer, device, store_slots=slots)
+               for layer in range(layers)]
+    return Workload("qwen3_decode_fp8", batches,
+                    notes=f"{layers} layers, E4M3 caches with per-kv-head scales")
 
 
 def random_prefill_batch(seed, num_chunks, num_q_heads, num_kv_heads, head_dim,
