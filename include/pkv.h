@@ -104,11 +104,14 @@ int pkv_kv_cache_store(const void* k, const void* v, void* k_cache, void* v_cach
  * Bytes of workspace needed by pkv_paged_attention_decode for the same
  * num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len and
  * partition_size (0 for invalid sizes).
- *  - partition_size > 0 (split-K): fp32 running max, sum and unnormalised
- *    output for every (sequence, q-head, partition); 0 when one partition
- *    covers max_context_len. Layout: m [num_seqs, num_q_heads, P],
+ *  - partition_size > 0 (split-K): 65536 int32 arrival counters (256 KiB,
+ *    at the start whatever the sizes; counter s * num_kv_heads + g), then
+ *    fp32 running max, sum and unnormalised output for every (sequence,
+ *    q-head, partition); 0 when one partition covers max_context_len.
+ *    Layout after the counters: m [num_seqs, num_q_heads, P],
  *    l [num_seqs, num_q_heads, P], o [num_seqs, num_q_heads, P, head_dim],
- *    P = ceil(max_context_len / partition_size).
+ *    P = ceil(max_context_len / partition_size). Split-K takes at most
+ *    65536 (sequence, kv-head) pairs.
  *  - PKV_PARTITION_BALANCED: 4096 int32 arrival counters (16 KiB, at the
  *    start whatever the sizes), then fp32 pieces of the partial results, two
  *    per wave of the largest grid (4096 waves).
@@ -128,9 +131,13 @@ size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *   partition_size: 0 runs one pass per (sequence, kv-head). Otherwise a
  *     positive multiple of 16: each (sequence, kv-head) is split into
  *     partitions of that many tokens whose partial results (running max,
- *     sum, unnormalised output) go to `workspace`, and a second launch merges
- *     them (log-sum-exp). Sequences that fit in one partition are written
- *     directly.
+ *     sum, unnormalised output) go to `workspace`; the partition that
+ *     finishes last, found with the workspace's arrival counters, merges
+ *     them (log-sum-exp) in the same launch. The counters must be zero
+ *     before the first call (e.g. a zero-filled workspace); every call leaves
+ *     them zero, so one workspace serves calls of any sizes in turn, but
+ *     calls that run at the same time must not share it. Sequences that fit
+ *     in one partition are written directly.
  *     PKV_PARTITION_BALANCED (MFMA kernel, bf16, at most 8192 sequences,
  *     fewer than 2^30 16-token tiles): one launch whose grid fills the GPU
  *     once; every wave takes an equal share of all (kv-head, sequence,

@@ -109,7 +109,10 @@ extern "C" size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_head
   int64_t nparts;
   partitioning(max_context_len, partition_size, &part, &nparts);
   if (nparts <= 1) return 0;
-  return (size_t)num_seqs * num_q_heads * nparts * (head_dim + 2) * sizeof(float);
+  // a fixed block of arrival counters (one per (sequence, kv-head)), then m,
+  // l, o of every (sequence, q-head, partition)
+  return (size_t)pkv::kSplitMaxItems * sizeof(int32_t) +
+         (size_t)num_seqs * num_q_heads * nparts * (head_dim + 2) * sizeof(float);
 }
 
 namespace {
@@ -170,6 +173,14 @@ int decode_impl(const char* fn, void* out, const void* q, const void* k_cache, c
     if ((int64_t)num_seqs * num_kv_heads * ceil_div(max_context_len, 16) >= ((int64_t)1 << 30))
       return fail(PKV_EUNSUPPORTED, "%s: more than 2^30 tiles for the work-balanced decode", fn);
   }
+  {
+    int32_t part_probe;
+    int64_t nparts_probe;
+    partitioning(max_context_len, balanced ? 0 : partition_size, &part_probe, &nparts_probe);
+    if (nparts_probe > 1 && (int64_t)num_seqs * num_kv_heads > pkv::kSplitMaxItems)
+      return fail(PKV_EUNSUPPORTED, "%s: split-K takes at most %d (sequence, kv-head) pairs", fn,
+                  pkv::kSplitMaxItems);
+  }
   if (num_seqs == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
     return fail(PKV_EINVAL, "%s: null pointer", fn);
@@ -209,6 +220,7 @@ int decode_impl(const char* fn, void* out, const void* q, const void* k_cache, c
   p.partition_size = part;
   p.num_partitions = (int32_t)nparts;
   p.ws_m = p.ws_l = p.ws_o = nullptr;
+  p.part_counters = nullptr;
   p.k_new = fused ? k_new : nullptr;
   p.v_new = fused ? v_new : nullptr;
   p.new_slots = fused ? new_slots : nullptr;
@@ -239,7 +251,8 @@ int decode_impl(const char* fn, void* out, const void* q, const void* k_cache, c
                   workspace ? workspace_bytes : (size_t)0);
     if (!aligned(workspace, 16)) return fail(PKV_EINVAL, "%s: workspace must be 16-byte aligned", fn);
     const int64_t cells = (int64_t)num_seqs * num_q_heads * nparts;
-    float* ws = reinterpret_cast<float*>(workspace);
+    p.part_counters = reinterpret_cast<int32_t*>(workspace);
+    float* ws = reinterpret_cast<float*>(p.part_counters + pkv::kSplitMaxItems);
     p.ws_m = ws;
     p.ws_l = ws + cells;
     p.ws_o = ws + 2 * cells;
@@ -248,7 +261,6 @@ int decode_impl(const char* fn, void* out, const void* q, const void* k_cache, c
                  : algo == PKV_DECODE_MFMA ? pkv::launch_decode_mfma(p, head_dim, st)
                                            : pkv::launch_decode_valu(p, head_dim, dtype, st);
   if (e != hipSuccess) return hip_status(e, fn);
-  if (nparts > 1) return hip_status(pkv::launch_splitk_reduce(p, head_dim, dtype, st), fn);
   return PKV_OK;
 }
 

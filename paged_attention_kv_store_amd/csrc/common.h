@@ -65,6 +65,7 @@ struct DecodeParams {
   float* ws_m;               // [num_seqs, num_q_heads, num_partitions]
   float* ws_l;               // same
   float* ws_o;               // [num_seqs, num_q_heads, num_partitions, head_dim]
+  int32_t* part_counters;    // [num_seqs * num_kv_heads] arrival counters, zero between calls
   // Fused store of one new row per sequence at position ctx-1 (all null when
   // not fused): k_new/v_new [num_seqs, num_kv_heads, head_dim], new_slots [num_seqs].
   const void* k_new;
@@ -79,6 +80,11 @@ struct DecodeParams {
   float* bal_pieces;
   int32_t bal_piece_stride;  // floats per piece
 };
+
+// Split-K: the workspace starts with this many arrival counters (one per
+// (sequence, kv-head)), at a fixed place so that calls of any sizes can share
+// a workspace; the partial results follow.
+constexpr int kSplitMaxItems = 65536;
 
 // Work-balanced decode limits. Every workgroup keeps the per-sequence tile
 // prefix sums in LDS, which bounds the batch; the piece area is sized for
@@ -125,7 +131,6 @@ hipError_t launch_decode_valu(const DecodeParams& p, int head_dim, int dtype, hi
 hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_decode_mfma_fp8(const DecodeParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_decode_balanced(const DecodeParams& p, int head_dim, hipStream_t stream);
-hipError_t launch_splitk_reduce(const DecodeParams& p, int head_dim, int dtype, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t stream);
 
 }  // namespace pkv

@@ -12,7 +12,8 @@
 // output accumulator); the four states are merged through LDS at the end.
 // A partition that is the sequence's only one writes the normalised output;
 // otherwise it writes (max, sum, unnormalised output) to the split-K
-// workspace and splitk_reduce_kernel merges the partitions.
+// workspace and the last partition of the sequence to finish merges them
+// (merge_and_write), in the same launch.
 //
 // Two kernel families compute the same thing:
 //  * decode_valu_kernel: lanes split a cache row into 16-byte pieces; q.k dot
@@ -82,8 +83,23 @@ __device__ void write_zero_rows(const DecodeParams& p, int s, int g) {
   }
 }
 
-// Merge the per-wave softmax states held in LDS and write either the final
-// output (single partition) or this partition's split-K partials.
+// Relaxed agent-scope atomic accesses of partial results: written through
+// to, and read from, the point where all XCDs see the same memory (each XCD
+// has its own L2), without a whole-cache write-back or invalidation.
+__device__ __forceinline__ void coherent_store(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float coherent_load(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Merge the per-wave softmax states held in LDS and write the output of a
+// sequence's only partition. With several partitions, write this partition's
+// (max, sum, unnormalised output) with agent-coherent stores, wait for them
+// to complete, and count the partition's arrival on the (sequence, kv-head)
+// counter; the workgroup that arrives last merges all partitions
+// (log-sum-exp: out = sum_k 2^(m_k - M) o_k / sum_k 2^(m_k - M) l_k) and
+// resets the counter. No workgroup waits for another.
 //   s_m[w*16 + h], s_l[w*16 + h]: wave w's reference max (log2) and sum
 //   s_o[(w*GP + h)*D + d]: wave w's unnormalised output
 template <typename T, int D, int GP>
@@ -91,6 +107,7 @@ __device__ void merge_and_write(const DecodeParams& p, int s, int g, int part, i
                                 const float* s_m, const float* s_l, const float* s_o,
                                 bool poisoned) {
   const int G = p.group;
+  const int64_t head0 = (int64_t)s * p.num_q_heads + g * G;   // first q-head of the group
   for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
     const int h = idx / D, d = idx - h * D;
     float M = neg_inf();
@@ -105,18 +122,61 @@ __device__ void merge_and_write(const DecodeParams& p, int s, int g, int part, i
       O += s_o[(w * GP + h) * D + d] * f;
     }
     if (poisoned) L = __builtin_nanf("");
-    const int qh = g * G + h;
     if (n_parts <= 1) {
-      store_out<T>(p.out, ((int64_t)s * p.num_q_heads + qh) * D + d, O / L);
+      store_out<T>(p.out, (head0 + h) * D + d, O / L);
     } else {
-      const int64_t base = ((int64_t)s * p.num_q_heads + qh) * p.num_partitions + part;
-      p.ws_o[base * D + d] = O;
+      const int64_t base = (head0 + h) * p.num_partitions + part;
+      coherent_store(p.ws_o + base * D + d, O);
       if (d == 0) {
-        p.ws_m[base] = M;
-        p.ws_l[base] = L;
+        coherent_store(p.ws_m + base, M);
+        coherent_store(p.ws_l + base, L);
       }
     }
   }
+  if (n_parts <= 1) return;
+
+  __shared__ int s_last;
+  // every thread's partial stores have completed before the arrival counts
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  int* counter = p.part_counters + (int64_t)s * p.num_kv_heads + g;
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n_parts - 1;
+  __syncthreads();
+  if (!s_last) return;
+  asm volatile("" ::: "memory");
+  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+    const int h = idx / D, d = idx - h * D;
+    const int64_t base = (head0 + h) * p.num_partitions;
+    float M = neg_inf(), L = 0.f, O = 0.f;
+    // eight partitions' loads in flight at a time, then their online merge
+    constexpr int kBatch = 8;
+    for (int k0 = 0; k0 < n_parts; k0 += kBatch) {
+      float mv[kBatch], lv[kBatch], ov[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int64_t k = base + min(k0 + u, n_parts - 1);
+        mv[u] = coherent_load(p.ws_m + k);
+        lv[u] = coherent_load(p.ws_l + k);
+        ov[u] = coherent_load(p.ws_o + k * D + d);
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (k0 + u >= n_parts) break;
+        if (mv[u] > M) {
+          const float f = (M == neg_inf()) ? 0.f : fast_exp2(M - mv[u]);
+          L *= f;
+          O *= f;
+          M = mv[u];
+        }
+        const float f = (mv[u] == neg_inf()) ? 0.f : fast_exp2(mv[u] - M);
+        L += f * lv[u];
+        O += f * ov[u];
+      }
+    }
+    store_out<T>(p.out, (head0 + h) * D + d, O / L);
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Context length as read from device memory, kept inside [0, max_ctx]: the
@@ -770,69 +830,6 @@ void decode_mfma_kernel(DecodeParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Split-K merge: out = sum_k 2^(m_k - M) o_k / sum_k 2^(m_k - M) l_k
-// One workgroup of D threads per (q-head, sequence). The partition weights
-// 2^(m_k - M) are computed once per chunk of D partitions into LDS; thread d
-// then sums column d of the partials with independent, unrolled loads.
-// ---------------------------------------------------------------------------
-template <int D>
-__device__ __forceinline__ float block_reduce(float v, bool is_max, float* scratch) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    const float o = shfl_xor_f(v, m);
-    v = is_max ? fmaxf(v, o) : v + o;
-  }
-  if constexpr (D > 64) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    if (lane == 0) scratch[w] = v;
-    __syncthreads();
-    v = scratch[0];
-#pragma unroll
-    for (int i = 1; i < D / 64; ++i) v = is_max ? fmaxf(v, scratch[i]) : v + scratch[i];
-    __syncthreads();
-  }
-  return v;
-}
-
-template <typename T, int D>
-__global__ __launch_bounds__(D) void splitk_reduce_kernel(DecodeParams p) {
-  __shared__ float s_f[D];
-  __shared__ float s_red[D / 64 > 0 ? D / 64 : 1];
-  const int h = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
-  const int ctx = clamp_ctx(p.context_lens[s], p.max_ctx);
-  const int P = p.partition_size;
-  const int n = (ctx + P - 1) / P;
-  if (n <= 1) return;   // written directly by the partition pass
-  const int64_t base = ((int64_t)s * p.num_q_heads + h) * p.num_partitions;
-  const float* wm = p.ws_m + base;
-  const float* wl = p.ws_l + base;
-  const float* wo = p.ws_o + base * D;
-  float M = neg_inf();
-  for (int k = d; k < n; k += D) M = fmaxf(M, wm[k]);
-  M = block_reduce<D>(M, true, s_red);
-  float L = 0.f, O = 0.f;
-  for (int kb = 0; kb < n; kb += D) {
-    const int k = kb + d;
-    const float f = k < n ? fast_exp2(wm[k] - M) : 0.f;
-    if (k < n) L += f * wl[k];
-    s_f[d] = f;
-    __syncthreads();
-    const int lim = min(D, n - kb);
-    const float* col = wo + (int64_t)kb * D + d;
-    int kk = 0;
-    for (; kk + 4 <= lim; kk += 4) {
-      const float o0 = col[(kk + 0) * D], o1 = col[(kk + 1) * D];
-      const float o2 = col[(kk + 2) * D], o3 = col[(kk + 3) * D];
-      O += s_f[kk] * o0 + s_f[kk + 1] * o1 + s_f[kk + 2] * o2 + s_f[kk + 3] * o3;
-    }
-    for (; kk < lim; ++kk) O += s_f[kk] * col[kk * D];
-    __syncthreads();
-  }
-  L = block_reduce<D>(L, false, s_red);
-  store_out<T>(p.out, ((int64_t)s * p.num_q_heads + h) * D + d, O / L);
-}
-
-// ---------------------------------------------------------------------------
 // Work-balanced matrix-core decode (bf16)
 // ---------------------------------------------------------------------------
 // The batch's 16-token tiles form one list, kv-head slowest, then sequence,
@@ -858,16 +855,6 @@ constexpr int kInfoRows = 31;           // tile descriptor: live rows (1..16)
 constexpr int kInfoLast = 1 << 5;       //   last tile of its item
 constexpr int kInfoNewRow = 1 << 6;     //   its last row comes from the new K/V rows
 constexpr int kInfoBad = 1 << 7;        //   block id outside the pool
-
-// Relaxed agent-scope atomic accesses of the pieces: written through to, and
-// read from, the point where all XCDs see the same memory (each XCD has its
-// own L2), without a whole-cache write-back or invalidation.
-__device__ __forceinline__ void coherent_store(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float coherent_load(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 template <int D>
 struct BalSlot {
@@ -1340,22 +1327,6 @@ hipError_t launch_decode_balanced(const DecodeParams& p, int head_dim, hipStream
     hipLaunchKernelGGL(decode_balanced_kernel<64>, grid, dim3(kBalThreads), 0, stream, p);
   else
     hipLaunchKernelGGL(decode_balanced_kernel<128>, grid, dim3(kBalThreads), 0, stream, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_splitk_reduce(const DecodeParams& p, int head_dim, int dtype, hipStream_t stream) {
-  const dim3 grid(p.num_q_heads, p.num_seqs);
-  if (dtype == 0) {
-    if (head_dim == 64)
-      hipLaunchKernelGGL((splitk_reduce_kernel<float, 64>), grid, dim3(64), 0, stream, p);
-    else
-      hipLaunchKernelGGL((splitk_reduce_kernel<float, 128>), grid, dim3(128), 0, stream, p);
-  } else {
-    if (head_dim == 64)
-      hipLaunchKernelGGL((splitk_reduce_kernel<uint16_t, 64>), grid, dim3(64), 0, stream, p);
-    else
-      hipLaunchKernelGGL((splitk_reduce_kernel<uint16_t, 128>), grid, dim3(128), 0, stream, p);
-  }
   return hipGetLastError();
 }
 

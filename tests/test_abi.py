@@ -71,6 +71,7 @@ def _decode(lib, **over):
     (dict(q=1028), binding.PKV_EINVAL),
     (dict(scale=float("nan")), binding.PKV_EINVAL),
     (dict(S=70000), binding.PKV_EUNSUPPORTED),
+    (dict(S=9000, Hq=64, Hkv=8, part=16, max_ctx=256, MB=16), binding.PKV_EUNSUPPORTED),   # 72000 pairs
     (dict(part=-1), binding.PKV_EUNSUPPORTED),                       # balanced needs bf16
     (dict(part=-1, dtype=1, algo=1), binding.PKV_EUNSUPPORTED),      # ... and the MFMA kernel
     (dict(part=-1, dtype=1, S=9000), binding.PKV_EUNSUPPORTED),      # at most 8192 sequences
@@ -94,9 +95,10 @@ def test_decode_empty_batch_is_a_no_op():
 def test_workspace_size():
     lib = pkv.lib()
     # 32 seqs x 32 heads x ceil(32768/512)=64 partitions x (128 + 2) floats
-    assert pkv.decode_workspace_size(32, 32, 8, 128, 32768, 512) == 32 * 32 * 64 * 130 * 4
+    # 65536 counters first, then partials (m, l, o) per (seq, q-head, partition)
+    assert pkv.decode_workspace_size(32, 32, 8, 128, 32768, 512) == 65536 * 4 + 32 * 32 * 64 * 130 * 4
     assert pkv.decode_workspace_size(32, 32, 8, 128, 512, 512) == 0      # one partition
-    assert pkv.decode_workspace_size(32, 32, 8, 128, 513, 512) == 32 * 32 * 2 * 130 * 4
+    assert pkv.decode_workspace_size(32, 32, 8, 128, 513, 512) == 65536 * 4 + 32 * 32 * 2 * 130 * 4
     assert lib.pkv_decode_workspace_size(4, 8, 4, 64, 100, 0) == 0
     assert lib.pkv_decode_workspace_size(4, 8, 3, 64, 100, 0) == 0       # Hq not a multiple of Hkv
     # work-balanced: 4096 int32 counters, then 2 pieces per wave of the largest

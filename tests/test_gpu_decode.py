@@ -243,3 +243,55 @@ def test_decode_store_fused_tiny_and_qwen3_layer():
         assert W.host_bits(dev["k_cache"]).tobytes() == kc.tobytes()
         assert_close(out.float().cpu().double().numpy(), oracle_decode(b, caches=(kc, vc)),
                      b.q.dtype, "fused workload")
+
+
+def test_split_k_counters_reset_across_calls_and_shapes():
+    """The partitions' arrival counters come back to zero: one workspace
+    serves repeated split-K calls of different shapes bit-identically."""
+    b1 = W.random_decode_batch(91, 20, 32, 8, 128, torch.bfloat16, max_ctx=2000, min_ctx=0, store=False)
+    b2 = W.random_decode_batch(92, 33, 32, 8, 128, torch.bfloat16, max_ctx=700, min_ctx=0, store=False)
+    need = max(pkv.decode_workspace_size(b.num_seqs, 32, 8, 128, 2000, 64) for b in (b1, b2))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    d1, d2 = to_device(b1), to_device(b2)
+
+    def run(b, dev, part):
+        out = torch.empty_like(dev["q"])
+        pkv.paged_attention_decode(out, dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
+                                   dev["context_lens"], b.scale, b.max_ctx, partition_size=part,
+                                   workspace=ws)
+        torch.cuda.synchronize()
+        return out.float().cpu().double().numpy()
+
+    first = run(b1, d1, 64)
+    assert_close(first, oracle_decode(b1, store=False), torch.bfloat16, "first")
+    assert_close(run(b2, d2, 128), oracle_decode(b2, store=False), torch.bfloat16, "second shape")
+    for _ in range(3):
+        np.testing.assert_array_equal(run(b1, d1, 64), first)
+    assert int(ws[:65536 * 4].view(torch.int32).abs().sum()) == 0
+
+
+def test_split_k_graph_replays_match_eager():
+    b = W.random_decode_batch(93, 40, 16, 8, 128, torch.bfloat16, max_ctx=1024, min_ctx=64, store=False)
+    dev = to_device(b)
+    out = torch.empty_like(dev["q"])
+    call = pkv.DecodeLaunch(out, dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
+                            dev["context_lens"], b.scale, b.max_ctx, partition_size=256)
+    call()
+    torch.cuda.synchronize()
+    want = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for _ in range(4):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), want.view(torch.int16))
+    assert_close(want.float().cpu().double().numpy(), oracle_decode(b, store=False), torch.bfloat16, "graph")
