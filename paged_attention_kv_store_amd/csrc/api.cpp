@@ -391,6 +391,8 @@ extern "C" int pkv_paged_attention_prefill_chunk(void* out, const void* q, const
     return fail(PKV_EUNSUPPORTED, "%s: GQA group %d not in {1, 2, 4, 8}", fn, group);
   if (block_size < 16 || block_size > 256 || (block_size & (block_size - 1)) != 0)
     return fail(PKV_EUNSUPPORTED, "%s: block_size %d must be a power of two in [16, 256]", fn, block_size);
+  if ((int64_t)block_size * num_kv_heads * head_dim * 2 >= ((int64_t)1 << 31))
+    return fail(PKV_EUNSUPPORTED, "%s: a cache block must be under 2 GiB", fn);
   if (max_blocks_per_seq <= 0) return fail(PKV_EINVAL, "%s: max_blocks_per_seq must be positive", fn);
   if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
     return fail(PKV_EINVAL, "%s: max_context_len outside [0, max_blocks_per_seq * block_size]", fn);

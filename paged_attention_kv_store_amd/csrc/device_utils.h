@@ -48,6 +48,17 @@ __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 __device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ uint2 load8(const void* p) { return *reinterpret_cast<const uint2*>(p); }
 
+// Max of v over the four lanes l, l^16, l^32, l^48 (the 16-lane rows of the
+// wave), with the gfx950 row-swap instructions instead of LDS permutes:
+// permlane16_swap(x, x) leaves rows (0,0,2,2) in one result and (1,1,3,3) in
+// the other, permlane32_swap(x, x) the lower and the upper halves.
+__device__ __forceinline__ float max_across_rows(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // ---- E4M3 quantisation (the cache format's reading) ------------------------
 // t = x / scale as one IEEE float32 division, clamped to +-448 (a NaN passes
 // through), rounded to the nearest E4M3 code with ties to even by the

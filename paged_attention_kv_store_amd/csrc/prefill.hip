@@ -86,9 +86,11 @@ void prefill_kernel(PrefillParams p) {
   const int bs = p.block_size;
   const int32_t* bt = p.block_tables + (int64_t)c * p.max_blocks;
   // A negative scale is applied as |scale| to negated q (exact in bf16), so
-  // the scale is >= 0 below and the row max of raw scores gives the max of
-  // scaled ones.
-  const float scale = fabsf(p.scale_log2);
+  // the scale is > 0 below and the row max of raw scores gives the max of
+  // scaled ones. A zero scale is taken as the smallest normal float: every
+  // weight 2^(FLT_MIN * x - m) then rounds to exactly what scale 0 gives,
+  // and a masked -inf score still yields weight 0 rather than NaN.
+  const float scale = fmaxf(fabsf(p.scale_log2), __FLT_MIN__);
   const uint32_t qsign = p.scale_log2 < 0.f ? 0x80008000u : 0u;
 
   // ---- the wave's Q rows (B operand of S^T = K Q^T) ----------------------
@@ -235,11 +237,8 @@ void prefill_kernel(PrefillParams p) {
 #pragma unroll
           for (int u = 0; u < 8; ++u) x[u] = (keyq + 16 * (u / 4) + (u % 4) < lim) ? x[u] : neg_inf();
         }
-        float mt = x[0];
-#pragma unroll
-        for (int u = 1; u < 8; ++u) mt = fmaxf(mt, x[u]);
-        mt = fmaxf(mt, shfl_xor_f(mt, 16));
-        mt = fmaxf(mt, shfl_xor_f(mt, 32));
+        float mt = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+        mt = max_across_rows(mt);
         mt = (mt == neg_inf()) ? mt : mt * scale;
         if (__any(mt > m_ref[t] + kRescaleThreshold)) {
           const float m_new = fmaxf(m_ref[t], mt);
@@ -253,19 +252,13 @@ void prefill_kernel(PrefillParams p) {
           }
           m_ref[t] = m_new;
         }
-        // weight 2^(scale*x - m); a masked score (-inf) gives 0
+        // weight 2^(scale*x - m): a masked score (-inf) gives exactly 0, since
+        // scale > 0 and m is finite (0 while the row has seen no key)
         const float nm = (m_ref[t] == neg_inf()) ? 0.f : -m_ref[t];
         uint32_t pw[4];
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          float e0 = fast_exp2(fmaf(x[2 * h], scale, nm));
-          float e1 = fast_exp2(fmaf(x[2 * h + 1], scale, nm));
-          if (!full) {
-            e0 = (x[2 * h] == neg_inf()) ? 0.f : e0;
-            e1 = (x[2 * h + 1] == neg_inf()) ? 0.f : e1;
-          }
-          pw[h] = pack_bf16x2(e0, e1);
-        }
+        for (int h = 0; h < 4; ++h)
+          pw[h] = pack_bf16x2(fast_exp2(fmaf(x[2 * h], scale, nm)), fast_exp2(fmaf(x[2 * h + 1], scale, nm)));
         pa[t] = bit_cast_to<bf16x8_t>(make_uint4(pw[0], pw[1], pw[2], pw[3]));
         lsum[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[t], ones, lsum[t], 0, 0, 0);
       }
