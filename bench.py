@@ -322,7 +322,13 @@ def secondary(device, steps, warmup, algo, bf16_step_ms):
     res["llama_prefix"] = {"ms": ms, "unique_GBps": ub / ms / 1e6, "logical_GBps": lb / ms / 1e6,
                            "pct_hbm_peak_unique": 100 * ub / ms / 1e6 / HBM_PEAK_GBS,
                            "tokens_per_s": b.num_seqs / (ms * 1e-3), "partition": 0,
-                           "balanced_ms": balanced_ms(b, bt, cl, steps, warmup)}
+                           "balanced_ms": balanced_ms(b, bt, cl, steps, warmup),
+                           "shared_prefix_ms": time_region(pkv.SharedPrefixDecodeLaunch(
+                               torch.empty_like(b.q), b.q, b.k_cache, b.v_cache, bt, cl,
+                               torch.arange(0, b.num_seqs + 1, 8, dtype=torch.int32, device=device),
+                               torch.full((b.num_seqs // 8,), 32 * b.block_size, dtype=torch.int32,
+                                          device=device),
+                               b.scale, b.max_ctx, 8, 32 * b.block_size), steps, warmup)}
     del dec, b
     b = W.long_splitk(device=device).batches[0]
     bt = torch.as_tensor(b.pool.block_tables, device=device)

@@ -252,6 +252,51 @@ int pkv_paged_attention_decode_store_fp8(void* out, const void* q, void* k_cache
                                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Shared-prefix decode. With prefix caching, sequences that start from the
+ * same prompt share its blocks ("Implementation Details", section
+ * "PagedAttention -- BlockPool": block hashes map equal content to one
+ * cached block, and blocks are reference-counted; "A vLLM engine small
+ * enough to read in one sitting", "Key highlights": prefix caching). This
+ * decode reads each shared block once per group instead of once per
+ * sequence; its result is that of pkv_paged_attention_decode.
+ *
+ * Sequences are split into num_groups groups of consecutive sequences:
+ * group j is sequences group_starts[j] .. group_starts[j+1]-1 (device int32
+ * [num_groups + 1], group_starts[0] = 0, group_starts[num_groups] =
+ * num_seqs; every sequence in exactly one group, singletons allowed). Its
+ * members share their first group_prefix_lens[j] tokens (device int32
+ * [num_groups]): a multiple of block_size (and of 16), at most every
+ * member's context length, with the same physical blocks in every member's
+ * block table (the first member's entries are the ones read). An unshared
+ * sequence is a group of one with prefix length 0.
+ *   max_group_size >= every group's size; max_prefix_len >= every prefix
+ *   length, <= max_context_len (host bounds for the grids).
+ * Two launches on `stream`: the groups' query rows over their prefixes (the
+ * prefill kernel, one non-causal chunk per group), writing fp32 partials to
+ * `workspace`; then decode over each sequence's remaining tokens, merged
+ * with its partials. A prefix length that is not a multiple of 16 or exceeds
+ * the context gives NaN rows; other violations give unspecified values.
+ *   workspace: pkv_decode_shared_prefix_workspace_size(...) bytes, 16-byte
+ *   aligned: m, l [num_seqs, num_q_heads], o [num_seqs, num_q_heads,
+ *   head_dim] fp32, then int32 [num_seqs]; scratch, no initial contents.
+ * Supported: bf16, head_dim 128, GQA group in {1, 2, 4, 8}, block_size a
+ * power of two in [16, 256].
+ */
+size_t pkv_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                               int32_t head_dim);
+int pkv_paged_attention_decode_shared_prefix(void* out, const void* q, const void* k_cache,
+                                             const void* v_cache, const int32_t* block_tables,
+                                             const int32_t* context_lens,
+                                             const int32_t* group_starts,
+                                             const int32_t* group_prefix_lens, int32_t num_groups,
+                                             int32_t max_group_size, int32_t max_prefix_len,
+                                             int32_t num_seqs, int32_t max_blocks_per_seq,
+                                             int32_t max_context_len, int32_t num_blocks,
+                                             int32_t block_size, int32_t num_q_heads,
+                                             int32_t num_kv_heads, int32_t head_dim, float scale,
+                                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * paged_attention_prefill_chunk: attention of packed query chunks over their
  * paged contexts. Chunk c owns q rows cu_seqlens_q[c] .. cu_seqlens_q[c+1]-1
  * (L_c rows); context_lens[c] >= L_c counts its cached tokens plus its own

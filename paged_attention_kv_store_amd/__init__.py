@@ -15,6 +15,7 @@ from .binding import (  # noqa: F401
     DecodeStoreLaunch,
     PkvError,
     PrefillLaunch,
+    SharedPrefixDecodeLaunch,
     StoreFp8Launch,
     StoreLaunch,
     decode_workspace_size,
@@ -24,6 +25,7 @@ from .binding import (  # noqa: F401
     library_path,
     paged_attention_decode,
     paged_attention_decode_fp8,
+    paged_attention_decode_shared_prefix,
     paged_attention_decode_store,
     paged_attention_decode_store_fp8,
     paged_attention_prefill_chunk,

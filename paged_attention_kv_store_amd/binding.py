@@ -47,6 +47,10 @@ _SIGNATURES = {
                                               _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                               ctypes.c_float, _i32, _vp, ctypes.c_size_t, _vp],
                                              ctypes.c_int),
+    "pkv_decode_shared_prefix_workspace_size": ([_i32, _i32, _i32], ctypes.c_size_t),
+    "pkv_paged_attention_decode_shared_prefix": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                                  _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                  ctypes.c_float, _vp, ctypes.c_size_t, _vp], ctypes.c_int),
     "pkv_paged_attention_prefill_chunk": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                                            _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                            ctypes.c_float, _i32, ctypes.c_int, _vp], ctypes.c_int),
@@ -230,6 +234,19 @@ def paged_attention_decode_store_fp8(out, q, k_cache, v_cache, k_scale, v_scale,
     the E4M3 caches, in one launch."""
     DecodeStoreFp8Launch(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, k_new,
                          v_new, slot_mapping, scale, max_context_len, partition_size, workspace)(stream)
+    return out
+
+
+def paged_attention_decode_shared_prefix(out, q, k_cache, v_cache, block_tables, context_lens,
+                                         group_starts, group_prefix_lens, scale, max_context_len,
+                                         max_group_size, max_prefix_len, workspace=None,
+                                         stream=None):
+    """Decode where groups of consecutive sequences share their first blocks:
+    group j is sequences group_starts[j] .. group_starts[j+1]-1 (int32 device
+    [NG+1]) sharing group_prefix_lens[j] tokens (int32 device [NG])."""
+    SharedPrefixDecodeLaunch(out, q, k_cache, v_cache, block_tables, context_lens, group_starts,
+                             group_prefix_lens, scale, max_context_len, max_group_size,
+                             max_prefix_len, workspace)(stream)
     return out
 
 
@@ -421,3 +438,36 @@ class DecodeStoreFp8Launch(_Prepared):
         self._keep = base._keep + (k_new, v_new, slot_mapping)
         self._fn = "pkv_paged_attention_decode_store_fp8"
         self._args = a[:8] + (_ptr(k_new), _ptr(v_new), _ptr(slot_mapping)) + a[8:]
+
+
+class SharedPrefixDecodeLaunch(_Prepared):
+    """paged_attention_decode_shared_prefix with fixed tensors; owns its workspace."""
+
+    def __init__(self, out, q, k_cache, v_cache, block_tables, context_lens, group_starts,
+                 group_prefix_lens, scale, max_context_len, max_group_size, max_prefix_len,
+                 workspace=None):
+        _dev(out, q, k_cache, v_cache, block_tables, context_lens, group_starts, group_prefix_lens)
+        _need(q.dim() == 3 and out.shape == q.shape and q.dtype == out.dtype == torch.bfloat16,
+              "q/out must be bf16 [S, Hq, D]")
+        _need(k_cache.dim() == 4 and v_cache.shape == k_cache.shape and k_cache.dtype == q.dtype,
+              "caches must be bf16 [NB, bs, Hkv, D]")
+        _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
+              and block_tables.shape[0] == q.shape[0], "block_tables must be int32 [S, MB]")
+        _need(context_lens.dtype == torch.int32 and context_lens.shape == (q.shape[0],),
+              "context_lens must be int32 [S]")
+        ng = group_prefix_lens.shape[0]
+        _need(group_starts.dtype == group_prefix_lens.dtype == torch.int32 and group_prefix_lens.dim() == 1
+              and group_starts.shape == (ng + 1,), "group_starts int32 [NG+1], group_prefix_lens int32 [NG]")
+        s, hq, d = q.shape
+        nb, bs, hkv, _ = k_cache.shape
+        need = int(lib().pkv_decode_shared_prefix_workspace_size(s, hq, d))
+        if workspace is None and need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        self._keep = (out, q, k_cache, v_cache, block_tables, context_lens, group_starts,
+                      group_prefix_lens, workspace)
+        self._fn = "pkv_paged_attention_decode_shared_prefix"
+        self._args = (_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                      _ptr(context_lens), _ptr(group_starts), _ptr(group_prefix_lens), ng,
+                      int(max_group_size), int(max_prefix_len), s, block_tables.shape[1],
+                      int(max_context_len), nb, bs, hq, hkv, d, float(scale), _ptr(workspace), ws_bytes)

@@ -226,6 +226,8 @@ int decode_impl(const char* fn, void* out, const void* q, const void* k_cache, c
   p.new_slots = fused ? new_slots : nullptr;
   p.k_scale = k_scale;
   p.v_scale = v_scale;
+  p.seq_prefix = nullptr;
+  p.pre_m = p.pre_l = p.pre_o = nullptr;
   p.bal_counters = nullptr;
   p.bal_pieces = nullptr;
   p.bal_piece_stride = 0;
@@ -427,5 +429,135 @@ extern "C" int pkv_paged_attention_prefill_chunk(void* out, const void* q, const
   p.max_ctx = max_context_len;
   p.scale_log2 = scale * pkv::kLog2e;
   p.causal = causal != 0;
+  p.table_row_is_first_q = 0;
+  p.part_m = p.part_l = p.part_o = nullptr;
+  p.seq_prefix = nullptr;
   return hip_status(pkv::launch_prefill(p, head_dim, (hipStream_t)stream), fn);
+}
+
+extern "C" size_t pkv_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                                          int32_t head_dim) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
+  // partials m, l, o per (sequence, q-head), then the prefix length of each sequence
+  return (size_t)num_seqs * num_q_heads * (head_dim + 2) * sizeof(float) + (size_t)num_seqs * sizeof(int32_t);
+}
+
+extern "C" int pkv_paged_attention_decode_shared_prefix(
+    void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+    const int32_t* context_lens, const int32_t* group_starts, const int32_t* group_prefix_lens,
+    int32_t num_groups, int32_t max_group_size, int32_t max_prefix_len, int32_t num_seqs,
+    int32_t max_blocks_per_seq, int32_t max_context_len, int32_t num_blocks, int32_t block_size,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float scale, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  const char* fn = "pkv_paged_attention_decode_shared_prefix";
+  if (num_seqs < 0 || num_groups < 0 || max_group_size < 0 || max_prefix_len < 0)
+    return fail(PKV_EINVAL, "%s: negative size", fn);
+  if (int rc = check_common(fn, num_blocks, block_size, num_kv_heads, head_dim, PKV_BF16)) return rc;
+  if (num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return fail(PKV_EINVAL, "%s: num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)", fn,
+                num_q_heads, num_kv_heads);
+  const int group = num_q_heads / num_kv_heads;
+  if (head_dim != 128) return fail(PKV_EUNSUPPORTED, "%s: head_dim 128 only", fn);
+  if (group != 1 && group != 2 && group != 4 && group != 8)
+    return fail(PKV_EUNSUPPORTED, "%s: GQA group %d not in {1, 2, 4, 8}", fn, group);
+  if (block_size < 16 || block_size > 256 || (block_size & (block_size - 1)) != 0)
+    return fail(PKV_EUNSUPPORTED, "%s: block_size %d must be a power of two in [16, 256]", fn, block_size);
+  if ((int64_t)block_size * num_kv_heads * head_dim * 2 >= ((int64_t)1 << 31))
+    return fail(PKV_EUNSUPPORTED, "%s: a cache block must be under 2 GiB", fn);
+  if (max_blocks_per_seq <= 0) return fail(PKV_EINVAL, "%s: max_blocks_per_seq must be positive", fn);
+  if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
+    return fail(PKV_EINVAL, "%s: max_context_len outside [0, max_blocks_per_seq * block_size]", fn);
+  if (max_prefix_len > max_context_len)
+    return fail(PKV_EINVAL, "%s: max_prefix_len exceeds max_context_len", fn);
+  if (!std::isfinite(scale)) return fail(PKV_EINVAL, "%s: scale is not finite", fn);
+  if (num_seqs > 65535 || num_kv_heads > 65535 || num_groups > 65535)
+    return fail(PKV_EUNSUPPORTED, "%s: num_seqs, num_groups and num_kv_heads are limited to 65535", fn);
+  if (num_seqs == 0) return PKV_OK;
+  if (num_groups == 0 || max_group_size == 0)
+    return fail(PKV_EINVAL, "%s: the groups must cover the sequences", fn);
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !group_starts ||
+      !group_prefix_lens)
+    return fail(PKV_EINVAL, "%s: null pointer", fn);
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 4) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(group_starts, 4) ||
+      !aligned(group_prefix_lens, 4))
+    return fail(PKV_EINVAL, "%s: q and caches must be 16-byte aligned; out and index arrays 4-byte", fn);
+  const size_t need = pkv_decode_shared_prefix_workspace_size(num_seqs, num_q_heads, head_dim);
+  if (!workspace || workspace_bytes < need)
+    return fail(PKV_EWORKSPACE, "%s: needs %zu workspace bytes, got %zu", fn, need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 16)) return fail(PKV_EINVAL, "%s: workspace must be 16-byte aligned", fn);
+  const int64_t cells = (int64_t)num_seqs * num_q_heads;
+  float* ws = reinterpret_cast<float*>(workspace);
+  float* part_m = ws;
+  float* part_l = ws + cells;
+  float* part_o = ws + 2 * cells;
+  int32_t* seq_prefix = reinterpret_cast<int32_t*>(ws + 2 * cells + cells * head_dim);
+  hipStream_t st = (hipStream_t)stream;
+
+  // first pass: each group's query rows over its shared prefix, as one
+  // non-causal chunk read through the first member's table
+  pkv::PrefillParams a;
+  a.out = nullptr;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.cu_seqlens_q = group_starts;
+  a.context_lens = group_prefix_lens;
+  a.num_seqs = num_groups;
+  a.total_q = num_seqs;
+  a.max_q_len = max_group_size;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.block_size = block_size;
+  a.block_size_log2 = __builtin_ctz((unsigned)block_size);
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = group;
+  a.max_ctx = max_prefix_len;
+  a.scale_log2 = scale * pkv::kLog2e;
+  a.causal = 0;
+  a.table_row_is_first_q = 1;
+  a.part_m = part_m;
+  a.part_l = part_l;
+  a.part_o = part_o;
+  a.seq_prefix = seq_prefix;
+  if (hipError_t e = pkv::launch_prefill(a, head_dim, st); e != hipSuccess) return hip_status(e, fn);
+
+  // second pass: each sequence's own tokens, merged with its prefix partials
+  pkv::DecodeParams b;
+  b.out = out;
+  b.q = q;
+  b.k_cache = k_cache;
+  b.v_cache = v_cache;
+  b.block_tables = block_tables;
+  b.context_lens = context_lens;
+  b.num_seqs = num_seqs;
+  b.max_blocks = max_blocks_per_seq;
+  b.num_blocks = num_blocks;
+  b.block_size = block_size;
+  b.num_q_heads = num_q_heads;
+  b.num_kv_heads = num_kv_heads;
+  b.group = group;
+  b.scale_log2 = scale * pkv::kLog2e;
+  b.max_ctx = max_context_len;
+  int32_t part;
+  int64_t nparts;
+  partitioning(max_context_len, 0, &part, &nparts);
+  b.partition_size = part;
+  b.num_partitions = 1;
+  b.ws_m = b.ws_l = b.ws_o = nullptr;
+  b.part_counters = nullptr;
+  b.k_new = b.v_new = nullptr;
+  b.new_slots = nullptr;
+  b.seq_prefix = seq_prefix;
+  b.pre_m = part_m;
+  b.pre_l = part_l;
+  b.pre_o = part_o;
+  b.k_scale = b.v_scale = nullptr;
+  b.bal_counters = nullptr;
+  b.bal_pieces = nullptr;
+  b.bal_piece_stride = 0;
+  return hip_status(pkv::launch_decode_mfma(b, head_dim, st), fn);
 }

@@ -71,6 +71,13 @@ struct DecodeParams {
   const void* k_new;
   const void* v_new;
   const int32_t* new_slots;
+  // Shared-prefix decode, second pass (null otherwise): the sequence's
+  // tokens before seq_prefix[s] are covered by partials of the first pass,
+  // merged into the output.
+  const int32_t* seq_prefix;   // [num_seqs]
+  const float* pre_m;          // [num_seqs, num_q_heads]
+  const float* pre_l;
+  const float* pre_o;          // [num_seqs, num_q_heads, head_dim]
   // E4M3 caches only (null otherwise): dequantisation scales [num_kv_heads].
   const float* k_scale;
   const float* v_scale;
@@ -122,6 +129,16 @@ struct PrefillParams {
   int32_t max_ctx;
   float scale_log2;
   int32_t causal;
+  // Shared-prefix decode, first pass (all null / 0 otherwise): chunk c is a
+  // group of sequences whose block-table row is that of its first query row
+  // (cu_seqlens_q[c]), and instead of normalised rows the kernel writes
+  // fp32 partials (log2 max, sum, unnormalised output) per (row, q-head),
+  // plus the chunk's context length for each of its rows in seq_prefix.
+  int32_t table_row_is_first_q;
+  float* part_m;             // [total_q, num_q_heads]
+  float* part_l;
+  float* part_o;             // [total_q, num_q_heads, head_dim]
+  int32_t* seq_prefix;       // [total_q]
 };
 
 // dtype codes match pkv_dtype

@@ -110,10 +110,18 @@ __device__ void merge_and_write(const DecodeParams& p, int s, int g, int part, i
   const int64_t head0 = (int64_t)s * p.num_q_heads + g * G;   // first q-head of the group
   for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
     const int h = idx / D, d = idx - h * D;
-    float M = neg_inf();
+    // a shared-prefix partial joins the waves' states as one more term
+    const bool pre = p.pre_m != nullptr;
+    const float mp = pre ? p.pre_m[head0 + h] : neg_inf();
+    float M = mp;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w * 16 + h]);
     float L = 0.f, O = 0.f;
+    if (pre && mp != neg_inf()) {
+      const float f = fast_exp2(mp - M);
+      L = p.pre_l[head0 + h] * f;
+      O = p.pre_o[(head0 + h) * D + d] * f;
+    }
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const float mw = s_m[w * 16 + h];
@@ -521,8 +529,20 @@ void decode_mfma_kernel(DecodeParams p) {
   const int G = p.group;
   const int ctx = clamp_ctx(p.context_lens[s], p.max_ctx);
   const int P = p.partition_size;
-  const int t0 = part * P;
-  if (t0 >= ctx) {
+  // Shared-prefix second pass: the tokens before `start` are covered by the
+  // first pass's partials (a prefix that is not a multiple of 16 or exceeds
+  // the context breaks the contract: the row is poisoned and no token read).
+  int start = 0;
+  bool bad_prefix = false;
+  if (p.seq_prefix != nullptr) {
+    start = p.seq_prefix[s];
+    if (start < 0 || start > ctx || (start & (kTile - 1)) != 0) {
+      bad_prefix = true;
+      start = ctx;
+    }
+  }
+  const int t0 = start + part * P;
+  if (t0 >= ctx && p.pre_m == nullptr) {
     if (part == 0) write_zero_rows<uint16_t, D>(p, s, g);
     return;
   }
@@ -821,7 +841,7 @@ void decode_mfma_kernel(DecodeParams p) {
       for (int e = 0; e < EPL; ++e) s_o[(w * GP + h) * D + EPL * n + e] = acc[e][r] * v_scale;
     }
   }
-  const bool poisoned = __any(bad);
+  const bool poisoned = __any(bad) || bad_prefix;
   if (threadIdx.x == 0) s_poison = 0;
   __syncthreads();
   if (poisoned && lane == 0) s_poison = 1;

@@ -84,7 +84,7 @@ void prefill_kernel(PrefillParams p) {
   const int n_kv = (kv_end + kKvTile - 1) / kKvTile;
   const int64_t row_elems = (int64_t)p.num_kv_heads * kD;
   const int bs = p.block_size;
-  const int32_t* bt = p.block_tables + (int64_t)c * p.max_blocks;
+  const int32_t* bt = p.block_tables + (int64_t)(p.table_row_is_first_q ? q_start : c) * p.max_blocks;
   // A negative scale is applied as |scale| to negated q (exact in bf16), so
   // the scale is > 0 below and the row max of raw scores gives the max of
   // scaled ones. A zero scale is taken as the smallest normal float: every
@@ -298,6 +298,31 @@ void prefill_kernel(PrefillParams p) {
   if (bad) s_bad = 1;
   __syncthreads();
   const bool poisoned = s_bad != 0;
+  if (p.part_m != nullptr) {
+    // partials for a later merge: row 16t + 4qg + r's reference max sits in
+    // the lane whose n is 4qg + r; sums are replicated over n
+    if (g == 0 && qt == 0 && w == 0)
+      for (int i = lane; i < L; i += 64) p.seq_prefix[q_start + i] = ctx;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float m = __shfl(m_ref[t], 4 * qg + r, 64);
+        const int mr = 32 * w + 16 * t + 4 * qg + r;
+        const int qi = r0 + mr / G;
+        if (qi >= L) continue;
+        const int64_t row = (int64_t)(q_start + qi) * p.num_q_heads + g * G + mr % G;
+        float* po = p.part_o + row * kD + 8 * n;
+        *reinterpret_cast<float4*>(po) = make_float4(acc[t][0][r], acc[t][1][r], acc[t][2][r], acc[t][3][r]);
+        *reinterpret_cast<float4*>(po + 4) = make_float4(acc[t][4][r], acc[t][5][r], acc[t][6][r], acc[t][7][r]);
+        if (n == 0) {
+          p.part_m[row] = m;
+          p.part_l[row] = poisoned ? __builtin_nanf("") : lsum[t][r];
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
 #pragma unroll

@@ -188,3 +188,37 @@ def test_fused_store_rejects_missing_rows():
                                               4, 16, 256, 64, 16, 8, 4, 64, 0.125, 0, None, 0, 0, 0,
                                               None)
     assert rc == binding.PKV_EINVAL
+
+
+def _shared(lib, **over):
+    a = dict(out=1024, q=1024, k=1024, v=1024, bt=1024, cl=1024, gs=1024, gp=1024, NG=2, GS=4, PL=64,
+             S=8, MB=16, max_ctx=256, NB=64, bs=16, Hq=32, Hkv=8, D=128, scale=0.08, ws=1024,
+             ws_bytes=1 << 20, stream=None)
+    a.update(over)
+    return lib.pkv_paged_attention_decode_shared_prefix(
+        a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["gs"], a["gp"], a["NG"], a["GS"], a["PL"],
+        a["S"], a["MB"], a["max_ctx"], a["NB"], a["bs"], a["Hq"], a["Hkv"], a["D"], a["scale"], a["ws"],
+        a["ws_bytes"], a["stream"])
+
+
+@needs_lib
+@pytest.mark.parametrize("over,code", [
+    (dict(S=-1), binding.PKV_EINVAL),
+    (dict(D=64), binding.PKV_EUNSUPPORTED),
+    (dict(Hq=24, Hkv=8), binding.PKV_EUNSUPPORTED),
+    (dict(bs=48), binding.PKV_EUNSUPPORTED),
+    (dict(PL=300), binding.PKV_EINVAL),
+    (dict(NG=0), binding.PKV_EINVAL),
+    (dict(gs=None), binding.PKV_EINVAL),
+    (dict(ws_bytes=100), binding.PKV_EWORKSPACE),
+    (dict(ws=1032), binding.PKV_EINVAL),
+])
+def test_shared_prefix_rejects(over, code):
+    lib = pkv.lib()
+    assert _shared(lib, **over) == code
+    assert lib.pkv_last_error()
+
+
+@needs_lib
+def test_shared_prefix_workspace_size():
+    assert pkv.lib().pkv_decode_shared_prefix_workspace_size(8, 32, 128) == 8 * 32 * 130 * 4 + 8 * 4
