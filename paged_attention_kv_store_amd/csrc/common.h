@@ -119,6 +119,7 @@ struct PrefillParams {
   int32_t total_q;
   int32_t max_q_len;
   int32_t num_q_tiles;       // set by the launcher
+  int32_t longest_first;     // set by the launcher: items start in order of cost
   int32_t max_blocks;
   int32_t num_blocks;
   int32_t block_size;

@@ -45,6 +45,99 @@ constexpr int kXcds = 8;              // accelerator complex dies, each with its
 // LDS position (in 16-byte units) of piece c of key row t in a tile.
 __device__ __forceinline__ int swz(int t, int c) { return t * kRowPieces + (c ^ (t & 15)); }
 
+// Rank of an item's cost: 1 + its 64-key tiles (0 for a q-tile past the end
+// of its chunk), capped at kOrderBuckets - 1.
+constexpr int kOrderBuckets = 4096;
+constexpr int kOrderMaxItems = 8192;   // (chunk, q-tile) items ranked in LDS
+
+template <int BQ>
+__device__ __forceinline__ int item_cost(const PrefillParams& p, int j) {
+  const int c = j / p.num_q_tiles, qt = j % p.num_q_tiles;
+  const int q_start = min(max(p.cu_seqlens_q[c], 0), p.total_q);
+  const int L = min(max(p.cu_seqlens_q[c + 1], q_start), p.total_q) - q_start;
+  const int r0 = qt * BQ;
+  if (r0 >= L) return 0;
+  const int ctx = min(max(p.context_lens[c], 0), p.max_ctx);
+  const int kv_end = p.causal ? min(ctx, max(ctx - L, 0) + min(r0 + BQ, L)) : ctx;
+  return min(1 + (kv_end + kKvTile - 1) / kKvTile, kOrderBuckets - 1);
+}
+
+// The (chunk, q-tile) item j = chunk * num_q_tiles + q-tile of the given
+// rank when items are ordered by cost, highest first, ties by j; -1 past the
+// last rank. Whole workgroup; hist (kOrderBuckets ints) and cost
+// (kOrderMaxItems entries) are LDS the caller does not use until after the
+// barrier this ends with.
+template <int BQ>
+__device__ int longest_first_item(const PrefillParams& p, int rank, int* hist, uint16_t* cost) {
+  constexpr int kPerThread = kOrderBuckets / kPThreads;   // 16 buckets per thread
+  __shared__ int s_wave[kPW];
+  __shared__ int s_pick[2];
+  const int n_items = p.num_q_tiles * p.num_seqs;
+  if (rank >= n_items) return -1;                           // workgroup-uniform
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int i = tid; i < kOrderBuckets; i += kPThreads) hist[i] = 0;
+  __syncthreads();
+  for (int j = tid; j < n_items; j += kPThreads) {
+    const int b = item_cost<BQ>(p, j);
+    cost[j] = (uint16_t)b;
+    atomicAdd(&hist[b], 1);
+  }
+  __syncthreads();
+  // items in this thread's buckets, and in all higher buckets (a suffix sum
+  // over threads: lanes above within the wave, then the waves above)
+  int mine = 0;
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) mine += hist[kPerThread * tid + i];
+  int suffix = mine;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int x = __shfl_down(suffix, d, 64);
+    if (lane + d < 64) suffix += x;
+  }
+  if (lane == 0) s_wave[w] = suffix;
+  __syncthreads();
+  int above = suffix - mine;
+  for (int v = w + 1; v < kPW; ++v) above += s_wave[v];
+  if (above <= rank && rank < above + mine) {
+    for (int i = kPerThread - 1; i >= 0; --i) {
+      const int cnt = hist[kPerThread * tid + i];
+      if (rank < above + cnt) {
+        s_pick[0] = kPerThread * tid + i;
+        s_pick[1] = rank - above;
+        break;
+      }
+      above += cnt;
+    }
+  }
+  __syncthreads();
+  // the k-th item (in index order) of the chosen bucket
+  const int bucket = s_pick[0];
+  int k = s_pick[1];
+  int item = -1;
+  for (int base = 0; base < n_items; base += kPThreads) {
+    const int j = base + tid;
+    const bool hit = j < n_items && cost[j] == bucket;
+    const uint64_t mask = __ballot(hit);
+    __syncthreads();                        // s_wave of the previous pass is read
+    if (lane == 0) s_wave[w] = __popcll(mask);
+    __syncthreads();
+    int before = 0, total = 0;
+    for (int v = 0; v < kPW; ++v) {
+      before += v < w ? s_wave[v] : 0;
+      total += s_wave[v];
+    }
+    if (k < total) {
+      if (hit && before + __popcll(mask & ((1ull << lane) - 1)) == k) s_pick[0] = j;
+      __syncthreads();
+      item = s_pick[0];
+      break;
+    }
+    k -= total;
+  }
+  __syncthreads();                          // hist, cost and s_pick are free again
+  return item;
+}
+
 }  // namespace
 
 template <int G>
@@ -56,19 +149,36 @@ void prefill_kernel(PrefillParams p) {
   __shared__ int s_bad;
 
   // Work item of this workgroup. Workgroups are handed to the 8 XCDs round
-  // robin (id % 8), each XCD with its own L2. Item i = x * (items/8) + id/8
-  // for x = id % 8 gives every XCD a contiguous range of items, ordered with
-  // the kv-head slowest and the q-tiles of a chunk adjacent: all q-tiles that
-  // read the same chunk's K/V run on one XCD, close in time, and share its
-  // L2. Within a chunk the q-tiles with more keys go first.
+  // robin (id % 8), each XCD with its own L2, and start in id order as
+  // earlier ones finish.
+  //  * Longest first (the usual case): id = rank * kv_heads + kv-head, where
+  //    rank orders the (chunk, q-tile) items by their key tiles, most first,
+  //    so the long items start at once and the short ones fill the tail.
+  //    With 8 kv-heads every XCD serves one kv-head, all its items in that
+  //    order, and the q-tiles of a chunk share the XCD's L2.
+  //  * Otherwise (too many items to rank in LDS): item i = x * (items/8) +
+  //    id/8 for x = id % 8 gives every XCD a contiguous range of items, the
+  //    kv-head slowest and the q-tiles of a chunk adjacent, the q-tiles with
+  //    more keys first.
   const int nqt = p.num_q_tiles;
-  const int per_xcd = gridDim.x / kXcds;
-  const int item = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-  if (item >= nqt * p.num_seqs * p.num_kv_heads) return;
-  const int qt = nqt - 1 - item % nqt;
-  const int c = (item / nqt) % p.num_seqs;
-  const int g = item / (nqt * p.num_seqs);
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x;
+  int qt, c, g;
+  if (p.longest_first) {
+    g = blockIdx.x % p.num_kv_heads;
+    const int j = longest_first_item<BQ>(p, blockIdx.x / p.num_kv_heads, reinterpret_cast<int*>(s_v[1]),
+                                         reinterpret_cast<uint16_t*>(s_k[1]));
+    if (j < 0) return;
+    c = j / nqt;
+    qt = j % nqt;
+  } else {
+    const int per_xcd = gridDim.x / kXcds;
+    const int item = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+    if (item >= nqt * p.num_seqs * p.num_kv_heads) return;
+    qt = nqt - 1 - item % nqt;
+    c = (item / nqt) % p.num_seqs;
+    g = item / (nqt * p.num_seqs);
+  }
+  const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, qg = lane >> 4;
 
@@ -346,6 +456,7 @@ hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t stre
   const int bq = kMRows / p.group;
   PrefillParams q = p;
   q.num_q_tiles = (p.max_q_len + bq - 1) / bq;
+  q.longest_first = (int64_t)q.num_q_tiles * p.num_seqs <= kOrderMaxItems;
   const int64_t items = (int64_t)q.num_q_tiles * p.num_seqs * p.num_kv_heads;
   if (items > 0x7fffffff - kXcds) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((items + kXcds - 1) / kXcds * kXcds));

@@ -18,7 +18,7 @@ def gpu_prefill(b, dev=None, causal=True, store=True):
     if store and b.k_new is not None:
         pkv.kv_cache_store(dev["k_new"], dev["v_new"], dev["k_cache"], dev["v_cache"],
                            dev["slot_mapping"])
-    out = torch.empty_like(dev["q"])
+    out = torch.full_like(dev["q"], float("nan"))   # a row no workgroup writes stays NaN
     cu = b.cu_seqlens_q
     pkv.paged_attention_prefill_chunk(out, dev["q"], dev["k_cache"], dev["v_cache"],
                                       dev["block_tables"], dev["cu_seqlens_q"],
