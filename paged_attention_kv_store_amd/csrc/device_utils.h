@@ -52,11 +52,19 @@ __device__ __forceinline__ uint2 load8(const void* p) { return *reinterpret_cast
 // wave), with the gfx950 row-swap instructions instead of LDS permutes:
 // permlane16_swap(x, x) leaves rows (0,0,2,2) in one result and (1,1,3,3) in
 // the other, permlane32_swap(x, x) the lower and the upper halves.
+// NaN-propagating (IEEE maximum, v_maximum3_f32 on gfx950: no canonicalising
+// moves as with fmaxf).
 __device__ __forceinline__ float max_across_rows(float v) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  v = __builtin_elementwise_maximum(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return __builtin_elementwise_maximum(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// NaN-propagating maximum of eight values (three v_maximum3_f32 on gfx950)
+__device__ __forceinline__ float max8(const float (&x)[8]) {
+  const auto mx = [](float a, float b) { return __builtin_elementwise_maximum(a, b); };
+  return mx(mx(mx(x[0], x[1]), mx(x[2], x[3])), mx(mx(x[4], x[5]), mx(x[6], x[7])));
 }
 
 // ---- E4M3 quantisation (the cache format's reading) ------------------------

@@ -14,8 +14,9 @@
 // The keys are walked in 64-token tiles gathered through the block table
 // straight into LDS with direct-to-LDS loads (double-buffered: the next
 // tile's loads are in flight while the current one is consumed), 16-byte
-// pieces XOR-swizzled by row so that both access patterns below are free of
-// bank conflicts. Per 16 keys:
+// pieces XOR-swizzled by row, with one swizzle for K and another for V, each
+// chosen (by measurement on gfx950) so that its read pattern below is free
+// of bank conflicts. Per 16 keys:
 //  * S^T = K Q^T on 16x16x32 bf16 MFMA (A = 16 K rows from LDS, B = the
 //    wave's Q rows kept in registers) gives each lane the scores of keys
 //    4*(l/16)+r for M row l%16;
@@ -42,8 +43,13 @@ constexpr int kKvTile = 64;           // keys per LDS tile
 constexpr int kRowPieces = kD * 2 / 16;   // 16-byte pieces per K/V row (16)
 constexpr int kXcds = 8;              // accelerator complex dies, each with its own L2
 
-// LDS position (in 16-byte units) of piece c of key row t in a tile.
-__device__ __forceinline__ int swz(int t, int c) { return t * kRowPieces + (c ^ (t & 15)); }
+// LDS position (in 16-byte units) of piece c of key row t in a tile: piece
+// c ^ sk(t) for K, c ^ sv(t) for V, where sk(t) = t mod 16 and sv swaps the
+// two 2-bit halves of t mod 16.
+__device__ __forceinline__ int k_swizzle(int t) { return t & 15; }
+__device__ __forceinline__ int v_swizzle(int t) { return ((t & 3) << 2) | ((t >> 2) & 3); }
+__device__ __forceinline__ int swz_k(int t, int c) { return t * kRowPieces + (c ^ k_swizzle(t)); }
+__device__ __forceinline__ int swz_v(int t, int c) { return t * kRowPieces + (c ^ v_swizzle(t)); }
 
 // Rank of an item's cost: 1 + its 64-key tiles (0 for a q-tile past the end
 // of its chunk), capped at kOrderBuckets - 1.
@@ -231,8 +237,9 @@ void prefill_kernel(PrefillParams p) {
   // ---- cooperative K/V tile gather, global memory straight into LDS -------
   // A direct-to-LDS load puts lane j's 16 bytes at (wave's LDS base) + 16j.
   // Load i of wave w fills LDS rows 16i + 4w .. +3 of the tile, so lane j
-  // fetches key row t = 16i + 4w + j/16, piece (j%16) ^ (t%16): the swizzled
-  // layout comes out of the choice of source addresses. Rows 16i .. 16i+15 of
+  // fetches key row t = 16i + 4w + j/16, piece (j%16) ^ sk(t) of K and
+  // (j%16) ^ sv(t) of V: the swizzled layout comes out of the choice of
+  // source addresses. Rows 16i .. 16i+15 of
   // a tile lie in one block (block_size is a power of two >= 16), so a tile
   // needs four block ids, all workgroup-uniform, scalar-loaded a tile ahead.
   // Rows past the context are read from the last live row instead (finite
@@ -258,14 +265,15 @@ void prefill_kernel(PrefillParams p) {
         bad = true;
       }
       const int t = 16 * i + lrow;
-      const int piece = (lane & 15) ^ (t & 15);
       const int pos = min(kv0 + t, ctx - 1);
-      const int64_t off = (((int64_t)blk << lbs) + (pos & (bs - 1))) * row_bytes + piece * 16;
+      const int64_t off = (((int64_t)blk << lbs) + (pos & (bs - 1))) * row_bytes;
       const int lds_pos = (16 * i + 4 * w) * kRowPieces;
-      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(kbase + off),
-                                       (void __attribute__((address_space(3)))*)(&s_k[buf][lds_pos]), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(vbase + off),
-                                       (void __attribute__((address_space(3)))*)(&s_v[buf][lds_pos]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1)))*)(kbase + off + ((lane & 15) ^ k_swizzle(t)) * 16),
+          (void __attribute__((address_space(3)))*)(&s_k[buf][lds_pos]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1)))*)(vbase + off + ((lane & 15) ^ v_swizzle(t)) * 16),
+          (void __attribute__((address_space(3)))*)(&s_v[buf][lds_pos]), 16, 0, 0);
     }
   };
   // all of this thread's direct-to-LDS loads have landed (vmcnt 0)
@@ -325,10 +333,12 @@ void prefill_kernel(PrefillParams p) {
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) kf[h][s] = bit_cast_to<bf16x8_t>(sk[swz(tb + 16 * h + n, 4 * s + qg)]);
+        for (int s = 0; s < 4; ++s) kf[h][s] = bit_cast_to<bf16x8_t>(sk[swz_k(tb + 16 * h + n, 4 * s + qg)]);
       const int keyq = kv0 + tb + 4 * qg;   // key of slot 0
       const bool full = kv0 + tb + 32 <= lim_wave;   // no key of the block is masked for this wave
       bf16x8_t pa[2];
+      bool grow[2] = {false, false};          // the tile's reference max rises (wave-uniform)
+      float alpha[2];                         // and the factor of the lane's softmax row
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         if (t == 1 && !live1) break;
@@ -347,20 +357,13 @@ void prefill_kernel(PrefillParams p) {
 #pragma unroll
           for (int u = 0; u < 8; ++u) x[u] = (keyq + 16 * (u / 4) + (u % 4) < lim) ? x[u] : neg_inf();
         }
-        float mt = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-        mt = max_across_rows(mt);
-        mt = (mt == neg_inf()) ? mt : mt * scale;
+        // scale > 0 is finite, so a row max of -inf stays -inf
+        const float mt = max_across_rows(max8(x)) * scale;
         if (__any(mt > m_ref[t] + kRescaleThreshold)) {
           const float m_new = fmaxf(m_ref[t], mt);
-          const float alpha = (m_new == neg_inf()) ? 1.f : fast_exp2(m_ref[t] - m_new);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float a = __shfl(alpha, 4 * qg + r, 64);   // factor of row 4qg + r
-            lsum[t][r] *= a;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[t][i][r] *= a;
-          }
+          alpha[t] = (m_new == neg_inf()) ? 1.f : fast_exp2(m_ref[t] - m_new);
           m_ref[t] = m_new;
+          grow[t] = true;
         }
         // weight 2^(scale*x - m): a masked score (-inf) gives exactly 0, since
         // scale > 0 and m is finite (0 while the row has seen no key)
@@ -370,13 +373,28 @@ void prefill_kernel(PrefillParams p) {
         for (int h = 0; h < 4; ++h)
           pw[h] = pack_bf16x2(fast_exp2(fmaf(x[2 * h], scale, nm)), fast_exp2(fmaf(x[2 * h + 1], scale, nm)));
         pa[t] = bit_cast_to<bf16x8_t>(make_uint4(pw[0], pw[1], pw[2], pw[3]));
+      }
+      // Rescale where the reference rose, once both tiles' scores are done
+      // (fewer registers live here than inside the softmax above).
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        if (t == 1 && !live1) break;
+        if (grow[t]) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float a = __shfl(alpha[t], 4 * qg + r, 64);   // factor of row 4qg + r
+            lsum[t][r] *= a;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[t][i][r] *= a;
+          }
+        }
         lsum[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[t], ones, lsum[t], 0, 0, 0);
       }
       // V rows of the lane's 8 keys, piece n (columns 8n .. 8n+7)
       uint32_t vd[8][4];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const uint4 v = sv[swz(tb + 16 * (u / 4) + 4 * qg + (u % 4), n)];
+        const uint4 v = sv[swz_v(tb + 16 * (u / 4) + 4 * qg + (u % 4), n)];
         vd[u][0] = v.x;
         vd[u][1] = v.y;
         vd[u][2] = v.z;
