@@ -231,6 +231,7 @@ int decode_impl(const char* fn, void* out, const void* q, const void* k_cache, c
   p.bal_counters = nullptr;
   p.bal_pieces = nullptr;
   p.bal_piece_stride = 0;
+  p.pair_span = 0;
   hipStream_t st = (hipStream_t)stream;
   if (balanced) {
     const size_t need = pkv_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,

@@ -86,6 +86,9 @@ struct DecodeParams {
   int32_t* bal_counters;
   float* bal_pieces;
   int32_t bal_piece_stride;  // floats per piece
+  // Set by the per-item launcher: the compute units, when workgroups are
+  // given their items by size (0: in index order).
+  int32_t pair_span;
 };
 
 // Split-K: the workspace starts with this many arrival counters (one per

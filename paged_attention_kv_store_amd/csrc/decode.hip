@@ -215,11 +215,10 @@ struct NewRow {
   int pos;
 };
 
-__device__ __forceinline__ NewRow new_row_of(const DecodeParams& p, int s, int ctx, int t0, int t1,
+__device__ __forceinline__ NewRow new_row_of(const DecodeParams& p, int slot, int ctx, int t0, int t1,
                                              int w) {
   NewRow r{false, -1, ctx - 1};
   if (p.new_slots == nullptr) return r;
-  const int slot = p.new_slots[s];
   if (slot < 0 || (int64_t)slot >= (int64_t)p.num_blocks * p.block_size) return r;  // padding / outside
   if (r.pos < t0 || r.pos >= t1) return r;                                            // another partition
   r.slot = slot;
@@ -239,18 +238,47 @@ __device__ __forceinline__ NewRow new_row_of(const DecodeParams& p, int s, int c
 //    index (with 2 partitions and mostly short sequences, a fixed mapping
 //    would leave half the XCDs nearly idle).
 // Returns false for the grid's padding.
+// The launchers keep the item count below 2^31, so 32-bit arithmetic holds.
 constexpr int kXcds = 8;
 __device__ __forceinline__ bool decode_item(const DecodeParams& p, int& g, int& part, int& s) {
-  int64_t item = blockIdx.x;
-  if (p.num_partitions > 1) {
-    const int64_t x = item % kXcds, k = item / kXcds;
+  uint32_t item = blockIdx.x;
+  const uint32_t np = (uint32_t)p.num_partitions, hkv = (uint32_t)p.num_kv_heads;
+  if (np > 1) {
+    const uint32_t x = item % kXcds, k = item / kXcds;
     item = k * kXcds + (x + k) % kXcds;
   }
-  if (item >= (int64_t)p.num_seqs * p.num_kv_heads * p.num_partitions) return false;
-  part = (int)(item % p.num_partitions);
-  g = (int)((item / p.num_partitions) % p.num_kv_heads);
-  s = (int)(item / ((int64_t)p.num_partitions * p.num_kv_heads));
+  if (item >= (uint32_t)p.num_seqs * hkv * np) return false;
+  const uint32_t r = np > 1 ? item / np : item;
+  part = (int)(item - r * np);
+  s = (int)(r / hkv);
+  g = (int)(r - (uint32_t)s * hkv);
   return true;
+}
+
+// Work item by size (single pass, no shared prefix). Two workgroups of this
+// kernel fit a compute unit, and with C units workgroup b and workgroup
+// b + C are placed on the same one (the dispatcher fills every unit once,
+// then again in the same order). Items are ranked by their 16-token tiles,
+// most first: workgroups 0 .. C-1 take ranks 0 .. C-1 and workgroups
+// C .. F-1 (F = min(items, 2C)) take ranks F-1 down to C, so each unit pairs
+// a long item with a short one; workgroups past F, started as earlier ones
+// finish, take the remaining ranks in order. Ranks are over sequences (all
+// kv-heads of a sequence are adjacent).
+constexpr int kRankBuckets = 2048;     // tiles per sequence, capped
+constexpr int kRankMaxSeqs = 4096;
+__device__ __forceinline__ bool ranked_item(const DecodeParams& p, int& g, int& s, int* hist, uint16_t* cost) {
+  const int hkv = p.num_kv_heads;
+  const int n = p.num_seqs * hkv, c = p.pair_span, f = min(n, 2 * c);
+  const int b = blockIdx.x;
+  const int r = b < c ? b : (b < f ? f - 1 - (b - c) : b);
+  if (r >= n) return false;                  // workgroup-uniform
+  const int q = r / hkv;
+  g = r - q * hkv;
+  s = item_of_rank<kThreads, kRankBuckets>(
+      q, p.num_seqs,
+      [&](int i) { return min((clamp_ctx(p.context_lens[i], p.max_ctx) + kTile - 1) / kTile, kRankBuckets - 1); },
+      hist, cost);
+  return s >= 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -336,7 +364,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
 
   // Fused store: the sequence's new row (position ctx-1) goes to its slot,
   // and the wave that owns the tile holding ctx-1 uses it from registers.
-  const NewRow nr = new_row_of(p, s, ctx, t0, t1, w);
+  const NewRow nr = new_row_of(p, p.new_slots != nullptr ? p.new_slots[s] : -1, ctx, t0, t1, w);
   uint4 nk = make_uint4(0, 0, 0, 0), nv = make_uint4(0, 0, 0, 0);
   if (nr.mine) {
     const int64_t src = ((int64_t)s * p.num_kv_heads + g) * D + c * EPL;
@@ -520,38 +548,32 @@ void decode_mfma_kernel(DecodeParams p) {
   __shared__ float s_m[kWaves * 16], s_l[kWaves * 16];
   __shared__ float s_o[kWaves * GP * D];
   __shared__ int s_poison;
+  __shared__ int s_rank_hist[kRankBuckets];
+  __shared__ uint16_t s_rank_cost[kRankMaxSeqs];
 
-  int g, part, s;
-  if (!decode_item(p, g, part, s)) return;
+  int g, part = 0, s;
+  if (p.pair_span > 0) {
+    if (!ranked_item(p, g, s, s_rank_hist, s_rank_cost)) return;
+  } else if (!decode_item(p, g, part, s)) {
+    return;
+  }
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, qg = lane >> 4;
   const int G = p.group;
-  const int ctx = clamp_ctx(p.context_lens[s], p.max_ctx);
   const int P = p.partition_size;
-  // Shared-prefix second pass: the tokens before `start` are covered by the
-  // first pass's partials (a prefix that is not a multiple of 16 or exceeds
-  // the context breaks the contract: the row is poisoned and no token read).
-  int start = 0;
-  bool bad_prefix = false;
-  if (p.seq_prefix != nullptr) {
-    start = p.seq_prefix[s];
-    if (start < 0 || start > ctx || (start & (kTile - 1)) != 0) {
-      bad_prefix = true;
-      start = ctx;
-    }
-  }
-  const int t0 = start + part * P;
-  if (t0 >= ctx && p.pre_m == nullptr) {
-    if (part == 0) write_zero_rows<uint16_t, D>(p, s, g);
-    return;
-  }
-  const int n_parts = (ctx + P - 1) / P;
-  const int t1 = min(ctx, t0 + P);
-  const int n_tiles = (t1 - t0 + kTile - 1) / kTile;
-  const int my_tiles = w < n_tiles ? (n_tiles - w + kWaves - 1) / kWaves : 0;
-  const int64_t row_elems = (int64_t)p.num_kv_heads * D;
   const int bs = p.block_size;
+  const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks;
+
+  // The loads that depend only on the work item are issued together, before
+  // any of them is waited for: the context length, the new row's slot and
+  // pieces (fused store), the shared prefix, the q rows, and the block of
+  // the wave's first tile as it is without a shared prefix (index kept
+  // inside the table row; used only when it is the right entry).
+  const int ctx_raw = p.context_lens[s];
+  const int slot_raw = p.new_slots != nullptr ? p.new_slots[s] : -1;
+  const int prefix_raw = p.seq_prefix != nullptr ? p.seq_prefix[s] : 0;
+  const int blk_first = bt[min((part * P + w * kTile) / bs, p.max_blocks - 1)];
 
   // B operand of q.k^T: column n is q-head g*G+n (zero past the group). In
   // step c, lane group qg holds head_dim elements [32c + 8qg, 32c + 8qg + 8),
@@ -570,6 +592,48 @@ void decode_mfma_kernel(DecodeParams p) {
       qb[j] = bit_cast_to<bf16x8_t>(v);
     }
   }
+  // The new row's pieces as this lane uses them (bf16), loaded whether or
+  // not this wave turns out to hold the new row's position.
+  constexpr int kNewK = FP8 ? 2 * (D / 64) : KCH;
+  uint4 nkr[kNewK], nvr = make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int c = 0; c < kNewK; ++c) nkr[c] = make_uint4(0, 0, 0, 0);
+  if (p.new_slots != nullptr) {
+    const uint16_t* kn = reinterpret_cast<const uint16_t*>(p.k_new) + ((int64_t)s * p.num_kv_heads + g) * D;
+    const uint16_t* vn = reinterpret_cast<const uint16_t*>(p.v_new) + ((int64_t)s * p.num_kv_heads + g) * D;
+#pragma unroll
+    for (int c = 0; c < kNewK; ++c) nkr[c] = load16(kn + (FP8 ? qg * (D / 4) + 8 * c : 8 * qg + 32 * c));
+    if constexpr (EPL == 8) {
+      nvr = load16(vn + EPL * n);
+    } else {
+      const uint2 h = load8(vn + EPL * n);
+      nvr = make_uint4(h.x, h.y, 0, 0);
+    }
+  }
+
+  const int ctx = clamp_ctx(ctx_raw, p.max_ctx);
+  // Shared-prefix second pass: the tokens before `start` are covered by the
+  // first pass's partials (a prefix that is not a multiple of 16 or exceeds
+  // the context breaks the contract: the row is poisoned and no token read).
+  int start = 0;
+  bool bad_prefix = false;
+  if (p.seq_prefix != nullptr) {
+    start = prefix_raw;
+    if (start < 0 || start > ctx || (start & (kTile - 1)) != 0) {
+      bad_prefix = true;
+      start = ctx;
+    }
+  }
+  const int t0 = start + part * P;
+  if (t0 >= ctx && p.pre_m == nullptr) {
+    if (part == 0) write_zero_rows<uint16_t, D>(p, s, g);
+    return;
+  }
+  const int n_parts = (ctx + P - 1) / P;
+  const int t1 = min(ctx, t0 + P);
+  const int n_tiles = (t1 - t0 + kTile - 1) / kTile;
+  const int my_tiles = w < n_tiles ? (n_tiles - w + kWaves - 1) / kWaves : 0;
+  const int64_t row_elems = (int64_t)p.num_kv_heads * D;
   // logit multiplier (with the K scale for E4M3 caches) and V scale
   const float logit_scale = FP8 ? p.scale_log2 * p.k_scale[g] : p.scale_log2;
 
@@ -577,7 +641,6 @@ void decode_mfma_kernel(DecodeParams p) {
   const char* kc = reinterpret_cast<const char*>(p.k_cache) + (g * D + (FP8 ? qg * (D / 4) : 8 * qg)) * kElt;
   // V: lane reads rows 4*qg + st (st = 0..3), columns EPL*n .. EPL*n+EPL-1
   const char* vc = reinterpret_cast<const char*>(p.v_cache) + (g * D + EPL * n) * kElt;
-  const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks;
 
   float m_ref = neg_inf();   // reference max of head n (replicated over qg)
   float l_part = 0.f;        // sum over this lane's tokens for head n
@@ -590,41 +653,25 @@ void decode_mfma_kernel(DecodeParams p) {
   // and the wave that owns the tile holding ctx-1 uses it from registers.
   // E4M3 caches: the new row is quantised here exactly as the store kernel
   // does, and its codes stand in for the cache's.
-  const NewRow nr = new_row_of(p, s, ctx, t0, t1, w);
-  uint4 nk[KCH], nv = make_uint4(0, 0, 0, 0);     // bf16 new row pieces
+  // (bf16 caches use nkr / nvr as they are.)
+  const NewRow nr = new_row_of(p, slot_raw, ctx, t0, t1, w);
   uint4 nk8[D / 64];                               // E4M3: codes of elements qg*D/4 ..
   uint2 nv8 = make_uint2(0u, 0u);                  // E4M3: codes of columns EPL*n ..
 #pragma unroll
-  for (int c = 0; c < KCH; ++c) nk[c] = make_uint4(0, 0, 0, 0);
-#pragma unroll
   for (int c = 0; c < D / 64; ++c) nk8[c] = make_uint4(0, 0, 0, 0);
-  if (nr.mine) {
-    const uint16_t* kn = reinterpret_cast<const uint16_t*>(p.k_new) + ((int64_t)s * p.num_kv_heads + g) * D;
-    const uint16_t* vn = reinterpret_cast<const uint16_t*>(p.v_new) + ((int64_t)s * p.num_kv_heads + g) * D;
-    if constexpr (FP8) {
-      const float ks = p.k_scale[g], vs = p.v_scale[g];
+  if (FP8 && nr.mine) {
+    const float ks = p.k_scale[g], vs = p.v_scale[g];
 #pragma unroll
-      for (int c = 0; c < D / 64; ++c) {
-        const uint2 a = quantize8_bf16(load16(kn + qg * (D / 4) + 16 * c), ks);
-        const uint2 b = quantize8_bf16(load16(kn + qg * (D / 4) + 16 * c + 8), ks);
-        nk8[c] = make_uint4(a.x, a.y, b.x, b.y);
-      }
-      if constexpr (EPL == 8) {
-        nv8 = quantize8_bf16(load16(vn + EPL * n), vs);
-      } else {
-        const uint2 h = load8(vn + EPL * n);
-        const float x[4] = {bf16_lo(h.x), bf16_hi(h.x), bf16_lo(h.y), bf16_hi(h.y)};
-        nv8 = make_uint2(quantize4(x, vs), 0u);
-      }
+    for (int c = 0; c < D / 64; ++c) {
+      const uint2 a = quantize8_bf16(nkr[2 * c], ks);
+      const uint2 b = quantize8_bf16(nkr[2 * c + 1], ks);
+      nk8[c] = make_uint4(a.x, a.y, b.x, b.y);
+    }
+    if constexpr (EPL == 8) {
+      nv8 = quantize8_bf16(nvr, vs);
     } else {
-#pragma unroll
-      for (int c = 0; c < KCH; ++c) nk[c] = load16(kn + 8 * qg + 32 * c);
-      if constexpr (EPL == 8) {
-        nv = load16(vn + EPL * n);
-      } else {
-        const uint2 h = load8(vn + EPL * n);
-        nv = make_uint4(h.x, h.y, 0, 0);
-      }
+      const float x[4] = {bf16_lo(nvr.x), bf16_hi(nvr.x), bf16_lo(nvr.y), bf16_hi(nvr.y)};
+      nv8 = make_uint2(quantize4(x, vs), 0u);
     }
   }
 
@@ -691,7 +738,7 @@ void decode_mfma_kernel(DecodeParams p) {
         kq = make_uint4(lo.x, lo.y, hi.x, hi.y);
       } else {
         kq = t.k[c];
-        if (ov && n == rn) kq = nk[c];
+        if (ov && n == rn) kq = nkr[c];
       }
       sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bit_cast_to<bf16x8_t>(kq), qb[c], sc, 0, 0, 0);
     }
@@ -700,9 +747,10 @@ void decode_mfma_kernel(DecodeParams p) {
     float x[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) x[r] = (tokq + r < t1) ? sc[r] * logit_scale : neg_inf();
-    float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    mt = fmaxf(mt, shfl_xor_f(mt, 16));
-    mt = fmaxf(mt, shfl_xor_f(mt, 32));
+    // max over the tile's 16 tokens: the lane's four, then across the lane
+    // groups qg (row swaps, no LDS round trip); NaN-propagating
+    const float mt = max_across_rows(__builtin_elementwise_maximum(__builtin_elementwise_maximum(x[0], x[1]),
+                                                                   __builtin_elementwise_maximum(x[2], x[3])));
     if (__any(mt > m_ref + kRescaleThreshold)) {
       const float m_new = fmaxf(m_ref, mt);
       const float alpha = fast_exp2(m_ref - m_new);
@@ -741,7 +789,7 @@ void decode_mfma_kernel(DecodeParams p) {
         vd[st][3] = b.y;
       } else {
         uint4 v = t.v[st];
-        if (ov && 4 * qg + st == rn) v = nv;
+        if (ov && 4 * qg + st == rn) v = nvr;
         vd[st][0] = v.x;
         vd[st][1] = v.y;
         vd[st][2] = v.z;
@@ -772,7 +820,7 @@ void decode_mfma_kernel(DecodeParams p) {
     // size so every buffer index is a compile-time constant and no register
     // copy (which would wait on its pending load) is needed.
     Tile buf[kStages];
-    int blk_ahead = block_of(0);
+    int blk_ahead = start == 0 ? blk_first : block_of(0);
 #pragma unroll
     for (int i = 0; i < kStages - 1; ++i) {
       const int b = blk_ahead;
@@ -815,13 +863,13 @@ void decode_mfma_kernel(DecodeParams p) {
                    (int64_t)nr.slot * row_elems + g * D;
     if (n == 0) {   // lanes n == 0 (qg = 0..3) hold all K pieces of the row
 #pragma unroll
-      for (int c = 0; c < KCH; ++c) *reinterpret_cast<uint4*>(kd + 8 * qg + 32 * c) = nk[c];
+      for (int c = 0; c < KCH; ++c) *reinterpret_cast<uint4*>(kd + 8 * qg + 32 * c) = nkr[c];
     }
     if (qg == 0) {  // lanes qg == 0 (n = 0..15) hold all V columns
       if constexpr (EPL == 8) {
-        *reinterpret_cast<uint4*>(vd + EPL * n) = nv;
+        *reinterpret_cast<uint4*>(vd + EPL * n) = nvr;
       } else {
-        *reinterpret_cast<uint2*>(vd + EPL * n) = make_uint2(nv.x, nv.y);
+        *reinterpret_cast<uint2*>(vd + EPL * n) = make_uint2(nvr.x, nvr.y);
       }
     }
   }
@@ -1275,6 +1323,10 @@ void decode_balanced_kernel(DecodeParams p) {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+static bool decode_grid_fits(const DecodeParams& p) {
+  return (int64_t)p.num_seqs * p.num_kv_heads * p.num_partitions <= 0x7fffffff - kXcds;
+}
+
 static dim3 decode_grid(const DecodeParams& p) {
   const int64_t items = (int64_t)p.num_seqs * p.num_kv_heads * p.num_partitions;
   return dim3((unsigned)((items + kXcds - 1) / kXcds * kXcds));
@@ -1282,6 +1334,7 @@ static dim3 decode_grid(const DecodeParams& p) {
 
 template <typename T, int D>
 static hipError_t launch_valu_g(const DecodeParams& p, hipStream_t stream) {
+  if (!decode_grid_fits(p)) return hipErrorInvalidValue;
   const dim3 grid = decode_grid(p);
   switch (p.group) {
 #define PKV_G(GV) \
@@ -1299,15 +1352,21 @@ hipError_t launch_decode_valu(const DecodeParams& p, int head_dim, int dtype, hi
   return head_dim == 64 ? launch_valu_g<uint16_t, 64>(p, stream) : launch_valu_g<uint16_t, 128>(p, stream);
 }
 
+static int device_compute_units();
+
 template <int D, bool FP8>
 static hipError_t launch_mfma_d(const DecodeParams& p, hipStream_t stream) {
+  if (!decode_grid_fits(p)) return hipErrorInvalidValue;
   const dim3 grid = decode_grid(p);
+  DecodeParams q = p;
+  q.pair_span = (p.num_partitions == 1 && p.seq_prefix == nullptr && p.num_seqs <= kRankMaxSeqs)
+                    ? device_compute_units() : 0;
   if (p.group <= 4)
-    hipLaunchKernelGGL((decode_mfma_kernel<D, 4, FP8>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((decode_mfma_kernel<D, 4, FP8>), grid, dim3(kThreads), 0, stream, q);
   else if (p.group <= 8)
-    hipLaunchKernelGGL((decode_mfma_kernel<D, 8, FP8>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((decode_mfma_kernel<D, 8, FP8>), grid, dim3(kThreads), 0, stream, q);
   else
-    hipLaunchKernelGGL((decode_mfma_kernel<D, 16, FP8>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((decode_mfma_kernel<D, 16, FP8>), grid, dim3(kThreads), 0, stream, q);
   return hipGetLastError();
 }
 

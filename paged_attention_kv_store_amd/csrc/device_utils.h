@@ -97,4 +97,85 @@ __device__ __forceinline__ uint2 quantize8_bf16(const uint4& v, float s) {
   return make_uint2(quantize4(x, s), quantize4(x + 4, s));
 }
 
+// ---- items in order of cost ------------------------------------------------
+// The item of the given rank when items 0 .. n_items-1 are ordered by cost,
+// highest first, ties by index; -1 past the last rank. cost_of(j) is an
+// integer in [0, kBuckets). Called by the whole workgroup of kThreads
+// threads (rank and n_items workgroup-uniform): a histogram of the costs in
+// LDS gives the cost of the rank and its place among the items of that
+// cost, then a scan in index order picks the item. hist (kBuckets ints) and
+// cost (n_items entries) are LDS the caller does not use again until after
+// the barrier this ends with. O(n_items / kThreads) per thread.
+template <int kThreads, int kBuckets, typename CostFn>
+__device__ int item_of_rank(int rank, int n_items, CostFn cost_of, int* hist, uint16_t* cost) {
+  static_assert(kBuckets % kThreads == 0 && kThreads % 64 == 0, "bucket split");
+  constexpr int kWaves = kThreads / 64;
+  constexpr int kPerThread = kBuckets / kThreads;
+  __shared__ int s_wave[kWaves];
+  __shared__ int s_pick[2];
+  if (rank >= n_items) return -1;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int i = tid; i < kBuckets; i += kThreads) hist[i] = 0;
+  __syncthreads();
+  for (int j = tid; j < n_items; j += kThreads) {
+    const int b = cost_of(j);
+    cost[j] = (uint16_t)b;
+    atomicAdd(&hist[b], 1);
+  }
+  __syncthreads();
+  // items in this thread's buckets, and in all higher buckets (a suffix sum
+  // over threads: lanes above within the wave, then the waves above)
+  int mine = 0;
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) mine += hist[kPerThread * tid + i];
+  int suffix = mine;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int x = __shfl_down(suffix, d, 64);
+    if (lane + d < 64) suffix += x;
+  }
+  if (lane == 0) s_wave[w] = suffix;
+  __syncthreads();
+  int above = suffix - mine;
+  for (int v = w + 1; v < kWaves; ++v) above += s_wave[v];
+  if (above <= rank && rank < above + mine) {
+    for (int i = kPerThread - 1; i >= 0; --i) {
+      const int cnt = hist[kPerThread * tid + i];
+      if (rank < above + cnt) {
+        s_pick[0] = kPerThread * tid + i;
+        s_pick[1] = rank - above;
+        break;
+      }
+      above += cnt;
+    }
+  }
+  __syncthreads();
+  // the k-th item (in index order) of the chosen bucket
+  const int bucket = s_pick[0];
+  int k = s_pick[1];
+  int item = -1;
+  for (int base = 0; base < n_items; base += kThreads) {
+    const int j = base + tid;
+    const bool hit = j < n_items && cost[j] == bucket;
+    const uint64_t mask = __ballot(hit);
+    __syncthreads();                        // s_wave of the previous pass is read
+    if (lane == 0) s_wave[w] = __popcll(mask);
+    __syncthreads();
+    int before = 0, total = 0;
+    for (int v = 0; v < kWaves; ++v) {
+      before += v < w ? s_wave[v] : 0;
+      total += s_wave[v];
+    }
+    if (k < total) {
+      if (hit && before + __popcll(mask & ((1ull << lane) - 1)) == k) s_pick[0] = j;
+      __syncthreads();
+      item = s_pick[0];
+      break;
+    }
+    k -= total;
+  }
+  __syncthreads();                          // hist, cost and s_pick are free again
+  return item;
+}
+
 }  // namespace pkv

@@ -68,82 +68,6 @@ __device__ __forceinline__ int item_cost(const PrefillParams& p, int j) {
   return min(1 + (kv_end + kKvTile - 1) / kKvTile, kOrderBuckets - 1);
 }
 
-// The (chunk, q-tile) item j = chunk * num_q_tiles + q-tile of the given
-// rank when items are ordered by cost, highest first, ties by j; -1 past the
-// last rank. Whole workgroup; hist (kOrderBuckets ints) and cost
-// (kOrderMaxItems entries) are LDS the caller does not use until after the
-// barrier this ends with.
-template <int BQ>
-__device__ int longest_first_item(const PrefillParams& p, int rank, int* hist, uint16_t* cost) {
-  constexpr int kPerThread = kOrderBuckets / kPThreads;   // 16 buckets per thread
-  __shared__ int s_wave[kPW];
-  __shared__ int s_pick[2];
-  const int n_items = p.num_q_tiles * p.num_seqs;
-  if (rank >= n_items) return -1;                           // workgroup-uniform
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  for (int i = tid; i < kOrderBuckets; i += kPThreads) hist[i] = 0;
-  __syncthreads();
-  for (int j = tid; j < n_items; j += kPThreads) {
-    const int b = item_cost<BQ>(p, j);
-    cost[j] = (uint16_t)b;
-    atomicAdd(&hist[b], 1);
-  }
-  __syncthreads();
-  // items in this thread's buckets, and in all higher buckets (a suffix sum
-  // over threads: lanes above within the wave, then the waves above)
-  int mine = 0;
-#pragma unroll
-  for (int i = 0; i < kPerThread; ++i) mine += hist[kPerThread * tid + i];
-  int suffix = mine;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int x = __shfl_down(suffix, d, 64);
-    if (lane + d < 64) suffix += x;
-  }
-  if (lane == 0) s_wave[w] = suffix;
-  __syncthreads();
-  int above = suffix - mine;
-  for (int v = w + 1; v < kPW; ++v) above += s_wave[v];
-  if (above <= rank && rank < above + mine) {
-    for (int i = kPerThread - 1; i >= 0; --i) {
-      const int cnt = hist[kPerThread * tid + i];
-      if (rank < above + cnt) {
-        s_pick[0] = kPerThread * tid + i;
-        s_pick[1] = rank - above;
-        break;
-      }
-      above += cnt;
-    }
-  }
-  __syncthreads();
-  // the k-th item (in index order) of the chosen bucket
-  const int bucket = s_pick[0];
-  int k = s_pick[1];
-  int item = -1;
-  for (int base = 0; base < n_items; base += kPThreads) {
-    const int j = base + tid;
-    const bool hit = j < n_items && cost[j] == bucket;
-    const uint64_t mask = __ballot(hit);
-    __syncthreads();                        // s_wave of the previous pass is read
-    if (lane == 0) s_wave[w] = __popcll(mask);
-    __syncthreads();
-    int before = 0, total = 0;
-    for (int v = 0; v < kPW; ++v) {
-      before += v < w ? s_wave[v] : 0;
-      total += s_wave[v];
-    }
-    if (k < total) {
-      if (hit && before + __popcll(mask & ((1ull << lane) - 1)) == k) s_pick[0] = j;
-      __syncthreads();
-      item = s_pick[0];
-      break;
-    }
-    k -= total;
-  }
-  __syncthreads();                          // hist, cost and s_pick are free again
-  return item;
-}
-
 }  // namespace
 
 template <int G>
@@ -171,8 +95,10 @@ void prefill_kernel(PrefillParams p) {
   int qt, c, g;
   if (p.longest_first) {
     g = blockIdx.x % p.num_kv_heads;
-    const int j = longest_first_item<BQ>(p, blockIdx.x / p.num_kv_heads, reinterpret_cast<int*>(s_v[1]),
-                                         reinterpret_cast<uint16_t*>(s_k[1]));
+    // (chunk, q-tile) item j = chunk * num_q_tiles + q-tile
+    const int j = item_of_rank<kPThreads, kOrderBuckets>(
+        blockIdx.x / p.num_kv_heads, nqt * p.num_seqs, [&](int i) { return item_cost<BQ>(p, i); },
+        reinterpret_cast<int*>(s_v[1]), reinterpret_cast<uint16_t*>(s_k[1]));
     if (j < 0) return;
     c = j / nqt;
     qt = j % nqt;
