@@ -47,7 +47,7 @@ def gpu_decode(batch: PagedBatch, dev=None, algo="auto", partition_size=0, store
     if store and batch.k_new is not None:
         pkv.kv_cache_store(dev["k_new"], dev["v_new"], dev["k_cache"], dev["v_cache"],
                            dev["slot_mapping"])
-    out = torch.empty_like(dev["q"])
+    out = torch.full_like(dev["q"], float("nan"))   # a row no workgroup writes stays NaN
     pkv.paged_attention_decode(out, dev["q"], dev["k_cache"], dev["v_cache"],
                                dev["block_tables"], dev["context_lens"], batch.scale,
                                batch.max_ctx, partition_size=partition_size, algo=algo)

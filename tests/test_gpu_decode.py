@@ -50,6 +50,20 @@ def test_random_sweep(case, partition):
     assert_close(got, oracle_decode(b), dtype, f"{algo} p={partition}")
 
 
+@pytest.mark.parametrize("num_seqs", [40, 70, 150])
+def test_items_handed_out_by_size(num_seqs):
+    """The single-pass kernel hands (sequence, kv-head) items to workgroups by
+    size, ties by index: between one and two items per compute unit (40 x 8),
+    more than two (70 x 8, 150 x 8), with short contexts so that most sizes
+    tie and some are empty. Every row must be written, and right."""
+    b = W.random_decode_batch(500 + num_seqs, num_seqs, 16, 8, 128, torch.bfloat16, max_ctx=70,
+                              min_ctx=0)
+    say(f"by size: S={num_seqs} ctx={b.pool.context_lens.tolist()}")
+    got = gpu_decode(b, algo="mfma", partition_size=0)
+    assert_close(got, oracle_decode(b), torch.bfloat16, f"S={num_seqs}")
+    assert (got[b.pool.context_lens == 0] == 0).all()
+
+
 @pytest.mark.parametrize("bs", [32, 64])
 @pytest.mark.parametrize("algo", ["valu", "mfma"])
 def test_larger_blocks(bs, algo):
