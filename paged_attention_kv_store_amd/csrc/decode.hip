@@ -258,27 +258,82 @@ __device__ __forceinline__ bool decode_item(const DecodeParams& p, int& g, int& 
 // Work item by size (single pass, no shared prefix). Two workgroups of this
 // kernel fit a compute unit, and with C units workgroup b and workgroup
 // b + C are placed on the same one (the dispatcher fills every unit once,
-// then again in the same order). Items are ranked by their 16-token tiles,
-// most first: workgroups 0 .. C-1 take ranks 0 .. C-1 and workgroups
-// C .. F-1 (F = min(items, 2C)) take ranks F-1 down to C, so each unit pairs
-// a long item with a short one; workgroups past F, started as earlier ones
-// finish, take the remaining ranks in order. Ranks are over sequences (all
-// kv-heads of a sequence are adjacent).
+// then again in the same order). Item x = sequence * kv_heads + kv-head;
+// its size is the sequence's 16-token tiles.
+//  * At most 2C items: workgroup b < C takes item b at once (no ranking on
+//    its path). Workgroup C + i, on the unit of item i, takes a second item
+//    from x >= C so that the two groups pair in opposite order of size: if
+//    item i is the r-th largest of the first C (r from 0), it takes the
+//    (C - 1 - r)-th largest of the rest, or none when there are not that
+//    many. The grid is then 2C workgroups.
+//  * More items: workgroup b < 2C takes the item of rank b < C, or of rank
+//    3C - 1 - b (the largest 2C items, each unit pairing a long one with a
+//    short one); workgroups past 2C, started as earlier ones finish, take the
+//    remaining ranks in order.
+// Ranks are by size, largest first, ties by item index (a histogram and a
+// selection scan in LDS; all kv-heads of a sequence are adjacent).
 constexpr int kRankBuckets = 2048;     // tiles per sequence, capped
 constexpr int kRankMaxSeqs = 4096;
-__device__ __forceinline__ bool ranked_item(const DecodeParams& p, int& g, int& s, int* hist, uint16_t* cost) {
+
+__device__ __forceinline__ int item_tiles(const DecodeParams& p, int x) {
+  const int c = clamp_ctx(p.context_lens[x / p.num_kv_heads], p.max_ctx);
+  return min((c + kTile - 1) / kTile, kRankBuckets - 1);
+}
+
+// Rank of item i among items 0 .. n-1 (largest first, ties by index).
+__device__ __forceinline__ int rank_among(const DecodeParams& p, int i, int n, int* s_sum) {
+  const int ti = item_tiles(p, i);
+  int cnt = 0;
+  for (int j = threadIdx.x; j < n; j += kThreads) {
+    const int tj = item_tiles(p, j);
+    cnt += (tj > ti || (tj == ti && j < i)) ? 1 : 0;
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) cnt += __shfl_xor(cnt, d, 64);
+  if ((threadIdx.x & 63) == 0) s_sum[threadIdx.x >> 6] = cnt;
+  __syncthreads();
+  int r = 0;
+#pragma unroll
+  for (int v = 0; v < kWaves; ++v) r += s_sum[v];
+  __syncthreads();                        // s_sum is free again
+  return r;
+}
+
+__device__ __forceinline__ bool sized_item(const DecodeParams& p, int& g, int& s, int* hist, uint16_t* cost,
+                                           int* s_sum) {
   const int hkv = p.num_kv_heads;
-  const int n = p.num_seqs * hkv, c = p.pair_span, f = min(n, 2 * c);
+  const int n = p.num_seqs * hkv, c = p.pair_span;
   const int b = blockIdx.x;
-  const int r = b < c ? b : (b < f ? f - 1 - (b - c) : b);
-  if (r >= n) return false;                  // workgroup-uniform
-  const int q = r / hkv;
-  g = r - q * hkv;
-  s = item_of_rank<kThreads, kRankBuckets>(
-      q, p.num_seqs,
-      [&](int i) { return min((clamp_ctx(p.context_lens[i], p.max_ctx) + kTile - 1) / kTile, kRankBuckets - 1); },
-      hist, cost);
-  return s >= 0;
+  int x;
+  if (n <= 2 * c) {
+    if (b < c) {
+      if (b >= n) return false;
+      x = b;
+    } else {
+      const int m = n - c;               // items of the second group
+      if (m <= 0) return false;
+      const int k = c - 1 - rank_among(p, b - c, c, s_sum);
+      if (k >= m) return false;          // workgroup-uniform
+      const int j = item_of_rank<kThreads, kRankBuckets>(
+          k, m, [&](int i) { return item_tiles(p, c + i); }, hist, cost);
+      if (j < 0) return false;
+      x = c + j;
+    }
+  } else {
+    const int f = 2 * c;
+    const int r = b < c ? b : (b < f ? 3 * c - 1 - b : b);
+    if (r >= n) return false;
+    const int q = r / hkv;
+    const int sq = item_of_rank<kThreads, kRankBuckets>(
+        q, p.num_seqs,
+        [&](int i) { return min((clamp_ctx(p.context_lens[i], p.max_ctx) + kTile - 1) / kTile, kRankBuckets - 1); },
+        hist, cost);
+    if (sq < 0) return false;
+    x = sq * hkv + (r - q * hkv);
+  }
+  s = x / hkv;
+  g = x - s * hkv;
+  return true;
 }
 
 // ---------------------------------------------------------------------------
@@ -550,10 +605,11 @@ void decode_mfma_kernel(DecodeParams p) {
   __shared__ int s_poison;
   __shared__ int s_rank_hist[kRankBuckets];
   __shared__ uint16_t s_rank_cost[kRankMaxSeqs];
+  __shared__ int s_rank_sum[kWaves];
 
   int g, part = 0, s;
   if (p.pair_span > 0) {
-    if (!ranked_item(p, g, s, s_rank_hist, s_rank_cost)) return;
+    if (!sized_item(p, g, s, s_rank_hist, s_rank_cost, s_rank_sum)) return;
   } else if (!decode_item(p, g, part, s)) {
     return;
   }
@@ -1357,10 +1413,15 @@ static int device_compute_units();
 template <int D, bool FP8>
 static hipError_t launch_mfma_d(const DecodeParams& p, hipStream_t stream) {
   if (!decode_grid_fits(p)) return hipErrorInvalidValue;
-  const dim3 grid = decode_grid(p);
+  dim3 grid = decode_grid(p);
   DecodeParams q = p;
-  q.pair_span = (p.num_partitions == 1 && p.seq_prefix == nullptr && p.num_seqs <= kRankMaxSeqs)
-                    ? device_compute_units() : 0;
+  const int cus = device_compute_units();
+  q.pair_span = (p.num_partitions == 1 && p.seq_prefix == nullptr && p.num_seqs <= kRankMaxSeqs &&
+                 cus <= kRankMaxSeqs)
+                    ? cus : 0;
+  const int64_t items = (int64_t)p.num_seqs * p.num_kv_heads;
+  if (q.pair_span > 0 && items > q.pair_span && items <= 2 * (int64_t)q.pair_span)
+    grid = dim3((unsigned)(2 * q.pair_span));   // a second workgroup on every unit
   if (p.group <= 4)
     hipLaunchKernelGGL((decode_mfma_kernel<D, 4, FP8>), grid, dim3(kThreads), 0, stream, q);
   else if (p.group <= 8)
