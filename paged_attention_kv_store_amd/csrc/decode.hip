@@ -275,17 +275,21 @@ __device__ __forceinline__ bool decode_item(const DecodeParams& p, int& g, int& 
 constexpr int kRankBuckets = 2048;     // tiles per sequence, capped
 constexpr int kRankMaxSeqs = 4096;
 
-__device__ __forceinline__ int item_tiles(const DecodeParams& p, int x) {
-  const int c = clamp_ctx(p.context_lens[x / p.num_kv_heads], p.max_ctx);
-  return min((c + kTile - 1) / kTile, kRankBuckets - 1);
+// Tiles of every sequence (capped), staged in LDS once per ranking workgroup.
+__device__ __forceinline__ void stage_tiles(const DecodeParams& p, uint16_t* tiles) {
+  for (int i = threadIdx.x; i < p.num_seqs; i += kThreads) {
+    const int c = clamp_ctx(p.context_lens[i], p.max_ctx);
+    tiles[i] = (uint16_t)min((c + kTile - 1) / kTile, kRankBuckets - 1);
+  }
+  __syncthreads();
 }
 
 // Rank of item i among items 0 .. n-1 (largest first, ties by index).
-__device__ __forceinline__ int rank_among(const DecodeParams& p, int i, int n, int* s_sum) {
-  const int ti = item_tiles(p, i);
+__device__ __forceinline__ int rank_among(int i, int n, int hkv, const uint16_t* tiles, int* s_sum) {
+  const int ti = tiles[i / hkv];
   int cnt = 0;
   for (int j = threadIdx.x; j < n; j += kThreads) {
-    const int tj = item_tiles(p, j);
+    const int tj = tiles[j / hkv];
     cnt += (tj > ti || (tj == ti && j < i)) ? 1 : 0;
   }
 #pragma unroll
@@ -300,7 +304,7 @@ __device__ __forceinline__ int rank_among(const DecodeParams& p, int i, int n, i
 }
 
 __device__ __forceinline__ bool sized_item(const DecodeParams& p, int& g, int& s, int* hist, uint16_t* cost,
-                                           int* s_sum) {
+                                           uint16_t* tiles, int* s_sum) {
   const int hkv = p.num_kv_heads;
   const int n = p.num_seqs * hkv, c = p.pair_span;
   const int b = blockIdx.x;
@@ -312,10 +316,11 @@ __device__ __forceinline__ bool sized_item(const DecodeParams& p, int& g, int& s
     } else {
       const int m = n - c;               // items of the second group
       if (m <= 0) return false;
-      const int k = c - 1 - rank_among(p, b - c, c, s_sum);
+      stage_tiles(p, tiles);
+      const int k = c - 1 - rank_among(b - c, c, hkv, tiles, s_sum);
       if (k >= m) return false;          // workgroup-uniform
       const int j = item_of_rank<kThreads, kRankBuckets>(
-          k, m, [&](int i) { return item_tiles(p, c + i); }, hist, cost);
+          k, m, [&](int i) { return (int)tiles[(c + i) / hkv]; }, hist, cost);
       if (j < 0) return false;
       x = c + j;
     }
@@ -323,11 +328,10 @@ __device__ __forceinline__ bool sized_item(const DecodeParams& p, int& g, int& s
     const int f = 2 * c;
     const int r = b < c ? b : (b < f ? 3 * c - 1 - b : b);
     if (r >= n) return false;
+    stage_tiles(p, tiles);
     const int q = r / hkv;
     const int sq = item_of_rank<kThreads, kRankBuckets>(
-        q, p.num_seqs,
-        [&](int i) { return min((clamp_ctx(p.context_lens[i], p.max_ctx) + kTile - 1) / kTile, kRankBuckets - 1); },
-        hist, cost);
+        q, p.num_seqs, [&](int i) { return (int)tiles[i]; }, hist, cost);
     if (sq < 0) return false;
     x = sq * hkv + (r - q * hkv);
   }
@@ -605,11 +609,12 @@ void decode_mfma_kernel(DecodeParams p) {
   __shared__ int s_poison;
   __shared__ int s_rank_hist[kRankBuckets];
   __shared__ uint16_t s_rank_cost[kRankMaxSeqs];
+  __shared__ uint16_t s_rank_tiles[kRankMaxSeqs];
   __shared__ int s_rank_sum[kWaves];
 
   int g, part = 0, s;
   if (p.pair_span > 0) {
-    if (!sized_item(p, g, s, s_rank_hist, s_rank_cost, s_rank_sum)) return;
+    if (!sized_item(p, g, s, s_rank_hist, s_rank_cost, s_rank_tiles, s_rank_sum)) return;
   } else if (!decode_item(p, g, part, s)) {
     return;
   }
