@@ -631,7 +631,13 @@ void decode_mfma_kernel(DecodeParams p) {
   // pieces (fused store), the shared prefix, the q rows, and the block of
   // the wave's first tile as it is without a shared prefix (index kept
   // inside the table row; used only when it is the right entry).
+  // With several partitions most workgroups of short sequences have nothing
+  // to do; those leave before loading anything else.
   const int ctx_raw = p.context_lens[s];
+  if (p.num_partitions > 1 && p.seq_prefix == nullptr && part * P >= clamp_ctx(ctx_raw, p.max_ctx)) {
+    if (part == 0) write_zero_rows<uint16_t, D>(p, s, g);
+    return;
+  }
   const int slot_raw = p.new_slots != nullptr ? p.new_slots[s] : -1;
   const int prefix_raw = p.seq_prefix != nullptr ? p.seq_prefix[s] : 0;
   const int blk_first = bt[min((part * P + w * kTile) / bs, p.max_blocks - 1)];
