@@ -2,8 +2,10 @@
 //
 // Per-item kernels (decode_valu_kernel, decode_mfma_kernel):
 // one workgroup of 4 wavefronts per (kv-head, partition, sequence).
-// The grid is one-dimensional and decode_item maps a workgroup to its item.
-// It serves all G = Hq/Hkv q-heads that share the kv-head, so each K/V byte is
+// The grid is one-dimensional; decode_item maps a workgroup to its item in
+// index order, and sized_item (the single-pass matrix-core kernel) by item
+// size, so that the two workgroups sharing a compute unit pair a long item
+// with a short one. A workgroup serves all G = Hq/Hkv q-heads that share the kv-head, so each K/V byte is
 // read once for the whole group. The partition's tokens are cut into 16-token
 // tiles; wave w takes tiles w, w+4, w+8, ... Every tile lies inside one
 // physical block (block_size is a multiple of 16 and tiles start at multiples
