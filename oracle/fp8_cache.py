@@ -27,7 +27,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .paged_attention import attend_rows, kv_cache_store, to_f64
+from .paged_attention import attend_rows, kv_cache_store, paged_attention_prefill_chunk, to_f64
 
 __all__ = [
     "E4M3_MAX",
@@ -38,6 +38,7 @@ __all__ = [
     "kv_cache_store_fp8",
     "dequantize",
     "paged_attention_decode_fp8",
+    "paged_attention_prefill_chunk_fp8",
 ]
 
 E4M3_MAX = 448.0
@@ -124,3 +125,14 @@ def paged_attention_decode_fp8(q, k_cache, v_cache, k_scale, v_scale, block_tabl
             g = h // group
             out[s, h] = attend_rows(qf[s, h][None, :], keys[:, g], values[:, g], scale, [ctx])[0]
     return out
+
+
+def paged_attention_prefill_chunk_fp8(q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                                      cu_seqlens_q, context_lens, scale, block_size, causal=True):
+    """Chunked prefill over E4M3 caches: the caches are dequantised (code
+    value times the kv-head's scale) and the unquantised prefill definition
+    is applied to them unchanged (same chunk, position and mask rules)."""
+    kd = E4M3_TABLE[np.asarray(k_cache)] * np.asarray(k_scale, dtype=np.float64)[None, None, :, None]
+    vd = E4M3_TABLE[np.asarray(v_cache)] * np.asarray(v_scale, dtype=np.float64)[None, None, :, None]
+    return paged_attention_prefill_chunk(q, kd, vd, block_tables, cu_seqlens_q, context_lens, scale,
+                                         block_size, causal=causal)

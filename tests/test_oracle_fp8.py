@@ -129,8 +129,47 @@ def check_decode_is_dequantised_decode(mod, seed=5):
     assert (got[3] == 0).all()
 
 
+def _codes(rng, shape):
+    """Random finite E4M3 codes of both signs (never 0x7f / 0xff)."""
+    return (rng.integers(0, 0x7F, shape) | (rng.integers(0, 2, shape) << 7)).astype(np.uint8)
+
+
+def check_prefill_pins(mod, seed=9):
+    rng = np.random.default_rng(seed)
+    nb, bs, hkv, hq, d = 16, 4, 2, 4, 8
+    kc, vc = _codes(rng, (nb, bs, hkv, d)), _codes(rng, (nb, bs, hkv, d))
+    ks = np.array([0.04, 0.003], np.float32)
+    vs = np.array([0.02, 0.5], np.float32)
+    ctx = np.array([9, 14, 5])
+    rows = np.array([4, 1, 5])                       # the last chunk has no earlier tokens
+    cu = np.concatenate([[0], np.cumsum(rows)])
+    tables = np.stack([rng.permutation(nb)[:5] for _ in range(3)])
+    q = rng.normal(0, 1, (int(cu[-1]), hq, d))
+    got = mod.paged_attention_prefill_chunk_fp8(q, kc, vc, ks, vs, tables, cu, ctx, 0.4, bs)
+    # row i of a chunk is single-row decode over the first ctx - L + i + 1 keys
+    for c in range(3):
+        for i in range(rows[c]):
+            r = cu[c] + i
+            want = mod.paged_attention_decode_fp8(q[r:r + 1], kc, vc, ks, vs, tables[c:c + 1],
+                                                  np.array([ctx[c] - rows[c] + i + 1]), 0.4, bs)
+            np.testing.assert_allclose(got[r], want[0], rtol=0, atol=1e-12)
+    # non-causal: every row sees all ctx keys, so the last row is unchanged
+    nc = mod.paged_attention_prefill_chunk_fp8(q, kc, vc, ks, vs, tables, cu, ctx, 0.4, bs, causal=False)
+    for c in range(3):
+        np.testing.assert_allclose(nc[cu[c + 1] - 1], got[cu[c + 1] - 1], rtol=0, atol=1e-12)
+    # identical keys: the weights are uniform, the output is the mean of the visible V rows
+    kc_same = np.broadcast_to(kc[:1, :1], kc.shape).copy()
+    same = mod.paged_attention_prefill_chunk_fp8(q, kc_same, vc, ks, vs, tables, cu, ctx, 0.4, bs)
+    for i in range(rows[0]):
+        n_vis = ctx[0] - rows[0] + i + 1
+        pos = np.arange(n_vis)
+        vrows = mod.E4M3_TABLE[vc[tables[0][pos // bs], pos % bs]]      # [n_vis, hkv, d]
+        for h in range(hq):
+            np.testing.assert_allclose(same[i, h], vrows[:, h // 2].mean(0) * vs[h // 2], rtol=1e-12, atol=1e-15)
+
+
 CHECKS = [check_table, check_encode_matches_torch, check_encode_closed_forms, check_quantized_store,
-          check_decode_is_dequantised_decode]
+          check_decode_is_dequantised_decode, check_prefill_pins]
 
 
 @pytest.mark.parametrize("check", CHECKS, ids=lambda c: c.__name__)
@@ -155,6 +194,11 @@ MUTANTS = {
     "gather_row_from_block": ("kc[physical, positions % block_size]", "kc[physical, positions // block_size]"),
     "values_with_k_scale": ("dequantize(vc[physical, positions % block_size], v_scale)",
                             "dequantize(vc[physical, positions % block_size], k_scale)"),
+    "prefill_v_scaled_by_k": ("vd = E4M3_TABLE[np.asarray(v_cache)] * np.asarray(v_scale,",
+                              "vd = E4M3_TABLE[np.asarray(v_cache)] * np.asarray(k_scale,"),
+    "prefill_k_unscaled": ("kd = E4M3_TABLE[np.asarray(k_cache)] * np.asarray(k_scale, dtype=np.float64)[None, None, :, None]",
+                           "kd = E4M3_TABLE[np.asarray(k_cache)] * 1.0"),
+    "prefill_not_causal": ("block_size, causal=causal)", "block_size, causal=False)"),
 }
 
 
