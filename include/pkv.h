@@ -320,6 +320,29 @@ int pkv_paged_attention_prefill_chunk(void* out, const void* q, const void* k_ca
                                       int32_t head_dim, float scale, int32_t causal,
                                       pkv_dtype dtype, void* stream);
 
+/*
+ * paged_attention_prefill_chunk_fp8: paged_attention_prefill_chunk over E4M3
+ * caches (the format, scales and dequantisation of paged_attention_decode_fp8;
+ * cache rows as written by kv_cache_store_fp8). The quantised-model support
+ * of "A vLLM engine small enough to read in one sitting", section "Key
+ * highlights"; the attention is the chunked-prefill definition above applied
+ * to the dequantised rows.
+ *   q, out: bf16 [total_q, num_q_heads, head_dim]; k_cache, v_cache: uint8
+ *   codes [num_blocks, block_size, num_kv_heads, head_dim]; k_scale, v_scale:
+ *   float32 [num_kv_heads] on the device (a row's values are code * scale).
+ * Supported and errors as paged_attention_prefill_chunk, plus PKV_EINVAL for a
+ * null or misaligned scale pointer.
+ */
+int pkv_paged_attention_prefill_chunk_fp8(void* out, const void* q, const void* k_cache,
+                                          const void* v_cache, const float* k_scale,
+                                          const float* v_scale, const int32_t* block_tables,
+                                          const int32_t* cu_seqlens_q, const int32_t* context_lens,
+                                          int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                                          int32_t max_blocks_per_seq, int32_t max_context_len,
+                                          int32_t num_blocks, int32_t block_size, int32_t num_q_heads,
+                                          int32_t num_kv_heads, int32_t head_dim, float scale,
+                                          int32_t causal, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

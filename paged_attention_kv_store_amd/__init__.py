@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     DecodeStoreFp8Launch,
     DecodeStoreLaunch,
     PkvError,
+    PrefillFp8Launch,
     PrefillLaunch,
     SharedPrefixDecodeLaunch,
     StoreFp8Launch,
@@ -29,4 +30,5 @@ from .binding import (  # noqa: F401
     paged_attention_decode_store,
     paged_attention_decode_store_fp8,
     paged_attention_prefill_chunk,
+    paged_attention_prefill_chunk_fp8,
 )

@@ -54,6 +54,9 @@ _SIGNATURES = {
     "pkv_paged_attention_prefill_chunk": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                                            _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                            ctypes.c_float, _i32, ctypes.c_int, _vp], ctypes.c_int),
+    "pkv_paged_attention_prefill_chunk_fp8": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                               _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                               ctypes.c_float, _i32, _vp], ctypes.c_int),
 }
 
 
@@ -332,6 +335,37 @@ class DecodeLaunch(_Prepared):
                       _dtype_code(q), DECODE_ALGOS[algo])
 
 
+def _prefill_args(out, q, k_cache, v_cache, block_tables, cu_seqlens_q, context_lens):
+    """Checks shared by the prefill entry points; returns (n, Tq, Hq, D, NB, bs, Hkv)."""
+    _dev(out, q, k_cache, v_cache, block_tables, cu_seqlens_q, context_lens)
+    _need(q.dim() == 3 and out.shape == q.shape and out.dtype == q.dtype, "q/out must be [Tq, Hq, D]")
+    _need(k_cache.dim() == 4 and v_cache.shape == k_cache.shape, "caches must be [NB, bs, Hkv, D]")
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2, "block_tables must be int32")
+    n = block_tables.shape[0]
+    _need(cu_seqlens_q.dtype == torch.int32 and cu_seqlens_q.shape == (n + 1,),
+          "cu_seqlens_q must be int32 [S+1]")
+    _need(context_lens.dtype == torch.int32 and context_lens.shape == (n,),
+          "context_lens must be int32 [S]")
+    return (n,) + tuple(q.shape) + tuple(k_cache.shape[:3])
+
+
+def paged_attention_prefill_chunk_fp8(out, q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                                      cu_seqlens_q, context_lens, scale, max_q_len, max_context_len,
+                                      causal=True, stream=None):
+    """Chunked prefill over E4M3 caches (uint8 [NB, bs, Hkv, D], scales float32
+    [Hkv]); bf16 q and out [Tq, Hq, D]."""
+    _check_fp8_cache(k_cache, v_cache, k_scale, v_scale)
+    _need(q.dtype == torch.bfloat16, "q must be bf16")
+    n, tq, hq, d, nb, bs, hkv = _prefill_args(out, q, k_cache, v_cache, block_tables, cu_seqlens_q,
+                                              context_lens)
+    _check(lib().pkv_paged_attention_prefill_chunk_fp8(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+        _ptr(block_tables), _ptr(cu_seqlens_q), _ptr(context_lens), n, tq, int(max_q_len),
+        block_tables.shape[1], int(max_context_len), nb, bs, hq, hkv, d, float(scale),
+        int(bool(causal)), _stream(stream)))
+    return out
+
+
 class PrefillLaunch(_Prepared):
     """paged_attention_prefill_chunk with fixed tensors."""
 
@@ -355,6 +389,24 @@ class PrefillLaunch(_Prepared):
                       _ptr(cu_seqlens_q), _ptr(context_lens), n, tq, int(max_q_len),
                       block_tables.shape[1], int(max_context_len), nb, bs, hq, hkv, d,
                       float(scale), int(bool(causal)), _dtype_code(q))
+
+
+class PrefillFp8Launch(_Prepared):
+    """paged_attention_prefill_chunk_fp8 with fixed tensors."""
+
+    def __init__(self, out, q, k_cache, v_cache, k_scale, v_scale, block_tables, cu_seqlens_q,
+                 context_lens, scale, max_q_len, max_context_len, causal=True):
+        _check_fp8_cache(k_cache, v_cache, k_scale, v_scale)
+        _need(q.dtype == torch.bfloat16, "q must be bf16")
+        n, tq, hq, d, nb, bs, hkv = _prefill_args(out, q, k_cache, v_cache, block_tables,
+                                                  cu_seqlens_q, context_lens)
+        self._keep = (out, q, k_cache, v_cache, k_scale, v_scale, block_tables, cu_seqlens_q,
+                      context_lens)
+        self._fn = "pkv_paged_attention_prefill_chunk_fp8"
+        self._args = (_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                      _ptr(block_tables), _ptr(cu_seqlens_q), _ptr(context_lens), n, tq, int(max_q_len),
+                      block_tables.shape[1], int(max_context_len), nb, bs, hq, hkv, d, float(scale),
+                      int(bool(causal)))
 
 
 class DecodeStoreLaunch(_Prepared):

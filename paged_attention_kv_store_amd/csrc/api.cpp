@@ -370,17 +370,12 @@ extern "C" int pkv_paged_attention_decode_store_fp8(
                      workspace_bytes, PKV_BF16, PKV_DECODE_MFMA, stream, true, k_scale, v_scale);
 }
 
-extern "C" int pkv_paged_attention_prefill_chunk(void* out, const void* q, const void* k_cache,
-                                                 const void* v_cache, const int32_t* block_tables,
-                                                 const int32_t* cu_seqlens_q,
-                                                 const int32_t* context_lens, int32_t num_seqs,
-                                                 int32_t total_q, int32_t max_q_len,
-                                                 int32_t max_blocks_per_seq, int32_t max_context_len,
-                                                 int32_t num_blocks, int32_t block_size,
-                                                 int32_t num_q_heads, int32_t num_kv_heads,
-                                                 int32_t head_dim, float scale, int32_t causal,
-                                                 pkv_dtype dtype, void* stream) {
-  const char* fn = "pkv_paged_attention_prefill_chunk";
+static int prefill_impl(const char* fn, void* out, const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* block_tables, const int32_t* cu_seqlens_q, const int32_t* context_lens,
+                        int32_t num_seqs, int32_t total_q, int32_t max_q_len, int32_t max_blocks_per_seq,
+                        int32_t max_context_len, int32_t num_blocks, int32_t block_size, int32_t num_q_heads,
+                        int32_t num_kv_heads, int32_t head_dim, float scale, int32_t causal, pkv_dtype dtype,
+                        bool fp8, const float* k_scale, const float* v_scale, void* stream) {
   if (num_seqs < 0 || total_q < 0 || max_q_len < 0)
     return fail(PKV_EINVAL, "%s: negative size", fn);
   if (int rc = check_common(fn, num_blocks, block_size, num_kv_heads, head_dim, dtype)) return rc;
@@ -388,13 +383,14 @@ extern "C" int pkv_paged_attention_prefill_chunk(void* out, const void* q, const
     return fail(PKV_EINVAL, "%s: num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)", fn,
                 num_q_heads, num_kv_heads);
   const int group = num_q_heads / num_kv_heads;
-  if (dtype != PKV_BF16) return fail(PKV_EUNSUPPORTED, "%s: prefill supports bf16 only", fn);
+  if (dtype != PKV_BF16)
+    return fail(PKV_EUNSUPPORTED, fp8 ? "%s: q and out must be bf16" : "%s: prefill supports bf16 only", fn);
   if (head_dim != 128) return fail(PKV_EUNSUPPORTED, "%s: prefill supports head_dim 128 only", fn);
   if (group != 1 && group != 2 && group != 4 && group != 8)
     return fail(PKV_EUNSUPPORTED, "%s: GQA group %d not in {1, 2, 4, 8}", fn, group);
   if (block_size < 16 || block_size > 256 || (block_size & (block_size - 1)) != 0)
     return fail(PKV_EUNSUPPORTED, "%s: block_size %d must be a power of two in [16, 256]", fn, block_size);
-  if ((int64_t)block_size * num_kv_heads * head_dim * 2 >= ((int64_t)1 << 31))
+  if ((int64_t)block_size * num_kv_heads * head_dim * (fp8 ? 1 : 2) >= ((int64_t)1 << 31))
     return fail(PKV_EUNSUPPORTED, "%s: a cache block must be under 2 GiB", fn);
   if (max_blocks_per_seq <= 0) return fail(PKV_EINVAL, "%s: max_blocks_per_seq must be positive", fn);
   if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
@@ -406,9 +402,11 @@ extern "C" int pkv_paged_attention_prefill_chunk(void* out, const void* q, const
   if (num_seqs == 0 || total_q == 0 || max_q_len == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !cu_seqlens_q || !context_lens)
     return fail(PKV_EINVAL, "%s: null pointer", fn);
+  if (fp8 && (!k_scale || !v_scale)) return fail(PKV_EINVAL, "%s: null scale pointer", fn);
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
-      !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(cu_seqlens_q, 4))
-    return fail(PKV_EINVAL, "%s: q, out and caches must be 16-byte aligned; index arrays 4-byte", fn);
+      !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(cu_seqlens_q, 4) ||
+      (fp8 && (!aligned(k_scale, 4) || !aligned(v_scale, 4))))
+    return fail(PKV_EINVAL, "%s: q, out and caches must be 16-byte aligned; index arrays and scales 4-byte", fn);
   pkv::PrefillParams p;
   p.out = out;
   p.q = q;
@@ -433,7 +431,43 @@ extern "C" int pkv_paged_attention_prefill_chunk(void* out, const void* q, const
   p.table_row_is_first_q = 0;
   p.part_m = p.part_l = p.part_o = nullptr;
   p.seq_prefix = nullptr;
-  return hip_status(pkv::launch_prefill(p, head_dim, (hipStream_t)stream), fn);
+  p.k_scale = fp8 ? k_scale : nullptr;
+  p.v_scale = fp8 ? v_scale : nullptr;
+  const hipStream_t st = (hipStream_t)stream;
+  return hip_status(fp8 ? pkv::launch_prefill_fp8(p, head_dim, st) : pkv::launch_prefill(p, head_dim, st), fn);
+}
+
+extern "C" int pkv_paged_attention_prefill_chunk(void* out, const void* q, const void* k_cache,
+                                                 const void* v_cache, const int32_t* block_tables,
+                                                 const int32_t* cu_seqlens_q,
+                                                 const int32_t* context_lens, int32_t num_seqs,
+                                                 int32_t total_q, int32_t max_q_len,
+                                                 int32_t max_blocks_per_seq, int32_t max_context_len,
+                                                 int32_t num_blocks, int32_t block_size,
+                                                 int32_t num_q_heads, int32_t num_kv_heads,
+                                                 int32_t head_dim, float scale, int32_t causal,
+                                                 pkv_dtype dtype, void* stream) {
+  return prefill_impl("pkv_paged_attention_prefill_chunk", out, q, k_cache, v_cache, block_tables,
+                      cu_seqlens_q, context_lens, num_seqs, total_q, max_q_len, max_blocks_per_seq,
+                      max_context_len, num_blocks, block_size, num_q_heads, num_kv_heads, head_dim, scale,
+                      causal, dtype, false, nullptr, nullptr, stream);
+}
+
+extern "C" int pkv_paged_attention_prefill_chunk_fp8(void* out, const void* q, const void* k_cache,
+                                                     const void* v_cache, const float* k_scale,
+                                                     const float* v_scale, const int32_t* block_tables,
+                                                     const int32_t* cu_seqlens_q,
+                                                     const int32_t* context_lens, int32_t num_seqs,
+                                                     int32_t total_q, int32_t max_q_len,
+                                                     int32_t max_blocks_per_seq, int32_t max_context_len,
+                                                     int32_t num_blocks, int32_t block_size,
+                                                     int32_t num_q_heads, int32_t num_kv_heads,
+                                                     int32_t head_dim, float scale, int32_t causal,
+                                                     void* stream) {
+  return prefill_impl("pkv_paged_attention_prefill_chunk_fp8", out, q, k_cache, v_cache, block_tables,
+                      cu_seqlens_q, context_lens, num_seqs, total_q, max_q_len, max_blocks_per_seq,
+                      max_context_len, num_blocks, block_size, num_q_heads, num_kv_heads, head_dim, scale,
+                      causal, PKV_BF16, true, k_scale, v_scale, stream);
 }
 
 extern "C" size_t pkv_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_q_heads,
@@ -524,6 +558,7 @@ extern "C" int pkv_paged_attention_decode_shared_prefix(
   a.part_l = part_l;
   a.part_o = part_o;
   a.seq_prefix = seq_prefix;
+  a.k_scale = a.v_scale = nullptr;
   if (hipError_t e = pkv::launch_prefill(a, head_dim, st); e != hipSuccess) return hip_status(e, fn);
 
   // second pass: each sequence's own tokens, merged with its prefix partials

@@ -143,6 +143,9 @@ struct PrefillParams {
   float* part_l;
   float* part_o;             // [total_q, num_q_heads, head_dim]
   int32_t* seq_prefix;       // [total_q]
+  // E4M3 caches only (null otherwise): dequantisation scales [num_kv_heads].
+  const float* k_scale;
+  const float* v_scale;
 };
 
 // dtype codes match pkv_dtype
@@ -153,5 +156,6 @@ hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, hipStream_t s
 hipError_t launch_decode_mfma_fp8(const DecodeParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_decode_balanced(const DecodeParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_prefill_fp8(const PrefillParams& p, int head_dim, hipStream_t stream);
 
 }  // namespace pkv

@@ -581,13 +581,6 @@ struct MfmaTile<D, true> {
   uint2 v[4];                          // EPL bytes of each V row (D = 64: .x only)
 };
 
-// Two bf16 words holding the exact values of the four E4M3 codes of w.
-__device__ __forceinline__ uint2 e4m3x4_to_bf16(uint32_t w) {
-  const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-  const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
-  return make_uint2(pack_bf16x2(lo.x, lo.y), pack_bf16x2(hi.x, hi.y));
-}
-
 __device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }

@@ -26,6 +26,13 @@
 //    two 16-key tiles are already laid out as the A operand (8 keys per
 //    lane); the B operand (the same 8 keys of one column per lane) comes from
 //    whole V rows read from LDS with four in-lane byte permutes.
+//
+// E4M3 caches (FP8 = true): the same kernel with a register-staged gather:
+// each lane fetches 16 codes of a row, and once they have landed converts
+// them exactly to bf16 (every E4M3 value is a bf16 value) and writes them
+// into the same swizzled bf16 LDS tile, so the matrix work is unchanged. The
+// kv-head's K scale is folded into the logit multiplier and its V scale into
+// the final normalisation.
 #include "common.h"
 #include "device_utils.h"
 
@@ -70,7 +77,7 @@ __device__ __forceinline__ int item_cost(const PrefillParams& p, int j) {
 
 }  // namespace
 
-template <int G>
+template <int G, bool FP8>
 __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(PrefillParams p) {
   constexpr int BQ = kMRows / G;      // query rows per workgroup
@@ -132,8 +139,11 @@ void prefill_kernel(PrefillParams p) {
   // scaled ones. A zero scale is taken as the smallest normal float: every
   // weight 2^(FLT_MIN * x - m) then rounds to exactly what scale 0 gives,
   // and a masked -inf score still yields weight 0 rather than NaN.
-  const float scale = fmaxf(fabsf(p.scale_log2), __FLT_MIN__);
-  const uint32_t qsign = p.scale_log2 < 0.f ? 0x80008000u : 0u;
+  // (E4M3: the multiplier includes the kv-head's K scale; a NaN one stays
+  // NaN, as the dequantised definition gives NaN rows then.)
+  const float eff = FP8 ? p.scale_log2 * p.k_scale[g] : p.scale_log2;
+  const float scale = (eff != eff) ? eff : fmaxf(fabsf(eff), __FLT_MIN__);
+  const uint32_t qsign = eff < 0.f ? 0x80008000u : 0u;
 
   // ---- the wave's Q rows (B operand of S^T = K Q^T) ----------------------
   // tile t, lane l: M row mr = 32w + 16t + l%16 (query row r0 + mr/G, head
@@ -202,7 +212,45 @@ void prefill_kernel(PrefillParams p) {
           (void __attribute__((address_space(3)))*)(&s_v[buf][lds_pos]), 16, 0, 0);
     }
   };
-  // all of this thread's direct-to-LDS loads have landed (vmcnt 0)
+  // E4M3 caches: wave w fetches rows 16w .. 16w+15 of a tile (one block);
+  // lane l of slot i takes codes 16c .. 16c+15 (c = l % 8) of row
+  // t = 16w + 8i + l/8 into registers, and once they have landed writes
+  // them as bf16 pieces 2c and 2c+1 of row t at their swizzled places.
+  const char* kbase8 = reinterpret_cast<const char*>(p.k_cache) + g * kD;
+  const char* vbase8 = reinterpret_cast<const char*>(p.v_cache) + g * kD;
+  uint4 st_k[2], st_v[2];
+  auto gather8 = [&](int kt, const int (&ids)[4]) {
+    const int kv0 = kt * kKvTile;
+    int blk = w == 0 ? ids[0] : w == 1 ? ids[1] : w == 2 ? ids[2] : ids[3];
+    if ((unsigned)blk >= (unsigned)p.num_blocks) {
+      blk = 0;
+      bad = true;
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int t = 16 * w + 8 * i + (lane >> 3);
+      const int pos = min(kv0 + t, ctx - 1);
+      const int64_t off = (((int64_t)blk << lbs) + (pos & (bs - 1))) * row_elems + (lane & 7) * 16;
+      st_k[i] = load16(kbase8 + off);
+      st_v[i] = load16(vbase8 + off);
+    }
+  };
+  auto store8 = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int t = 16 * w + 8 * i + (lane >> 3);
+      const int c = 2 * (lane & 7);
+      const uint2 k0 = e4m3x4_to_bf16(st_k[i].x), k1 = e4m3x4_to_bf16(st_k[i].y);
+      const uint2 k2 = e4m3x4_to_bf16(st_k[i].z), k3 = e4m3x4_to_bf16(st_k[i].w);
+      s_k[buf][swz_k(t, c)] = make_uint4(k0.x, k0.y, k1.x, k1.y);
+      s_k[buf][swz_k(t, c + 1)] = make_uint4(k2.x, k2.y, k3.x, k3.y);
+      const uint2 v0 = e4m3x4_to_bf16(st_v[i].x), v1 = e4m3x4_to_bf16(st_v[i].y);
+      const uint2 v2 = e4m3x4_to_bf16(st_v[i].z), v3 = e4m3x4_to_bf16(st_v[i].w);
+      s_v[buf][swz_v(t, c)] = make_uint4(v0.x, v0.y, v1.x, v1.y);
+      s_v[buf][swz_v(t, c + 1)] = make_uint4(v2.x, v2.y, v3.x, v3.y);
+    }
+  };
+  // all of this thread's loads (direct-to-LDS or staged) have landed (vmcnt 0)
   auto wait_loads = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };
 
   float m_ref[2] = {neg_inf(), neg_inf()};   // per softmax row (lane's n), scaled units
@@ -231,9 +279,11 @@ void prefill_kernel(PrefillParams p) {
     int ids0[4];
     tile_blocks(0, ids0);
     tile_blocks(1, ids_next);
-    gather(0, 0, ids0);
+    if constexpr (FP8) gather8(0, ids0);
+    else gather(0, 0, ids0);
   }
   wait_loads();
+  if (FP8 && n_kv > 0) store8(0);
   __syncthreads();
 
   for (int kt = 0; kt < n_kv; ++kt) {
@@ -241,7 +291,10 @@ void prefill_kernel(PrefillParams p) {
     const bool more = kt + 1 < n_kv;
     tile_blocks(kt + 2, ids_after);
     // the other buffer was last read before the previous barrier
-    if (more) gather(kt + 1, buf ^ 1, ids_next);
+    if (more) {
+      if constexpr (FP8) gather8(kt + 1, ids_next);
+      else gather(kt + 1, buf ^ 1, ids_next);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) ids_next[i] = ids_after[i];
     const int kv0 = kt * kKvTile;
@@ -344,6 +397,7 @@ void prefill_kernel(PrefillParams p) {
       else pv(std::false_type{});
     }
     wait_loads();
+    if (FP8 && more) store8(buf ^ 1);
     __syncthreads();
   }
 
@@ -352,6 +406,7 @@ void prefill_kernel(PrefillParams p) {
   if (bad) s_bad = 1;
   __syncthreads();
   const bool poisoned = s_bad != 0;
+  const float vsc = FP8 ? p.v_scale[g] : 1.f;   // E4M3: the kv-head's V scale
   if (p.part_m != nullptr) {
     // partials for a later merge: row 16t + 4qg + r's reference max sits in
     // the lane whose n is 4qg + r; sums are replicated over n
@@ -367,8 +422,10 @@ void prefill_kernel(PrefillParams p) {
         if (qi >= L) continue;
         const int64_t row = (int64_t)(q_start + qi) * p.num_q_heads + g * G + mr % G;
         float* po = p.part_o + row * kD + 8 * n;
-        *reinterpret_cast<float4*>(po) = make_float4(acc[t][0][r], acc[t][1][r], acc[t][2][r], acc[t][3][r]);
-        *reinterpret_cast<float4*>(po + 4) = make_float4(acc[t][4][r], acc[t][5][r], acc[t][6][r], acc[t][7][r]);
+        *reinterpret_cast<float4*>(po) = make_float4(acc[t][0][r] * vsc, acc[t][1][r] * vsc,
+                                                     acc[t][2][r] * vsc, acc[t][3][r] * vsc);
+        *reinterpret_cast<float4*>(po + 4) = make_float4(acc[t][4][r] * vsc, acc[t][5][r] * vsc,
+                                                         acc[t][6][r] * vsc, acc[t][7][r] * vsc);
         if (n == 0) {
           p.part_m[row] = m;
           p.part_l[row] = poisoned ? __builtin_nanf("") : lsum[t][r];
@@ -384,7 +441,7 @@ void prefill_kernel(PrefillParams p) {
       const int mr = 32 * w + 16 * t + 4 * qg + r;
       const int qi = r0 + mr / G;
       if (qi >= L) continue;
-      const float inv = poisoned ? __builtin_nanf("") : 1.f / lsum[t][r];
+      const float inv = poisoned ? __builtin_nanf("") : vsc / lsum[t][r];
       uint32_t o[4];
 #pragma unroll
       for (int h = 0; h < 4; ++h) o[h] = pack_bf16x2(acc[t][2 * h][r] * inv, acc[t][2 * h + 1][r] * inv);
@@ -395,7 +452,8 @@ void prefill_kernel(PrefillParams p) {
   }
 }
 
-hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t stream) {
+template <bool FP8>
+static hipError_t launch_prefill_t(const PrefillParams& p, int head_dim, hipStream_t stream) {
   if (head_dim != kD) return hipErrorInvalidValue;
   const int bq = kMRows / p.group;
   PrefillParams q = p;
@@ -405,13 +463,21 @@ hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t stre
   if (items > 0x7fffffff - kXcds) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((items + kXcds - 1) / kXcds * kXcds));
   switch (p.group) {
-    case 1: hipLaunchKernelGGL(prefill_kernel<1>, grid, dim3(kPThreads), 0, stream, q); break;
-    case 2: hipLaunchKernelGGL(prefill_kernel<2>, grid, dim3(kPThreads), 0, stream, q); break;
-    case 4: hipLaunchKernelGGL(prefill_kernel<4>, grid, dim3(kPThreads), 0, stream, q); break;
-    case 8: hipLaunchKernelGGL(prefill_kernel<8>, grid, dim3(kPThreads), 0, stream, q); break;
+    case 1: hipLaunchKernelGGL((prefill_kernel<1, FP8>), grid, dim3(kPThreads), 0, stream, q); break;
+    case 2: hipLaunchKernelGGL((prefill_kernel<2, FP8>), grid, dim3(kPThreads), 0, stream, q); break;
+    case 4: hipLaunchKernelGGL((prefill_kernel<4, FP8>), grid, dim3(kPThreads), 0, stream, q); break;
+    case 8: hipLaunchKernelGGL((prefill_kernel<8, FP8>), grid, dim3(kPThreads), 0, stream, q); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t stream) {
+  return launch_prefill_t<false>(p, head_dim, stream);
+}
+
+hipError_t launch_prefill_fp8(const PrefillParams& p, int head_dim, hipStream_t stream) {
+  return launch_prefill_t<true>(p, head_dim, stream);
 }
 
 }  // namespace pkv

@@ -459,6 +459,47 @@ def qwen3_decode_fp8(seed: int = 1, device="cpu", layers: int = 28) -> Workload:
                     notes=f"{layers} layers, E4M3 caches with per-kv-head scales")
 
 
+def random_prefill_batch_fp8(seed, num_chunks, num_q_heads, num_kv_heads, head_dim, max_rows,
+                             max_prior, min_rows=1, block_size=BLOCK_SIZE, device="cpu",
+                             scale=None) -> PagedBatch:
+    """random_prefill_batch with E4M3 caches (bf16 q and new rows)."""
+    (rng,) = _streams(seed, 1)
+    rows = rng.integers(min_rows, max_rows, size=num_chunks, endpoint=True).astype(np.int32)
+    prior = rng.integers(0, max_prior, size=num_chunks, endpoint=True).astype(np.int32)
+    ctx = (rows + prior).astype(np.int32)
+    pool = make_pool(rng, ctx, block_size=block_size, reserve=2)
+    slots = np.concatenate(
+        [_slots_of(pool, c, np.arange(prior[c], ctx[c]), block_size) for c in range(num_chunks)]
+        + [np.zeros(0, np.int32)]).astype(np.int32)
+    cu = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
+    batch = build_batch_fp8(pool, num_q_heads, num_kv_heads, head_dim, seed, 10, device,
+                            num_queries=int(cu[-1]), store_slots=slots, block_size=block_size,
+                            scale=scale)
+    batch.cu_seqlens_q = cu
+    return batch
+
+
+def mixed_prefill_fp8(seed: int = 4, device="cpu") -> PagedBatch:
+    """The mixed workload's prefill part (8 chunks x 512 rows after U{0..8192}
+    cached tokens, 32 q / 8 kv heads) over E4M3 caches: the same lengths and
+    tables as mixed(seed), its own draws of q, caches and new rows."""
+    (rng,) = _streams(seed, 1)
+    chunk = 512
+    prior = rng.integers(0, 8192, size=8, endpoint=True).astype(np.int32)
+    dctx = rng.integers(256, 4096, size=128, endpoint=True).astype(np.int32)
+    ctx = np.concatenate([prior + chunk, dctx]).astype(np.int32)
+    pool = make_pool(rng, ctx)
+    slots = np.concatenate([_slots_of(pool, c, np.arange(prior[c], prior[c] + chunk), BLOCK_SIZE)
+                            for c in range(8)]).astype(np.int32)
+    mb = int(-(-int(ctx[:8].max()) // BLOCK_SIZE))
+    pre_pool = Pool(pool.context_lens[:8].copy(), np.ascontiguousarray(pool.block_tables[:8, :mb]),
+                    pool.num_blocks, pool.used, pool.pad_block)
+    batch = build_batch_fp8(pre_pool, 32, 8, 128, seed, 11, device, num_queries=8 * chunk,
+                            store_slots=slots)
+    batch.cu_seqlens_q = np.arange(0, 8 * chunk + 1, chunk, dtype=np.int32)
+    return batch
+
+
 def random_prefill_batch(seed, num_chunks, num_q_heads, num_kv_heads, head_dim,
                          dtype, max_rows, max_prior, min_rows=1,
                          block_size=BLOCK_SIZE, device="cpu", scale=None) -> PagedBatch:

@@ -176,3 +176,103 @@ def test_decode_store_fused(case):
     assert_close(got[live], _oracle_decode(b, caches, seqs=live), torch.bfloat16, "fp8 fused")
     if b.pool.context_lens[3] > 0:
         assert np.isnan(got[3]).all()            # its newest row is a poisoned cache row
+
+
+# ---- chunked prefill over E4M3 caches ------------------------------------------
+
+def _gpu_prefill(b, d, causal=True):
+    pkv.kv_cache_store_fp8(d["k_new"], d["v_new"], d["k_cache"], d["v_cache"], d["slot_mapping"],
+                           d["k_scale"], d["v_scale"])
+    out = torch.full_like(d["q"], float("nan"))   # a row no workgroup writes stays NaN
+    cu = torch.as_tensor(b.cu_seqlens_q, device="cuda")
+    pkv.paged_attention_prefill_chunk_fp8(out, d["q"], d["k_cache"], d["v_cache"], d["k_scale"],
+                                          d["v_scale"], d["block_tables"], cu, d["context_lens"],
+                                          b.scale, int(np.diff(b.cu_seqlens_q).max()), b.max_ctx,
+                                          causal=causal)
+    torch.cuda.synchronize()
+    return out.float().cpu().double().numpy()
+
+
+def _oracle_prefill(b, caches, causal=True):
+    kc, vc = caches
+    return FP8.paged_attention_prefill_chunk_fp8(W.host_bits(b.q), kc, vc, W.host_bits(b.k_scale),
+                                                 W.host_bits(b.v_scale), b.pool.block_tables,
+                                                 b.cu_seqlens_q, b.pool.context_lens, b.scale,
+                                                 b.block_size, causal=causal)
+
+
+PREFILL = [
+    # (hq, hkv, chunks, max_rows, max_prior, block_size)
+    (32, 8, 3, 150, 300, 16),
+    (16, 8, 4, 70, 90, 16),
+    (8, 8, 2, 200, 20, 32),
+    (32, 4, 3, 40, 200, 64),
+    (8, 1, 2, 33, 64, 16),
+    (32, 8, 9, 4, 1500, 16),     # verification-sized chunks
+]
+
+
+@pytest.mark.parametrize("case", PREFILL, ids=lambda c: f"{c[0]}x{c[1]}-r{c[3]}-p{c[4]}-bs{c[5]}")
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_fp8_matches_oracle(case, causal):
+    hq, hkv, chunks, max_rows, max_prior, bs = case
+    b = W.random_prefill_batch_fp8(hq * 11 + max_rows + bs, chunks, hq, hkv, 128, max_rows=max_rows,
+                                   max_prior=max_prior, block_size=bs)
+    say(f"prefill fp8 {case} causal={causal} rows={np.diff(b.cu_seqlens_q).tolist()} "
+        f"ctx={b.pool.context_lens.tolist()}")
+    d = _dev(b)
+    got = _gpu_prefill(b, d, causal=causal)
+    assert_close(got, _oracle_prefill(b, _oracle_caches(b), causal=causal), torch.bfloat16,
+                 f"prefill fp8 causal={causal}")
+
+
+def test_prefill_fp8_rows_match_fp8_decode():
+    """Row i of a chunk equals the E4M3 decode kernel over the first P0 + i + 1 keys."""
+    b = W.random_prefill_batch_fp8(77, 5, 32, 8, 128, max_rows=6, min_rows=6, max_prior=700)
+    d = _dev(b)
+    got = _gpu_prefill(b, d)
+    cu, ctx = b.cu_seqlens_q, b.pool.context_lens
+    seq = np.repeat(np.arange(len(ctx)), 6)
+    row_ctx = np.concatenate([ctx[c] - 6 + 1 + np.arange(6) for c in range(len(ctx))]).astype(np.int32)
+    out = torch.empty_like(d["q"])
+    pkv.paged_attention_decode_fp8(out, d["q"], d["k_cache"], d["v_cache"], d["k_scale"], d["v_scale"],
+                                   torch.as_tensor(np.ascontiguousarray(b.pool.block_tables[seq]), device="cuda"),
+                                   torch.as_tensor(row_ctx, device="cuda"), b.scale, int(row_ctx.max()))
+    torch.cuda.synchronize()
+    dec = out.float().cpu().double().numpy()
+    assert cu[-1] == len(row_ctx)
+    assert_close(got, dec, torch.bfloat16, "prefill rows vs decode")
+
+
+def test_prefill_fp8_out_of_pool_block_poisons_its_chunk():
+    b = W.random_prefill_batch_fp8(79, 3, 32, 8, 128, max_rows=60, max_prior=80)
+    d = _dev(b)
+    bt = b.pool.block_tables.copy()
+    bt[1, 0] = b.pool.num_blocks + 3
+    d["block_tables"] = torch.as_tensor(bt, device="cuda")
+    got = _gpu_prefill(b, d)
+    cu = b.cu_seqlens_q
+    assert np.isnan(got[cu[1]:cu[2]]).all()
+    want = _oracle_prefill(b, _oracle_caches(b))
+    for c in (0, 2):
+        assert_close(got[cu[c]:cu[c + 1]], want[cu[c]:cu[c + 1]], torch.bfloat16, f"chunk {c}")
+
+
+@pytest.mark.slow
+def test_mixed_prefill_fp8_sampled_rows():
+    b = W.mixed_prefill_fp8()
+    d = {k: getattr(b, k).to("cuda") for k in ("q", "k_cache", "v_cache", "k_scale", "v_scale",
+                                                "k_new", "v_new", "slot_mapping")}
+    d["block_tables"] = torch.as_tensor(b.pool.block_tables, device="cuda")
+    d["context_lens"] = torch.as_tensor(b.pool.context_lens, device="cuda")
+    say(f"mixed prefill fp8: ctx={b.pool.context_lens.tolist()}")
+    got = _gpu_prefill(b, d)
+    kc, vc = _oracle_caches(b)
+    q, cu = W.host_bits(b.q), b.cu_seqlens_q
+    for c in range(8):
+        prior = int(b.pool.context_lens[c]) - 512
+        for i in sorted({0, 1, 63, 255, 511} | set(range(7, 512, 131))):
+            want = FP8.paged_attention_decode_fp8(q[cu[c] + i][None], kc, vc, W.host_bits(b.k_scale),
+                                                  W.host_bits(b.v_scale), b.pool.block_tables[c:c + 1],
+                                                  np.array([prior + i + 1]), b.scale, 16)
+            assert_close(got[cu[c] + i][None], want, torch.bfloat16, f"chunk {c} row {i}")
