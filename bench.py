@@ -368,6 +368,22 @@ def secondary(device, steps, warmup, algo, bf16_step_ms):
                     "decode_balanced_ms": t_dec_bal,
                     "tokens_per_s": 4224 / ((t_store + t_pre + t_dec) * 1e-3)}
     del store, prefill, dec, wl, pre, db
+    torch.cuda.empty_cache()
+    # the same chunked prefill over E4M3 caches (its own draws, same lengths and tables)
+    pf = W.mixed_prefill_fp8(device=device)
+    pkv.kv_cache_store_fp8(pf.k_new, pf.v_new, pf.k_cache, pf.v_cache, pf.slot_mapping, pf.k_scale,
+                           pf.v_scale)
+    prefill8 = pkv.PrefillFp8Launch(torch.empty_like(pf.q), pf.q, pf.k_cache, pf.v_cache, pf.k_scale,
+                                    pf.v_scale, torch.as_tensor(pf.pool.block_tables, device=device),
+                                    torch.as_tensor(pf.cu_seqlens_q, device=device),
+                                    torch.as_tensor(pf.pool.context_lens, device=device), pf.scale,
+                                    int(np.diff(pf.cu_seqlens_q).max()), pf.max_ctx, causal=True)
+    t_pre8 = time_region(prefill8, steps, warmup)
+    fl8 = prefill_flops(pf)
+    res["mixed"].update({"prefill_fp8_ms": t_pre8, "prefill_fp8_TFLOPs": fl8 / t_pre8 / 1e9,
+                         "prefill_fp8_mfma_util_pct": 100 * fl8 / t_pre8 / 1e9 / BF16_MFMA_PEAK_TFLOPS})
+    del prefill8, pf
+    torch.cuda.empty_cache()
     # verification of drafted tokens: 128 seqs x 4 causal rows, one chunk call
     sv = W.spec_verify(device=device).prefill
     pkv.kv_cache_store(sv.k_new, sv.v_new, sv.k_cache, sv.v_cache, sv.slot_mapping)
