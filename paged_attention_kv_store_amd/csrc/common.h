@@ -123,6 +123,7 @@ struct PrefillParams {
   int32_t max_q_len;
   int32_t num_q_tiles;       // set by the launcher
   int32_t longest_first;     // set by the launcher: items start in order of cost
+  int32_t pair_span;         // set by the launcher: compute units, when ids C .. 2C-1 are mirrored
   int32_t max_blocks;
   int32_t num_blocks;
   int32_t block_size;
@@ -147,6 +148,9 @@ struct PrefillParams {
   const float* k_scale;
   const float* v_scale;
 };
+
+// Compute units of the current device (queried once per device).
+int device_compute_units();
 
 // dtype codes match pkv_dtype
 hipError_t launch_store(const StoreParams& p, hipStream_t stream);

@@ -1414,8 +1414,6 @@ hipError_t launch_decode_valu(const DecodeParams& p, int head_dim, int dtype, hi
   return head_dim == 64 ? launch_valu_g<uint16_t, 64>(p, stream) : launch_valu_g<uint16_t, 128>(p, stream);
 }
 
-static int device_compute_units();
-
 template <int D, bool FP8>
 static hipError_t launch_mfma_d(const DecodeParams& p, hipStream_t stream) {
   if (!decode_grid_fits(p)) return hipErrorInvalidValue;
@@ -1446,7 +1444,7 @@ hipError_t launch_decode_mfma_fp8(const DecodeParams& p, int head_dim, hipStream
 }
 
 // Compute units of the current device (queried once per device).
-static int device_compute_units() {
+int device_compute_units() {
   constexpr int kMaxDevices = 64;
   static std::atomic<int> cache[kMaxDevices];
   int dev = 0;

@@ -101,10 +101,15 @@ void prefill_kernel(PrefillParams p) {
   const int tid = threadIdx.x;
   int qt, c, g;
   if (p.longest_first) {
-    g = blockIdx.x % p.num_kv_heads;
+    // Two workgroups share a compute unit, id b and id b + C on C units:
+    // ids C .. 2C-1 take the first round's ranks in reverse, so that each
+    // unit pairs a costly item with a cheaper one.
+    int b = blockIdx.x;
+    if (p.pair_span > 0 && b >= p.pair_span && b < 2 * p.pair_span) b = 3 * p.pair_span - 1 - b;
+    g = b % p.num_kv_heads;
     // (chunk, q-tile) item j = chunk * num_q_tiles + q-tile
     const int j = item_of_rank<kPThreads, kOrderBuckets>(
-        blockIdx.x / p.num_kv_heads, nqt * p.num_seqs, [&](int i) { return item_cost<BQ>(p, i); },
+        b / p.num_kv_heads, nqt * p.num_seqs, [&](int i) { return item_cost<BQ>(p, i); },
         reinterpret_cast<int*>(s_v[1]), reinterpret_cast<uint16_t*>(s_k[1]));
     if (j < 0) return;
     c = j / nqt;
@@ -462,6 +467,8 @@ static hipError_t launch_prefill_t(const PrefillParams& p, int head_dim, hipStre
   const int64_t items = (int64_t)q.num_q_tiles * p.num_seqs * p.num_kv_heads;
   if (items > 0x7fffffff - kXcds) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((items + kXcds - 1) / kXcds * kXcds));
+  const int cus = device_compute_units();
+  q.pair_span = (q.longest_first && (int64_t)grid.x >= 2 * (int64_t)cus) ? cus : 0;
   switch (p.group) {
     case 1: hipLaunchKernelGGL((prefill_kernel<1, FP8>), grid, dim3(kPThreads), 0, stream, q); break;
     case 2: hipLaunchKernelGGL((prefill_kernel<2, FP8>), grid, dim3(kPThreads), 0, stream, q); break;
