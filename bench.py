@@ -182,23 +182,34 @@ def copy_bandwidth(device, nbytes=2 << 30):
 # --------------------------------------------------------------------------
 
 class Layer:
-    def __init__(self, b: W.PagedBatch, bt, cl, partition, algo):
+    def __init__(self, b: W.PagedBatch, bt, cl, partition, algo, plan=None):
         self.b = b
         self.out = torch.empty_like(b.q)
         self.store = pkv.StoreLaunch(b.k_new, b.v_new, b.k_cache, b.v_cache, b.slot_mapping)
         self.decode = pkv.DecodeLaunch(self.out, b.q, b.k_cache, b.v_cache, bt, cl, b.scale,
-                                       b.max_ctx, partition_size=partition, algo=algo)
+                                       b.max_ctx, partition_size=partition, algo=algo, workspace=plan)
         self.fused = pkv.DecodeStoreLaunch(self.out, b.q, b.k_cache, b.v_cache, bt, cl, b.k_new,
                                            b.v_new, b.slot_mapping, b.scale, b.max_ctx,
-                                           partition_size=partition, algo=algo)
+                                           partition_size=partition, algo=algo, workspace=plan)
+
+
+def parse_partition(v):
+    return v if v in ("planned", "balanced") else int(v)
 
 
 def build_headline(device, layers, partition, algo):
+    """The 28 layers, and the step's plan launch (None unless the decode is
+    planned: one plan per step, written before the first layer, serves all)."""
     wl = W.qwen3_decode(device=device, layers=layers)
     b0 = wl.batches[0]
     bt = torch.as_tensor(b0.pool.block_tables, device=device)
     cl = torch.as_tensor(b0.pool.context_lens, device=device)
-    return wl, [Layer(b, bt, cl, partition, algo) for b in wl.batches]
+    plan = plan_launch = None
+    if partition == "planned":
+        plan = pkv.new_decode_plan(b0.num_seqs, device)
+        plan_launch = pkv.DecodePlanLaunch(plan, bt, cl, b0.max_ctx, b0.block_size)
+        plan_launch()
+    return wl, [Layer(b, bt, cl, partition, algo, plan) for b in wl.batches], plan_launch
 
 
 def capture_step(step, outs, replays=3):
@@ -284,7 +295,22 @@ def balanced_ms(b, bt, cl, steps, warmup):
     return time_region(dec, steps, warmup)
 
 
-def fp8_step(device, steps, warmup, bf16_step_ms):
+def planned_ms(b, bt, cl, steps, warmup):
+    """The same decode in the order of a plan, the plan's launch included
+    (one decode call per step here, so nothing amortises it)."""
+    plan = pkv.new_decode_plan(b.num_seqs, b.q.device)
+    mk = pkv.DecodePlanLaunch(plan, bt, cl, b.max_ctx, b.block_size)
+    mk()
+    dec = pkv.DecodeLaunch(torch.empty_like(b.q), b.q, b.k_cache, b.v_cache, bt, cl, b.scale,
+                           b.max_ctx, partition_size="planned", algo="mfma", workspace=plan)
+
+    def run():
+        mk()
+        dec()
+    return time_region(run, steps, warmup)
+
+
+def fp8_step(device, steps, warmup, bf16_step_ms, partition=0):
     """The headline step over E4M3 caches: per layer, decode with the
     quantising store of the 60 new rows fused in, 28 layers, one graph replay."""
     wl = W.qwen3_decode_fp8(device=device)
@@ -292,13 +318,21 @@ def fp8_step(device, steps, warmup, bf16_step_ms):
     bt = torch.as_tensor(b0.pool.block_tables, device=device)
     cl = torch.as_tensor(b0.pool.context_lens, device=device)
     calls, outs = [], []
+    plan = mk = None
+    if partition == "planned":
+        plan = pkv.new_decode_plan(b0.num_seqs, device)
+        mk = pkv.DecodePlanLaunch(plan, bt, cl, b0.max_ctx, b0.block_size)
+        mk()
     for b in wl.batches:
         out = torch.empty_like(b.q)
         outs.append(out)
         calls.append(pkv.DecodeStoreFp8Launch(out, b.q, b.k_cache, b.v_cache, b.k_scale, b.v_scale, bt,
-                                              cl, b.k_new, b.v_new, b.slot_mapping, b.scale, b.max_ctx))
+                                              cl, b.k_new, b.v_new, b.slot_mapping, b.scale, b.max_ctx,
+                                              partition_size=partition, workspace=plan))
 
     def step():
+        if mk is not None:
+            mk()
         for c in calls:
             c()
     graph = capture_step(step, outs)
@@ -308,11 +342,11 @@ def fp8_step(device, steps, warmup, bf16_step_ms):
     return {"ms_per_step": ms, "GBps": per_launch * len(calls) / ms / 1e6,
             "tokens_per_s": b0.num_seqs / (ms * 1e-3), "speedup_vs_bf16_step": bf16_step_ms / ms,
             "decode_avg_launch_us": dec_ms * 1e3, "decode_GBps": per_launch / dec_ms / 1e6,
-            "cache": "E4M3 codes, per-kv-head scales; store fused into decode"}
+            "partition": partition, "cache": "E4M3 codes, per-kv-head scales; store fused into decode"}
 
 
-def secondary(device, steps, warmup, algo, bf16_step_ms):
-    res = {"qwen3_fp8": fp8_step(device, steps, warmup, bf16_step_ms)}
+def secondary(device, steps, warmup, algo, bf16_step_ms, partition=0):
+    res = {"qwen3_fp8": fp8_step(device, steps, warmup, bf16_step_ms, partition)}
     torch.cuda.empty_cache()
     b = W.llama_prefix(device=device).batches[0]
     bt = torch.as_tensor(b.pool.block_tables, device=device)
@@ -325,6 +359,7 @@ def secondary(device, steps, warmup, algo, bf16_step_ms):
                            "pct_hbm_peak_unique": 100 * ub / ms / 1e6 / HBM_PEAK_GBS,
                            "tokens_per_s": b.num_seqs / (ms * 1e-3), "partition": 0,
                            "balanced_ms": balanced_ms(b, bt, cl, steps, warmup),
+                           "planned_ms": planned_ms(b, bt, cl, steps, warmup),
                            "shared_prefix_ms": time_region(pkv.SharedPrefixDecodeLaunch(
                                torch.empty_like(b.q), b.q, b.k_cache, b.v_cache, bt, cl,
                                torch.arange(0, b.num_seqs + 1, 8, dtype=torch.int32, device=device),
@@ -341,7 +376,8 @@ def secondary(device, steps, warmup, algo, bf16_step_ms):
     by = decode_bytes(b)
     res["long_splitk"] = {"ms": ms, "GBps": by / ms / 1e6, "pct_hbm_peak": 100 * by / ms / 1e6 / HBM_PEAK_GBS,
                           "tokens_per_s": b.num_seqs / (ms * 1e-3), "partition": 512,
-                          "balanced_ms": balanced_ms(b, bt, cl, steps, warmup)}
+                          "balanced_ms": balanced_ms(b, bt, cl, steps, warmup),
+                          "planned_ms": planned_ms(b, bt, cl, steps, warmup)}
     del dec, b
     wl = W.mixed(device=device)
     pre, db = wl.prefill, wl.batches[0]
@@ -360,12 +396,14 @@ def secondary(device, steps, warmup, algo, bf16_step_ms):
     t_dec = time_region(dec, steps, warmup)
     t_dec_bal = balanced_ms(db, torch.as_tensor(db.pool.block_tables, device=device),
                             torch.as_tensor(db.pool.context_lens, device=device), steps, warmup)
+    t_dec_plan = planned_ms(db, torch.as_tensor(db.pool.block_tables, device=device),
+                            torch.as_tensor(db.pool.context_lens, device=device), steps, warmup)
     fl = prefill_flops(pre)
     res["mixed"] = {"store_ms": t_store, "store_GBps": store_bytes(pre) / t_store / 1e6,
                     "prefill_ms": t_pre, "prefill_TFLOPs": fl / t_pre / 1e9,
                     "prefill_mfma_util_pct": 100 * fl / t_pre / 1e9 / BF16_MFMA_PEAK_TFLOPS,
                     "decode_ms": t_dec, "decode_GBps": decode_bytes(db) / t_dec / 1e6,
-                    "decode_balanced_ms": t_dec_bal,
+                    "decode_balanced_ms": t_dec_bal, "decode_planned_ms": t_dec_plan,
                     "tokens_per_s": 4224 / ((t_store + t_pre + t_dec) * 1e-3)}
     del store, prefill, dec, wl, pre, db
     torch.cuda.empty_cache()
@@ -412,12 +450,12 @@ def calib_bytes():
     return 2 * CALIB_TOKENS * row + 4 * CALIB_TOKENS, 2 * CALIB_TOKENS * row
 
 
-def pmc_pass(device, layers):
+def pmc_pass(device, layers, partition):
     """The headline's launches once each (decode with the store fused, as
     timed), then a plain copy of known size: a kv_cache_store of 65536 new
     rows into a pool of exactly as many slots (identity slots), i.e. 256 MiB
     read and 256 MiB written."""
-    wl, lyr = build_headline(device, layers, 0, "auto")
+    wl, lyr, plan_launch = build_headline(device, layers, partition, "auto")
     torch.cuda.synchronize()
     for ly in lyr:
         ly.fused()
@@ -623,7 +661,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--partition", type=int, default=0, help="decode partition size for the step (-1: work-balanced)")
+    ap.add_argument("--partition", type=parse_partition, default="planned",
+                    help="decode partition size for the step: 'planned' (items in the order of a plan "
+                         "made once per step), 0 (one pass, items ranked in the kernel), a multiple of "
+                         "16 (split-K) or 'balanced'")
     ap.add_argument("--algo", default="auto", choices=sorted(pkv.DECODE_ALGOS))
     ap.add_argument("--layers", type=int, default=28)
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replay")
@@ -655,24 +696,30 @@ def main():
     device = torch.device("cuda:0")
     torch.cuda.set_device(device)
     if args.pmc_pass:
-        pmc_pass(device, args.layers)
+        pmc_pass(device, args.layers, args.partition)
         return
     if args.prefill_pmc_pass:
         prefill_pmc_pass(device)
         return
 
     log("generating the qwen3-shaped decode workload on the GPU")
-    wl, lyr = build_headline(device, args.layers, args.partition, args.algo)
+    wl, lyr, plan_launch = build_headline(device, args.layers, args.partition, args.algo)
     b0 = wl.batches[0]
     step_bytes = (decode_bytes(b0) + store_bytes(b0)) * len(lyr)
 
+    def make_plan():
+        if plan_launch is not None:
+            plan_launch()
+
     if args.unfused:
         def step():
+            make_plan()
             for ly in lyr:
                 ly.store()
                 ly.decode()
     else:
         def step():
+            make_plan()
             for ly in lyr:
                 ly.fused()
 
@@ -690,6 +737,7 @@ def main():
     dec_bytes = decode_bytes(b0) + (0.0 if args.unfused else store_bytes(b0))
     dec_ms = time_each_launch([ly.decode if args.unfused else ly.fused for ly in lyr], 4)
     store_ms = time_each_launch([ly.store for ly in lyr], 2)
+    plan_us = time_each_launch([plan_launch], 20) * 1e3 if plan_launch is not None else None
     copy_gbps = copy_bandwidth(device)
     achieved = dec_bytes / (dec_ms * 1e-3) / 1e9
 
@@ -724,9 +772,10 @@ def main():
         "config": {"workload": "qwen3_decode", "num_seqs": 60, "context_lens": "U{64..1024}",
                    "num_q_heads": 16, "num_kv_heads": 8, "head_dim": 128, "block_size": 16,
                    "layers": len(lyr), "partition_size": args.partition, "algo": args.algo,
-                   "step": ("per layer: kv_cache_store of 60 new rows, then paged_attention_decode"
-                            if args.unfused else
-                            "per layer: paged_attention_decode_store (store of 60 new rows fused)"),
+                   "step": (("decode_plan once, then " if plan_launch is not None else "") +
+                            ("per layer: kv_cache_store of 60 new rows, then paged_attention_decode"
+                             if args.unfused else
+                             "per layer: paged_attention_decode_store (store of 60 new rows fused)")),
                    "launch": "eager" if args.eager else "hip graph replay",
                    "parallelism": "single GPU"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
@@ -740,6 +789,7 @@ def main():
                      "avg_launch_us": round(dec_ms * 1e3, 2),
                      "algorithmic_bytes_per_launch": dec_bytes},
         "store_avg_launch_us": round(store_ms * 1e3, 2),
+        "plan_avg_launch_us": None if plan_us is None else round(plan_us, 2),
         "parity_sample_max_abs_err": parity_err,
     }
     if not args.no_secondary:
@@ -748,7 +798,7 @@ def main():
             del graph, run
         torch.cuda.empty_cache()
         log("secondary workloads")
-        result["secondary"] = secondary(device, max(5, args.steps // 2), 3, args.algo, ms)
+        result["secondary"] = secondary(device, max(5, args.steps // 2), 3, args.algo, ms, args.partition)
     if not args.no_cpu_baseline:
         log("oracle baseline on the host")
         result["cpu_baseline"] = cpu_baseline(W.qwen3_decode(device="cpu", layers=1).batches[0])

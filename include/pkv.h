@@ -74,9 +74,9 @@ typedef enum {
   PKV_DECODE_MFMA = 2     /* GQA group packed into matrix-core tiles (bf16 only) */
 } pkv_decode_algo;
 
-/* partition_size value selecting the work-balanced decode (see
- * pkv_paged_attention_decode). */
-enum { PKV_PARTITION_BALANCED = -1 };
+/* partition_size values selecting the work-balanced decode and the planned
+ * decode (see pkv_paged_attention_decode and pkv_decode_plan). */
+enum { PKV_PARTITION_BALANCED = -1, PKV_PARTITION_PLANNED = -2 };
 
 /* Library version as major*10000 + minor*100 + patch. */
 int pkv_version(void);
@@ -115,11 +115,38 @@ int pkv_kv_cache_store(const void* k, const void* v, void* k_cache, void* v_cach
  *  - PKV_PARTITION_BALANCED: 4096 int32 arrival counters (16 KiB, at the
  *    start whatever the sizes), then fp32 pieces of the partial results, two
  *    per wave of the largest grid (4096 waves).
+ *  - PKV_PARTITION_PLANNED: pkv_decode_plan_size(num_seqs) (the plan).
  *  - 0 (single pass): 0.
  */
 size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_context_len,
                                  int32_t partition_size);
+
+/*
+ * Decode plan: the sequences of one decode step in order of their number of
+ * 16-token tiles (ceil(min(context_lens[s], max_context_len) / 16), capped
+ * at 2047), largest first, ties by sequence index, for a single-pass decode
+ * whose workgroups then start their long items first and pair long with
+ * short ones on each compute unit without ranking the batch themselves.
+ * Every layer of a step shares one block table and one set of lengths, so
+ * one plan serves all the layers' decode calls (pass partition_size =
+ * PKV_PARTITION_PLANNED and the plan as `workspace`).
+ *   plan: device buffer of pkv_decode_plan_size(num_seqs) bytes, 16-byte
+ *     aligned, owned by the caller. Entry r (8 int32): the r-th sequence s,
+ *     its context_lens value, the table entries block_tables[s][(16 w) /
+ *     block_size] (w = 0..3, capped at the row's last entry), 0, 0.
+ *   The other arguments are those of pkv_paged_attention_decode. One
+ *   workgroup, asynchronous on `stream`. The plan describes context_lens and
+ *   block_tables as they are when it runs: make a new plan whenever either
+ *   changes. A decode whose plan does not match them (a sequence's length or
+ *   first blocks differ) writes that sequence's rows as NaN; whether a fused
+ *   store then wrote its new row is unspecified.
+ * Supported: num_seqs <= 65535, block_size a multiple of 16 up to 256.
+ */
+size_t pkv_decode_plan_size(int32_t num_seqs);
+int pkv_decode_plan(void* plan, size_t plan_bytes, const int32_t* block_tables,
+                    const int32_t* context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
+                    int32_t max_context_len, int32_t block_size, void* stream);
 
 /*
  * paged_attention_decode: out[s, h] = softmax_j(scale * q[s, h] . K_s[j, g])
@@ -149,6 +176,12 @@ size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *     workspace); every call leaves them zero, so one workspace serves calls
  *     of any sizes in turn, but calls that run at the same time must not
  *     share it. out must be 16-byte aligned.
+ *     PKV_PARTITION_PLANNED (MFMA kernel; bf16 or E4M3 caches): one pass per
+ *     (sequence, kv-head), with the items handed out in the order of the
+ *     plan that pkv_decode_plan wrote into `workspace` for the same
+ *     num_seqs, context_lens and block_tables (workspace_bytes >=
+ *     pkv_decode_plan_size(num_seqs)). The results are those of
+ *     partition_size 0.
  *   workspace / workspace_bytes: device buffer of at least
  *     pkv_decode_workspace_size(...) bytes (may be NULL when that is 0),
  *     256-byte aligned for PKV_PARTITION_BALANCED.

@@ -9,8 +9,10 @@ library; the first call does, and raises if it has not been built.
 from .binding import (  # noqa: F401
     DECODE_ALGOS,
     PARTITION_BALANCED,
+    PARTITION_PLANNED,
     DecodeFp8Launch,
     DecodeLaunch,
+    DecodePlanLaunch,
     DecodeStoreFp8Launch,
     DecodeStoreLaunch,
     PkvError,
@@ -19,11 +21,14 @@ from .binding import (  # noqa: F401
     SharedPrefixDecodeLaunch,
     StoreFp8Launch,
     StoreLaunch,
+    decode_plan,
+    decode_plan_size,
     decode_workspace_size,
     kv_cache_store,
     kv_cache_store_fp8,
     lib,
     library_path,
+    new_decode_plan,
     paged_attention_decode,
     paged_attention_decode_fp8,
     paged_attention_decode_shared_prefix,

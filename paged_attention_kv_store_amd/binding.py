@@ -23,6 +23,7 @@ PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EWORKSPACE, PKV_EHIP = 0, -1, -2, -3, 
 PKV_F32, PKV_BF16 = 0, 1
 DECODE_ALGOS = {"auto": 0, "valu": 1, "mfma": 2}
 PARTITION_BALANCED = -1      # partition_size selecting the work-balanced decode
+PARTITION_PLANNED = -2       # partition_size selecting the planned decode (workspace = the plan)
 
 _i32 = ctypes.c_int32
 _vp = ctypes.c_void_p
@@ -32,6 +33,8 @@ _SIGNATURES = {
     "pkv_kv_cache_store": ([_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _vp],
                            ctypes.c_int),
     "pkv_decode_workspace_size": ([_i32, _i32, _i32, _i32, _i32, _i32], ctypes.c_size_t),
+    "pkv_decode_plan_size": ([_i32], ctypes.c_size_t),
+    "pkv_decode_plan": ([_vp, ctypes.c_size_t, _vp, _vp, _i32, _i32, _i32, _i32, _vp], ctypes.c_int),
     "pkv_paged_attention_decode": ([_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                     _i32, _i32, _i32, ctypes.c_float, _i32, _vp, ctypes.c_size_t,
                                     ctypes.c_int, _i32, _vp], ctypes.c_int),
@@ -142,7 +145,47 @@ def kv_cache_store(k, v, k_cache, v_cache, slot_mapping, stream=None):
 
 
 def _partition(partition_size):
-    return PARTITION_BALANCED if partition_size == "balanced" else int(partition_size)
+    if partition_size == "balanced":
+        return PARTITION_BALANCED
+    if partition_size == "planned":
+        return PARTITION_PLANNED
+    return int(partition_size)
+
+
+def decode_plan_size(num_seqs):
+    return int(lib().pkv_decode_plan_size(num_seqs))
+
+
+def new_decode_plan(num_seqs, device):
+    """A device buffer for decode_plan (uint8, pkv_decode_plan_size bytes)."""
+    return torch.empty(max(decode_plan_size(num_seqs), 16), dtype=torch.uint8, device=device)
+
+
+class DecodePlanLaunch:
+    """decode_plan with fixed tensors: one C call per launch."""
+
+    def __init__(self, plan, block_tables, context_lens, max_context_len, block_size):
+        _dev(plan, block_tables, context_lens)
+        _need(plan.dtype == torch.uint8 and plan.is_contiguous(), "plan must be a contiguous uint8 tensor")
+        _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2, "block_tables must be int32 [S, MB]")
+        _need(context_lens.dtype == torch.int32 and context_lens.shape == (block_tables.shape[0],),
+              "context_lens must be int32 [S]")
+        _need(block_tables.is_contiguous() and context_lens.is_contiguous(), "index arrays must be contiguous")
+        self._keep = (plan, block_tables, context_lens)
+        self._args = (_ptr(plan), plan.numel(), _ptr(block_tables), _ptr(context_lens),
+                      block_tables.shape[0], block_tables.shape[1], int(max_context_len), int(block_size))
+
+    def __call__(self, stream=None):
+        _check(lib().pkv_decode_plan(*self._args, _stream(stream)))
+
+
+def decode_plan(plan, block_tables, context_lens, max_context_len, block_size, stream=None):
+    """Order the step's sequences by size, largest first, into `plan` (see
+    new_decode_plan); decode calls with partition_size="planned" and
+    workspace=plan then use it, for as long as context_lens and block_tables
+    stay as they were."""
+    DecodePlanLaunch(plan, block_tables, context_lens, max_context_len, block_size)(stream)
+    return plan
 
 
 def decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
@@ -155,6 +198,8 @@ def _decode_workspace(workspace, s, hq, hkv, d, max_context_len, partition, devi
     """The caller's workspace, or a new one when the call needs it: zero-filled
     (the work-balanced decode requires zero counters before its first call)."""
     need = decode_workspace_size(s, hq, hkv, d, max_context_len, partition) if partition else 0
+    _need(partition != PARTITION_PLANNED or workspace is not None,
+          "the planned decode takes its plan (written by decode_plan) as workspace")
     if need and workspace is None:
         workspace = torch.zeros(need, dtype=torch.uint8, device=device)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
@@ -168,7 +213,9 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
 
     max_context_len is a host-side bound on context_lens (it sizes the grid).
     partition_size: 0 (one pass per sequence and kv-head), a positive multiple
-    of 16 (split-K), or "balanced" / PARTITION_BALANCED (work-balanced decode).
+    of 16 (split-K), "balanced" / PARTITION_BALANCED (work-balanced decode), or
+    "planned" / PARTITION_PLANNED (one pass in the order of the plan passed as
+    `workspace`, written by decode_plan).
     The workspace those need is taken from `workspace` (a uint8 device
     tensor; zero-filled before its first work-balanced use) or allocated here
     through torch when omitted.
@@ -462,7 +509,7 @@ class DecodeFp8Launch(_Prepared):
         _need(k_cache.shape[3] == q.shape[2], "head_dim mismatch")
         s, hq, d = q.shape
         nb, bs, hkv, _ = k_cache.shape
-        part = int(partition_size)
+        part = _partition(partition_size)
         workspace, ws_bytes = _decode_workspace(workspace, s, hq, hkv, d, max_context_len, part,
                                                 q.device)
         self._keep = (out, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, workspace)

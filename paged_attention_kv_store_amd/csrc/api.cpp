@@ -92,6 +92,41 @@ extern "C" int pkv_kv_cache_store(const void* k, const void* v, void* k_cache, v
 }
 
 
+extern "C" size_t pkv_decode_plan_size(int32_t num_seqs) {
+  if (num_seqs <= 0) return 0;
+  return (size_t)num_seqs * pkv::kPlanEntryInts * sizeof(int32_t);
+}
+
+extern "C" int pkv_decode_plan(void* plan, size_t plan_bytes, const int32_t* block_tables,
+                               const int32_t* context_lens, int32_t num_seqs,
+                               int32_t max_blocks_per_seq, int32_t max_context_len,
+                               int32_t block_size, void* stream) {
+  const char* fn = "pkv_decode_plan";
+  if (num_seqs < 0 || num_seqs > 65535) return fail(PKV_EINVAL, "%s: num_seqs %d outside [0, 65535]", fn, num_seqs);
+  if (block_size % 16 != 0 || block_size <= 0 || block_size > 256)
+    return fail(PKV_EUNSUPPORTED, "%s: block_size %d must be a multiple of 16 up to 256", fn, block_size);
+  if (max_blocks_per_seq <= 0) return fail(PKV_EINVAL, "%s: max_blocks_per_seq must be positive", fn);
+  if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
+    return fail(PKV_EINVAL, "%s: max_context_len %d outside [0, max_blocks_per_seq * block_size = %lld]", fn,
+                max_context_len, (long long)max_blocks_per_seq * block_size);
+  if (num_seqs == 0) return PKV_OK;
+  if (!plan || !block_tables || !context_lens) return fail(PKV_EINVAL, "%s: null pointer", fn);
+  if (plan_bytes < pkv_decode_plan_size(num_seqs))
+    return fail(PKV_EWORKSPACE, "%s: the plan needs %zu bytes, got %zu", fn, pkv_decode_plan_size(num_seqs),
+                plan_bytes);
+  if (!aligned(plan, 16) || !aligned(block_tables, 4) || !aligned(context_lens, 4))
+    return fail(PKV_EINVAL, "%s: plan must be 16-byte aligned, index arrays 4-byte", fn);
+  pkv::PlanParams p;
+  p.plan = reinterpret_cast<int32_t*>(plan);
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.num_seqs = num_seqs;
+  p.max_blocks = max_blocks_per_seq;
+  p.max_ctx = max_context_len;
+  p.block_size = block_size;
+  return hip_status(pkv::launch_decode_plan(p, (hipStream_t)stream), fn);
+}
+
 extern "C" size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                             int32_t head_dim, int32_t max_context_len,
                                             int32_t partition_size) {
@@ -104,6 +139,7 @@ extern "C" size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_head
     return (size_t)(pkv::kBalMaxWaves * (int64_t)sizeof(int32_t) +
                     2 * (int64_t)pkv::kBalMaxWaves * stride * (int64_t)sizeof(float));
   }
+  if (partition_size == PKV_PARTITION_PLANNED) return pkv_decode_plan_size(num_seqs);
   if (partition_size <= 0) return 0;
   int32_t part;
   int64_t nparts;
@@ -142,9 +178,10 @@ int decode_impl(const char* fn, void* out, const void* q, const void* k_cache, c
     return fail(PKV_EINVAL, "%s: max_context_len %d outside [0, max_blocks_per_seq * block_size = %lld]", fn,
                 max_context_len, (long long)max_blocks_per_seq * block_size);
   const bool balanced = partition_size == PKV_PARTITION_BALANCED;
-  if (!balanced && (partition_size < 0 || partition_size % 16 != 0))
-    return fail(PKV_EINVAL, "%s: partition_size %d must be 0, a positive multiple of 16 or "
-                "PKV_PARTITION_BALANCED", fn, partition_size);
+  const bool planned = partition_size == PKV_PARTITION_PLANNED;
+  if (!balanced && !planned && (partition_size < 0 || partition_size % 16 != 0))
+    return fail(PKV_EINVAL, "%s: partition_size %d must be 0, a positive multiple of 16, "
+                "PKV_PARTITION_BALANCED or PKV_PARTITION_PLANNED", fn, partition_size);
   if (!std::isfinite(scale)) return fail(PKV_EINVAL, "%s: scale is not finite", fn);
   if (algo == PKV_DECODE_AUTO) algo = dtype == PKV_BF16 ? PKV_DECODE_MFMA : PKV_DECODE_VALU;
   if (fp8) {
@@ -164,6 +201,8 @@ int decode_impl(const char* fn, void* out, const void* q, const void* k_cache, c
   }
   if (num_seqs > 65535 || num_kv_heads > 65535)
     return fail(PKV_EUNSUPPORTED, "%s: num_seqs and num_kv_heads are limited to 65535", fn);
+  if (planned && algo != PKV_DECODE_MFMA)
+    return fail(PKV_EUNSUPPORTED, "%s: the planned decode runs on the MFMA kernel (bf16)", fn);
   if (balanced) {
     if (algo != PKV_DECODE_MFMA)
       return fail(PKV_EUNSUPPORTED, "%s: the work-balanced decode runs on the MFMA kernel (bf16)", fn);
@@ -176,7 +215,7 @@ int decode_impl(const char* fn, void* out, const void* q, const void* k_cache, c
   {
     int32_t part_probe;
     int64_t nparts_probe;
-    partitioning(max_context_len, balanced ? 0 : partition_size, &part_probe, &nparts_probe);
+    partitioning(max_context_len, (balanced || planned) ? 0 : partition_size, &part_probe, &nparts_probe);
     if (nparts_probe > 1 && (int64_t)num_seqs * num_kv_heads > pkv::kSplitMaxItems)
       return fail(PKV_EUNSUPPORTED, "%s: split-K takes at most %d (sequence, kv-head) pairs", fn,
                   pkv::kSplitMaxItems);
@@ -197,7 +236,7 @@ int decode_impl(const char* fn, void* out, const void* q, const void* k_cache, c
 
   int32_t part;
   int64_t nparts;
-  partitioning(max_context_len, balanced ? 0 : partition_size, &part, &nparts);
+  partitioning(max_context_len, (balanced || planned) ? 0 : partition_size, &part, &nparts);
   if ((int64_t)num_seqs * num_kv_heads * nparts > 0x7ffffff0)
     return fail(PKV_EUNSUPPORTED, "%s: %lld work items exceed the grid; use a larger partition_size", fn,
                 (long long)num_seqs * num_kv_heads * nparts);
@@ -232,7 +271,16 @@ int decode_impl(const char* fn, void* out, const void* q, const void* k_cache, c
   p.bal_pieces = nullptr;
   p.bal_piece_stride = 0;
   p.pair_span = 0;
+  p.plan = nullptr;
   hipStream_t st = (hipStream_t)stream;
+  if (planned) {
+    const size_t need = pkv_decode_plan_size(num_seqs);
+    if (!workspace || workspace_bytes < need)
+      return fail(PKV_EWORKSPACE, "%s: the planned decode needs its plan (%zu bytes) as workspace, got %zu", fn,
+                  need, workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 16)) return fail(PKV_EINVAL, "%s: the plan must be 16-byte aligned", fn);
+    p.plan = reinterpret_cast<const int32_t*>(workspace);
+  }
   if (balanced) {
     const size_t need = pkv_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                                   max_context_len, partition_size);
@@ -595,5 +643,7 @@ extern "C" int pkv_paged_attention_decode_shared_prefix(
   b.bal_counters = nullptr;
   b.bal_pieces = nullptr;
   b.bal_piece_stride = 0;
+  b.pair_span = 0;
+  b.plan = nullptr;
   return hip_status(pkv::launch_decode_mfma(b, head_dim, st), fn);
 }

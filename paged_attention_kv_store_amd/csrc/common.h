@@ -89,6 +89,24 @@ struct DecodeParams {
   // Set by the per-item launcher: the compute units, when workgroups are
   // given their items by size (0: in index order).
   int32_t pair_span;
+  // Planned single-pass decode (null otherwise): kPlanEntryInts int32 per
+  // sequence, largest first, written by decode_plan_kernel.
+  const int32_t* plan;
+};
+
+// A decode plan lists the sequences of a step largest first. Entry r:
+// {sequence, its context_lens value, the table entries of the first tiles of
+// waves 0..3 (16-token tiles w, i.e. block (16 w) / block_size), 0, 0}.
+constexpr int kPlanEntryInts = 8;
+
+struct PlanParams {
+  int32_t* plan;             // [num_seqs, kPlanEntryInts]
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int32_t num_seqs;
+  int32_t max_blocks;
+  int32_t max_ctx;
+  int32_t block_size;
 };
 
 // Split-K: the workspace starts with this many arrival counters (one per
@@ -159,6 +177,7 @@ hipError_t launch_decode_valu(const DecodeParams& p, int head_dim, int dtype, hi
 hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_decode_mfma_fp8(const DecodeParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_decode_balanced(const DecodeParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_decode_plan(const PlanParams& p, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_prefill_fp8(const PrefillParams& p, int head_dim, hipStream_t stream);
 

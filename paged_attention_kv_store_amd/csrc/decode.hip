@@ -75,13 +75,15 @@ __device__ __forceinline__ void store_out<uint16_t>(void* out, int64_t idx, floa
   reinterpret_cast<uint16_t*>(out)[idx] = f32_to_bf16_rne(v);
 }
 
-// Rows of q-heads g*G .. g*G+G-1 of sequence s set to zero (empty context).
+// Rows of q-heads g*G .. g*G+G-1 of sequence s set to zero (empty context),
+// or to NaN (poisoned).
 template <typename T, int D>
-__device__ void write_zero_rows(const DecodeParams& p, int s, int g) {
+__device__ void write_zero_rows(const DecodeParams& p, int s, int g, bool poisoned = false) {
   const int G = p.group;
+  const float v = poisoned ? __builtin_nanf("") : 0.f;
   for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
     const int h = idx / D, d = idx - h * D;
-    store_out<T>(p.out, ((int64_t)s * p.num_q_heads + g * G + h) * D + d, 0.f);
+    store_out<T>(p.out, ((int64_t)s * p.num_q_heads + g * G + h) * D + d, v);
   }
 }
 
@@ -340,6 +342,93 @@ __device__ __forceinline__ bool sized_item(const DecodeParams& p, int& g, int& s
   s = x / hkv;
   g = x - s * hkv;
   return true;
+}
+
+// Work item from a plan (single pass): the same pairing as sized_item with
+// the ranks already computed, once per step, by decode_plan_kernel. Workgroup
+// b takes rank b < C, or rank 3C - 1 - b for C <= b < 2C (each unit pairs the
+// r-th largest item with the (2C - 1 - r)-th), or rank b past 2C. Rank r is
+// kv-head r % Hkv of the (r / Hkv)-th largest sequence. The plan entry also
+// holds the sequence's length and the block of wave w's first tile, so the
+// first K/V loads wait for one load, as in index order.
+static_assert(kWaves <= kPlanEntryInts - 2, "plan entry holds one block per wave");
+__device__ __forceinline__ bool planned_item(const DecodeParams& p, int w, int& g, int& s, int& ctx_raw,
+                                             int& blk0) {
+  const int hkv = p.num_kv_heads, n = p.num_seqs * hkv, c = p.pair_span;
+  const int b = blockIdx.x;
+  const int r = b < c ? b : (b < 2 * c ? 3 * c - 1 - b : b);
+  if (r >= n) return false;
+  const int q = r / hkv;
+  g = r - q * hkv;
+  const int32_t* e = p.plan + (int64_t)q * kPlanEntryInts;
+  s = e[0];
+  ctx_raw = e[1];
+  blk0 = e[2 + w];
+  return (unsigned)s < (unsigned)p.num_seqs;   // a foreign plan never leads out of bounds
+}
+
+// The plan of a single-pass decode step (one workgroup): sequences in order
+// of 16-token tiles (capped at kRankBuckets - 1), largest first, ties by
+// index. A histogram gives each size's first rank; sequences then take
+// their places chunk by chunk, counting equal sizes before them in the chunk.
+__global__ __launch_bounds__(kThreads) void decode_plan_kernel(PlanParams p) {
+  constexpr int kPer = kRankBuckets / kThreads;   // buckets per thread
+  static_assert(kRankBuckets % kThreads == 0, "bucket split");
+  __shared__ int s_first[kRankBuckets];   // counts, then the next rank of each size
+  __shared__ int s_wave[kWaves];
+  __shared__ int s_chunk[kThreads];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  auto bucket = [&](int i) {
+    const int c = clamp_ctx(p.context_lens[i], p.max_ctx);
+    return min((c + kTile - 1) / kTile, kRankBuckets - 1);
+  };
+  for (int i = tid; i < kRankBuckets; i += kThreads) s_first[i] = 0;
+  __syncthreads();
+  for (int i = tid; i < p.num_seqs; i += kThreads) atomicAdd(&s_first[bucket(i)], 1);
+  __syncthreads();
+  // sequences in this thread's buckets, and in all larger ones (a suffix sum
+  // over threads: lanes above within the wave, then the waves above)
+  int mine = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) mine += s_first[kPer * tid + i];
+  int suffix = mine;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int x = __shfl_down(suffix, d, 64);
+    if (lane + d < 64) suffix += x;
+  }
+  if (lane == 0) s_wave[w] = suffix;
+  __syncthreads();
+  int above = suffix - mine;
+  for (int v = w + 1; v < kWaves; ++v) above += s_wave[v];
+  for (int i = kPer - 1; i >= 0; --i) {   // only this thread touches its buckets
+    const int cnt = s_first[kPer * tid + i];
+    s_first[kPer * tid + i] = above;
+    above += cnt;
+  }
+  __syncthreads();
+  for (int base = 0; base < p.num_seqs; base += kThreads) {
+    const int i = base + tid;
+    const int b = i < p.num_seqs ? bucket(i) : -1;
+    s_chunk[tid] = b;
+    __syncthreads();
+    if (i < p.num_seqs) {
+      int tie = 0;
+      for (int j = 0; j < tid; ++j) tie += s_chunk[j] == b ? 1 : 0;
+      const int r = s_first[b] + tie;
+      const int32_t* bt = p.block_tables + (int64_t)i * p.max_blocks;
+      int blk[kPlanEntryInts - 2];
+#pragma unroll
+      for (int v = 0; v < kPlanEntryInts - 2; ++v)
+        blk[v] = v < kWaves ? bt[min((v * kTile) / p.block_size, p.max_blocks - 1)] : 0;
+      int4* e = reinterpret_cast<int4*>(p.plan + (int64_t)r * kPlanEntryInts);
+      e[0] = make_int4(i, p.context_lens[i], blk[0], blk[1]);
+      e[1] = make_int4(blk[2], blk[3], blk[4], blk[5]);
+    }
+    __syncthreads();
+    if (i < p.num_seqs) atomicAdd(&s_first[b], 1);
+    __syncthreads();
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -607,14 +696,18 @@ void decode_mfma_kernel(DecodeParams p) {
   __shared__ uint16_t s_rank_tiles[kRankMaxSeqs];
   __shared__ int s_rank_sum[kWaves];
 
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int g, part = 0, s;
-  if (p.pair_span > 0) {
+  int plan_ctx = 0, plan_blk = 0;
+  const bool planned = p.plan != nullptr;
+  if (planned) {
+    if (!planned_item(p, w, g, s, plan_ctx, plan_blk)) return;
+  } else if (p.pair_span > 0) {
     if (!sized_item(p, g, s, s_rank_hist, s_rank_cost, s_rank_tiles, s_rank_sum)) return;
   } else if (!decode_item(p, g, part, s)) {
     return;
   }
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, qg = lane >> 4;
   const int G = p.group;
   const int P = p.partition_size;
@@ -628,14 +721,20 @@ void decode_mfma_kernel(DecodeParams p) {
   // inside the table row; used only when it is the right entry).
   // With several partitions most workgroups of short sequences have nothing
   // to do; those leave before loading anything else.
-  const int ctx_raw = p.context_lens[s];
+  // With a plan, the length and the first block come from it; the kernel
+  // still reads both from context_lens and the table, off the path of the
+  // first loads, and poisons the row if the plan does not match them.
+  const int ctx_raw = planned ? plan_ctx : p.context_lens[s];
   if (p.num_partitions > 1 && p.seq_prefix == nullptr && part * P >= clamp_ctx(ctx_raw, p.max_ctx)) {
     if (part == 0) write_zero_rows<uint16_t, D>(p, s, g);
     return;
   }
   const int slot_raw = p.new_slots != nullptr ? p.new_slots[s] : -1;
   const int prefix_raw = p.seq_prefix != nullptr ? p.seq_prefix[s] : 0;
-  const int blk_first = bt[min((part * P + w * kTile) / bs, p.max_blocks - 1)];
+  const int blk_idx = min((part * P + w * kTile) / bs, p.max_blocks - 1);
+  const int blk_first = planned ? plan_blk : bt[blk_idx];
+  const int ctx_check = planned ? p.context_lens[s] : 0;
+  const int blk_check = planned ? bt[blk_idx] : 0;
 
   // B operand of q.k^T: column n is q-head g*G+n (zero past the group). In
   // step c, lane group qg holds head_dim elements [32c + 8qg, 32c + 8qg + 8),
@@ -688,7 +787,7 @@ void decode_mfma_kernel(DecodeParams p) {
   }
   const int t0 = start + part * P;
   if (t0 >= ctx && p.pre_m == nullptr) {
-    if (part == 0) write_zero_rows<uint16_t, D>(p, s, g);
+    if (part == 0) write_zero_rows<uint16_t, D>(p, s, g, planned && ctx_check != ctx_raw);
     return;
   }
   const int n_parts = (ctx + P - 1) / P;
@@ -951,7 +1050,8 @@ void decode_mfma_kernel(DecodeParams p) {
       for (int e = 0; e < EPL; ++e) s_o[(w * GP + h) * D + EPL * n + e] = acc[e][r] * v_scale;
     }
   }
-  const bool poisoned = __any(bad) || bad_prefix;
+  const bool stale = planned && (ctx_check != ctx_raw || (my_tiles > 0 && blk_check != blk_first));
+  const bool poisoned = __any(bad) || bad_prefix || stale;
   if (threadIdx.x == 0) s_poison = 0;
   __syncthreads();
   if (poisoned && lane == 0) s_poison = 1;
@@ -1420,9 +1520,12 @@ static hipError_t launch_mfma_d(const DecodeParams& p, hipStream_t stream) {
   dim3 grid = decode_grid(p);
   DecodeParams q = p;
   const int cus = device_compute_units();
-  q.pair_span = (p.num_partitions == 1 && p.seq_prefix == nullptr && p.num_seqs <= kRankMaxSeqs &&
-                 cus <= kRankMaxSeqs)
-                    ? cus : 0;
+  if (p.plan != nullptr)
+    q.pair_span = cus;   // the plan holds the ranks: no limit from ranking in LDS
+  else
+    q.pair_span = (p.num_partitions == 1 && p.seq_prefix == nullptr && p.num_seqs <= kRankMaxSeqs &&
+                   cus <= kRankMaxSeqs)
+                      ? cus : 0;
   const int64_t items = (int64_t)p.num_seqs * p.num_kv_heads;
   if (q.pair_span > 0 && items > q.pair_span && items <= 2 * (int64_t)q.pair_span)
     grid = dim3((unsigned)(2 * q.pair_span));   // a second workgroup on every unit
@@ -1441,6 +1544,11 @@ hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, hipStream_t s
 
 hipError_t launch_decode_mfma_fp8(const DecodeParams& p, int head_dim, hipStream_t stream) {
   return head_dim == 64 ? launch_mfma_d<64, true>(p, stream) : launch_mfma_d<128, true>(p, stream);
+}
+
+hipError_t launch_decode_plan(const PlanParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
 }
 
 // Compute units of the current device (queried once per device).

@@ -78,7 +78,11 @@ def _decode(lib, **over):
     (dict(part=-1, dtype=1), binding.PKV_EWORKSPACE),
     (dict(part=-1, dtype=1, ws=1040, ws_bytes=1 << 30), binding.PKV_EINVAL),   # 256-byte alignment
     (dict(part=-1, dtype=1, out=1032), binding.PKV_EINVAL),          # out 16-byte aligned
-    (dict(part=-2), binding.PKV_EINVAL),
+    (dict(part=-3), binding.PKV_EINVAL),
+    (dict(part=-2), binding.PKV_EUNSUPPORTED),                       # planned needs the MFMA kernel
+    (dict(part=-2, dtype=1), binding.PKV_EWORKSPACE),                # ... and its plan
+    (dict(part=-2, dtype=1, ws=1024, ws_bytes=4 * 32 - 1), binding.PKV_EWORKSPACE),
+    (dict(part=-2, dtype=1, ws=1032, ws_bytes=1 << 20), binding.PKV_EINVAL),   # 16-byte alignment
 ])
 def test_decode_rejects(over, code):
     lib = pkv.lib()
@@ -89,6 +93,48 @@ def test_decode_rejects(over, code):
 @needs_lib
 def test_decode_empty_batch_is_a_no_op():
     assert _decode(pkv.lib(), S=0, out=None, q=None) == binding.PKV_OK
+
+
+def _plan(lib, **over):
+    a = dict(plan=1024, plan_bytes=1 << 20, bt=1024, cl=1024, S=4, MB=16, max_ctx=256, bs=16, stream=None)
+    a.update(over)
+    return lib.pkv_decode_plan(a["plan"], a["plan_bytes"], a["bt"], a["cl"], a["S"], a["MB"], a["max_ctx"],
+                               a["bs"], a["stream"])
+
+
+@needs_lib
+@pytest.mark.parametrize("over,code", [
+    (dict(S=-1), binding.PKV_EINVAL),
+    (dict(S=70000), binding.PKV_EINVAL),
+    (dict(bs=8), binding.PKV_EUNSUPPORTED),
+    (dict(bs=512), binding.PKV_EUNSUPPORTED),
+    (dict(MB=0), binding.PKV_EINVAL),
+    (dict(max_ctx=257), binding.PKV_EINVAL),
+    (dict(plan=None), binding.PKV_EINVAL),
+    (dict(cl=None), binding.PKV_EINVAL),
+    (dict(plan_bytes=4 * 32 - 4), binding.PKV_EWORKSPACE),
+    (dict(plan=1032), binding.PKV_EINVAL),
+    (dict(cl=1026), binding.PKV_EINVAL),
+])
+def test_plan_rejects(over, code):
+    lib = pkv.lib()
+    assert _plan(lib, **over) == code
+    assert lib.pkv_last_error()
+
+
+@needs_lib
+def test_plan_empty_batch_is_a_no_op():
+    assert _plan(pkv.lib(), S=0, plan=None, bt=None, cl=None) == binding.PKV_OK
+
+
+@needs_lib
+def test_plan_size():
+    lib = pkv.lib()
+    # eight int32 per sequence: sequence, length, four first blocks, two spare
+    assert pkv.decode_plan_size(60) == 60 * 32
+    assert lib.pkv_decode_plan_size(0) == 0
+    assert pkv.decode_workspace_size(60, 16, 8, 128, 1024, "planned") == 60 * 32
+    assert pkv.decode_workspace_size(60, 16, 8, 128, 1024, binding.PARTITION_PLANNED) == 60 * 32
 
 
 @needs_lib
