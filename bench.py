@@ -567,7 +567,7 @@ def summarize_pmc(fetch_csv, write_csv):
     fr, fw = read_known / f_cal, write_known / w_cal
     wl = W.qwen3_decode(device="cpu", layers=1)
     out = {
-        "kernel": "decode_mfma_kernel (single pass, store of the 60 new rows fused), qwen3-shaped layer",
+        "kernel": "decode_mfma_kernel (planned single pass, store of the 60 new rows fused), qwen3-shaped layer",
         "decode_source_hash": decode_source_hash(),
         "fetch_bytes_raw_per_launch": float(np.mean(f_dec)),
         "write_bytes_raw_per_launch": float(np.mean(w_dec)),
@@ -591,8 +591,8 @@ def traffic_markdown(t):
     c = t["calibration"]
     return f"""# HBM traffic of the decode kernel, Qwen3-shaped layer
 
-Kernel: `decode_mfma_kernel<128, 4>` (single pass, the store of the 60 new K/V rows fused into it,
-as the benchmark's step launches it), one layer of the Qwen3-0.6B-shaped decode step
+Kernel: `decode_mfma_kernel<128, 4>` (single pass with items in the order of the step's plan, the
+store of the 60 new K/V rows fused into it, as the benchmark's step launches it), one layer of the Qwen3-0.6B-shaped decode step
 (60 sequences, contexts U{{64..1024}}, 16 q / 8 kv heads, head_dim 128, block_size 16, bf16),
 {t['launches_averaged']} launches on distinct layer caches (4.7 GB in total, so the 256 MB last-level cache
 cannot hold them).
