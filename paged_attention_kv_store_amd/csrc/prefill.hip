@@ -36,8 +36,6 @@
 #include "common.h"
 #include "device_utils.h"
 
-#include <type_traits>
-
 namespace pkv {
 
 namespace {
@@ -320,7 +318,12 @@ void prefill_kernel(PrefillParams p) {
         for (int s = 0; s < 4; ++s) kf[h][s] = bit_cast_to<bf16x8_t>(sk[swz_k(tb + 16 * h + n, 4 * s + qg)]);
       const int keyq = kv0 + tb + 4 * qg;   // key of slot 0
       const bool full = kv0 + tb + 32 <= lim_wave;   // no key of the block is masked for this wave
-      bf16x8_t pa[2];
+      // P of both tiles; a tile without a live row keeps zero weights, so
+      // the P.V steps below run for both tiles without a variant for one
+      // (its rows are never written). One instruction sequence for every
+      // wave also keeps the accumulators in place: a variant per tile count
+      // cost register copies on the common path.
+      bf16x8_t pa[2] = {bit_cast_to<bf16x8_t>(make_uint4(0, 0, 0, 0)), bit_cast_to<bf16x8_t>(make_uint4(0, 0, 0, 0))};
       bool grow[2] = {false, false};          // the tile's reference max rises (wave-uniform)
       float alpha[2];                         // and the factor of the lane's softmax row
 #pragma unroll
@@ -385,21 +388,16 @@ void prefill_kernel(PrefillParams p) {
         vd[u][3] = v.w;
       }
       // step i: B column n = V[the lane's 8 keys][8n + i]
-      auto pv = [&](auto both) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
-          uint32_t b[4];
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+        uint32_t b[4];
 #pragma unroll
-          for (int h = 0; h < 4; ++h) b[h] = __builtin_amdgcn_perm(vd[2 * h + 1][i / 2], vd[2 * h][i / 2], sel);
-          const bf16x8_t vb = bit_cast_to<bf16x8_t>(make_uint4(b[0], b[1], b[2], b[3]));
-          acc[0][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[0], vb, acc[0][i], 0, 0, 0);
-          if constexpr (decltype(both)::value)
-            acc[1][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[1], vb, acc[1][i], 0, 0, 0);
-        }
-      };
-      if (live1) pv(std::true_type{});
-      else pv(std::false_type{});
+        for (int h = 0; h < 4; ++h) b[h] = __builtin_amdgcn_perm(vd[2 * h + 1][i / 2], vd[2 * h][i / 2], sel);
+        const bf16x8_t vb = bit_cast_to<bf16x8_t>(make_uint4(b[0], b[1], b[2], b[3]));
+        acc[0][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[0], vb, acc[0][i], 0, 0, 0);
+        acc[1][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[1], vb, acc[1][i], 0, 0, 0);
+      }
     }
     wait_loads();
     if (FP8 && more) store8(buf ^ 1);
