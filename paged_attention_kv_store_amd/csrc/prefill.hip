@@ -24,8 +24,10 @@
 //    rescaling), P rounded to bf16;
 //  * O += P V on 16x16x32 bf16 MFMA over 32 keys at a time: the scores of
 //    two 16-key tiles are already laid out as the A operand (8 keys per
-//    lane); the B operand (the same 8 keys of one column per lane) comes from
-//    whole V rows read from LDS with four in-lane byte permutes.
+//    lane); the B operand (the same 8 keys of one column per lane) comes
+//    from two transposing LDS reads (ds_read_b64_tr_b16), which hand each
+//    lane four key rows of one column from the row-major V tile. Output
+//    column block c of the accumulator holds columns 16c .. 16c+15.
 //
 // E4M3 caches (FP8 = true): the same kernel with a register-staged gather:
 // each lane fetches 16 codes of a row, and once they have landed converts
@@ -49,10 +51,12 @@ constexpr int kRowPieces = kD * 2 / 16;   // 16-byte pieces per K/V row (16)
 constexpr int kXcds = 8;              // accelerator complex dies, each with its own L2
 
 // LDS position (in 16-byte units) of piece c of key row t in a tile: piece
-// c ^ sk(t) for K, c ^ sv(t) for V, where sk(t) = t mod 16 and sv swaps the
-// two 2-bit halves of t mod 16.
+// c ^ sk(t) for K, c ^ sv(t) for V, where sk(t) = t mod 16 and sv(t) =
+// 2 (t mod 8) + bit 3 of t. A transposing read of V takes 32 bytes (two
+// pieces 2c', 2c'+1) from each of 8 rows per half-wave: sv / 2 = t mod 8
+// puts those 8 rows on 8 different bank groups.
 __device__ __forceinline__ int k_swizzle(int t) { return t & 15; }
-__device__ __forceinline__ int v_swizzle(int t) { return ((t & 3) << 2) | ((t >> 2) & 3); }
+__device__ __forceinline__ int v_swizzle(int t) { return ((t & 7) << 1) | ((t >> 3) & 1); }
 __device__ __forceinline__ int swz_k(int t, int c) { return t * kRowPieces + (c ^ k_swizzle(t)); }
 __device__ __forceinline__ int swz_v(int t, int c) { return t * kRowPieces + (c ^ v_swizzle(t)); }
 
@@ -257,7 +261,7 @@ void prefill_kernel(PrefillParams p) {
   auto wait_loads = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };
 
   float m_ref[2] = {neg_inf(), neg_inf()};   // per softmax row (lane's n), scaled units
-  f32x4_t acc[2][8];                          // acc[t][i][r] = O[row 16t + 4qg + r][8n + i]
+  f32x4_t acc[2][8];                          // acc[t][c][r] = O[row 16t + 4qg + r][16c + n]
   f32x4_t lsum[2];                            // lsum[t][r]   = sum of P over row 16t + 4qg + r
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
@@ -276,6 +280,14 @@ void prefill_kernel(PrefillParams p) {
   const bool live0 = r0 + (32 * w) / G < L;
   const bool live1 = r0 + (32 * w + 16) / G < L;
 
+  // byte offset, within key row kb + n / 4 of a V tile, of the 8-byte piece
+  // lane n reads for column block c: columns 16c + 4(n % 4), i.e. half n % 2
+  // of 16-byte piece 2c + (n % 4) / 2, at its swizzled place (the row's
+  // swizzle depends on the row mod 16 = 4qg + n / 4 for both reads)
+  int vtr_off[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+    vtr_off[c] = (((2 * c + ((n & 3) >> 1)) ^ v_swizzle(4 * qg + (n >> 2))) * 16) + (n & 1) * 8;
   if (tid == 0) s_bad = 0;
   int ids_next[4], ids_after[4];
   if (n_kv > 0) {
@@ -377,26 +389,25 @@ void prefill_kernel(PrefillParams p) {
         }
         lsum[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[t], ones, lsum[t], 0, 0, 0);
       }
-      // V rows of the lane's 8 keys, piece n (columns 8n .. 8n+7)
-      uint32_t vd[8][4];
+      // B operands of P.V by transposing LDS reads. Within a 16-lane group
+      // a read hands lane d element d % 4 of the 8-byte pieces that lanes
+      // d / 4, d / 4 + 4, d / 4 + 8 and d / 4 + 12 address. Lane n of group
+      // qg addresses columns 16c + 4(n % 4) .. +3 of key row kb + n / 4, so
+      // it receives column 16c + n of key rows kb .. kb + 3: with kb = tb +
+      // 4qg, then kb + 16, the 8 keys of its P slots, in the same order.
+      const char* vrow = reinterpret_cast<const char*>(sv) + (tb + 4 * qg + (n >> 2)) * (kRowPieces * 16);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const uint4 v = sv[swz_v(tb + 16 * (u / 4) + 4 * qg + (u % 4), n)];
-        vd[u][0] = v.x;
-        vd[u][1] = v.y;
-        vd[u][2] = v.z;
-        vd[u][3] = v.w;
-      }
-      // step i: B column n = V[the lane's 8 keys][8n + i]
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
-        uint32_t b[4];
-#pragma unroll
-        for (int h = 0; h < 4; ++h) b[h] = __builtin_amdgcn_perm(vd[2 * h + 1][i / 2], vd[2 * h][i / 2], sel);
-        const bf16x8_t vb = bit_cast_to<bf16x8_t>(make_uint4(b[0], b[1], b[2], b[3]));
-        acc[0][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[0], vb, acc[0][i], 0, 0, 0);
-        acc[1][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[1], vb, acc[1][i], 0, 0, 0);
+      for (int c = 0; c < 8; ++c) {
+        typedef short tr4_t __attribute__((ext_vector_type(4)));
+        const char* a = vrow + vtr_off[c];
+        const tr4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) tr4_t*)(a));
+        const tr4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) tr4_t*)(a + 16 * kRowPieces * 16));
+        const bf16x8_t vb = __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo), __builtin_bit_cast(bf16x4_t, hi),
+                                                    0, 1, 2, 3, 4, 5, 6, 7);
+        acc[0][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[0], vb, acc[0][c], 0, 0, 0);
+        acc[1][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[1], vb, acc[1][c], 0, 0, 0);
       }
     }
     wait_loads();
@@ -424,11 +435,9 @@ void prefill_kernel(PrefillParams p) {
         const int qi = r0 + mr / G;
         if (qi >= L) continue;
         const int64_t row = (int64_t)(q_start + qi) * p.num_q_heads + g * G + mr % G;
-        float* po = p.part_o + row * kD + 8 * n;
-        *reinterpret_cast<float4*>(po) = make_float4(acc[t][0][r] * vsc, acc[t][1][r] * vsc,
-                                                     acc[t][2][r] * vsc, acc[t][3][r] * vsc);
-        *reinterpret_cast<float4*>(po + 4) = make_float4(acc[t][4][r] * vsc, acc[t][5][r] * vsc,
-                                                         acc[t][6][r] * vsc, acc[t][7][r] * vsc);
+        float* po = p.part_o + row * kD + n;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) po[16 * c] = acc[t][c][r] * vsc;
         if (n == 0) {
           p.part_m[row] = m;
           p.part_l[row] = poisoned ? __builtin_nanf("") : lsum[t][r];
@@ -445,12 +454,10 @@ void prefill_kernel(PrefillParams p) {
       const int qi = r0 + mr / G;
       if (qi >= L) continue;
       const float inv = poisoned ? __builtin_nanf("") : vsc / lsum[t][r];
-      uint32_t o[4];
-#pragma unroll
-      for (int h = 0; h < 4; ++h) o[h] = pack_bf16x2(acc[t][2 * h][r] * inv, acc[t][2 * h + 1][r] * inv);
       uint16_t* orow = reinterpret_cast<uint16_t*>(p.out) +
-                       ((int64_t)(q_start + qi) * p.num_q_heads + g * G + mr % G) * kD + 8 * n;
-      *reinterpret_cast<uint4*>(orow) = make_uint4(o[0], o[1], o[2], o[3]);
+                       ((int64_t)(q_start + qi) * p.num_q_heads + g * G + mr % G) * kD + n;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) orow[16 * c] = f32_to_bf16_rne(acc[t][c][r] * inv);
     }
   }
 }
