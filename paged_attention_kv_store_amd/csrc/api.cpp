@@ -440,6 +440,8 @@ static int prefill_impl(const char* fn, void* out, const void* q, const void* k_
     return fail(PKV_EUNSUPPORTED, "%s: block_size %d must be a power of two in [16, 256]", fn, block_size);
   if ((int64_t)block_size * num_kv_heads * head_dim * (fp8 ? 1 : 2) >= ((int64_t)1 << 31))
     return fail(PKV_EUNSUPPORTED, "%s: a cache block must be under 2 GiB", fn);
+  if ((int64_t)num_blocks * block_size > (int64_t)0xffffffff)
+    return fail(PKV_EUNSUPPORTED, "%s: the pool must hold fewer than 2^32 token rows", fn);
   if (max_blocks_per_seq <= 0) return fail(PKV_EINVAL, "%s: max_blocks_per_seq must be positive", fn);
   if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
     return fail(PKV_EINVAL, "%s: max_context_len outside [0, max_blocks_per_seq * block_size]", fn);
@@ -547,6 +549,8 @@ extern "C" int pkv_paged_attention_decode_shared_prefix(
     return fail(PKV_EUNSUPPORTED, "%s: block_size %d must be a power of two in [16, 256]", fn, block_size);
   if ((int64_t)block_size * num_kv_heads * head_dim * 2 >= ((int64_t)1 << 31))
     return fail(PKV_EUNSUPPORTED, "%s: a cache block must be under 2 GiB", fn);
+  if ((int64_t)num_blocks * block_size > (int64_t)0xffffffff)
+    return fail(PKV_EUNSUPPORTED, "%s: the pool must hold fewer than 2^32 token rows", fn);
   if (max_blocks_per_seq <= 0) return fail(PKV_EINVAL, "%s: max_blocks_per_seq must be positive", fn);
   if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
     return fail(PKV_EINVAL, "%s: max_context_len outside [0, max_blocks_per_seq * block_size]", fn);

@@ -209,7 +209,9 @@ void prefill_kernel(PrefillParams p) {
       }
       const int t = 16 * i + lrow;
       const int pos = min(kv0 + t, ctx - 1);
-      const int64_t off = (((int64_t)blk << lbs) + (pos & (bs - 1))) * row_bytes;
+      // pool rows fit 32 bits (checked on the host): one 32 x 32 -> 64-bit multiply
+      const uint32_t row = ((uint32_t)blk << lbs) + (uint32_t)(pos & (bs - 1));
+      const uint64_t off = (uint64_t)row * (uint64_t)(uint32_t)row_bytes;
       const int lds_pos = (16 * i + 4 * w) * kRowPieces;
       __builtin_amdgcn_global_load_lds(
           (const void __attribute__((address_space(1)))*)(kbase + off + ((lane & 15) ^ k_swizzle(t)) * 16),

@@ -209,6 +209,7 @@ def _prefill(lib, **over):
     (dict(maxq=300, max_ctx=256), binding.PKV_EINVAL),
     (dict(cu=None), binding.PKV_EINVAL),
     (dict(out=1030), binding.PKV_EINVAL),
+    (dict(NB=1 << 28, bs=32), binding.PKV_EUNSUPPORTED),        # 2^33 pool rows
 ])
 def test_prefill_rejects(over, code):
     lib = pkv.lib()
