@@ -394,6 +394,28 @@ def secondary(device, steps, warmup, algo, bf16_step_ms, partition=0):
     t_store = time_region(store, steps, warmup)
     t_pre = time_region(prefill, steps, warmup)
     t_dec = time_region(dec, steps, warmup)
+
+    def serial():
+        store()
+        prefill()
+        dec()
+    # the same batch with the prefill chunks and the decode sequences on two
+    # streams (default priority), both after the store
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def two_streams():
+        cur = torch.cuda.current_stream()
+        store()
+        sa.wait_stream(cur)
+        sb.wait_stream(cur)
+        with torch.cuda.stream(sa):
+            prefill()
+        with torch.cuda.stream(sb):
+            dec()
+        cur.wait_stream(sa)
+        cur.wait_stream(sb)
+    t_serial = time_region(serial, steps, warmup)
+    t_two = time_region(two_streams, steps, warmup)
     t_dec_bal = balanced_ms(db, torch.as_tensor(db.pool.block_tables, device=device),
                             torch.as_tensor(db.pool.context_lens, device=device), steps, warmup)
     t_dec_plan = planned_ms(db, torch.as_tensor(db.pool.block_tables, device=device),
@@ -404,7 +426,9 @@ def secondary(device, steps, warmup, algo, bf16_step_ms, partition=0):
                     "prefill_mfma_util_pct": 100 * fl / t_pre / 1e9 / BF16_MFMA_PEAK_TFLOPS,
                     "decode_ms": t_dec, "decode_GBps": decode_bytes(db) / t_dec / 1e6,
                     "decode_balanced_ms": t_dec_bal, "decode_planned_ms": t_dec_plan,
-                    "tokens_per_s": 4224 / ((t_store + t_pre + t_dec) * 1e-3)}
+                    "tokens_per_s": 4224 / ((t_store + t_pre + t_dec) * 1e-3),
+                    "serial_step_ms": t_serial, "two_stream_step_ms": t_two,
+                    "tokens_per_s_two_streams": 4224 / (t_two * 1e-3)}
     del store, prefill, dec, wl, pre, db
     torch.cuda.empty_cache()
     # the same chunked prefill over E4M3 caches (its own draws, same lengths and tables)

@@ -209,6 +209,48 @@ def test_mixed_decode_part_full():
     assert_close(got[seqs], want, torch.bfloat16, "mixed decode")
 
 
+@pytest.mark.slow
+def test_mixed_prefill_and_decode_on_two_streams_match_serial():
+    """The mixed batch with its prefill chunks and decode sequences on two
+    streams (after the store) gives the bits of the serial run."""
+    wl = W.mixed(device="cuda")
+    pre, dec = wl.prefill, wl.batches[0]
+    store = pkv.StoreLaunch(pre.k_new, pre.v_new, pre.k_cache, pre.v_cache, pre.slot_mapping)
+    outs = {}
+    for mode in ("serial", "two"):
+        po = torch.full_like(pre.q, float("nan"))
+        do = torch.full_like(dec.q, float("nan"))
+        prefill = pkv.PrefillLaunch(po, pre.q, pre.k_cache, pre.v_cache,
+                                    torch.as_tensor(pre.pool.block_tables, device="cuda"),
+                                    torch.as_tensor(pre.cu_seqlens_q, device="cuda"),
+                                    torch.as_tensor(pre.pool.context_lens, device="cuda"), pre.scale,
+                                    int(np.diff(pre.cu_seqlens_q).max()), pre.max_ctx, causal=True)
+        decode = pkv.DecodeLaunch(do, dec.q, dec.k_cache, dec.v_cache,
+                                  torch.as_tensor(dec.pool.block_tables, device="cuda"),
+                                  torch.as_tensor(dec.pool.context_lens, device="cuda"), dec.scale, dec.max_ctx)
+        torch.cuda.synchronize()
+        store()
+        if mode == "serial":
+            prefill()
+            decode()
+        else:
+            cur = torch.cuda.current_stream()
+            sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+            sa.wait_stream(cur)
+            sb.wait_stream(cur)
+            with torch.cuda.stream(sa):
+                prefill()
+            with torch.cuda.stream(sb):
+                decode()
+            cur.wait_stream(sa)
+            cur.wait_stream(sb)
+        torch.cuda.synchronize()
+        outs[mode] = (po, do)
+    assert torch.isfinite(outs["serial"][0].float()).all() and torch.isfinite(outs["serial"][1].float()).all()
+    for a, b in zip(outs["serial"], outs["two"]):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
 # --------------------------------------------------------------------------
 # store fused into decode
 # --------------------------------------------------------------------------
