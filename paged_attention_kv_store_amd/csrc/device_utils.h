@@ -67,13 +67,14 @@ __device__ __forceinline__ float max8(const float (&x)[8]) {
   return mx(mx(mx(x[0], x[1]), mx(x[2], x[3])), mx(mx(x[4], x[5]), mx(x[6], x[7])));
 }
 
-// Two bf16 words holding the exact values of the four E4M3 codes of w
-// (hardware E4M3 -> f32 conversion; every E4M3 value is a bf16 value, so the
-// nearest-even bf16 packing is exact).
+// Two bf16 words holding the exact values of the four E4M3 codes of w (every
+// E4M3 value is a bf16 value). gfx950's scaled conversion goes straight to
+// packed bf16, scale 1; checked on the GPU to give, for all 256 codes, the
+// bits of the E4M3 -> f32 conversion followed by the nearest-even bf16 pack.
 __device__ __forceinline__ uint2 e4m3x4_to_bf16(uint32_t w) {
-  const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-  const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
-  return make_uint2(pack_bf16x2(lo.x, lo.y), pack_bf16x2(hi.x, hi.y));
+  const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+  return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
 }
 
 // ---- E4M3 quantisation (the cache format's reading) ------------------------
