@@ -172,6 +172,31 @@ def test_planned_decode_store_fp8():
     assert_close(out.float().cpu().double().numpy(), want, torch.bfloat16, "planned fp8")
 
 
+def test_planned_decode_past_the_in_kernel_ranking_limit():
+    """5000 sequences: more than the 4096 the kernel ranks in LDS itself,
+    which the plan does not need; every row written and right."""
+    s = 5000
+    b = W.random_decode_batch(3100, s, 8, 8, 64, torch.bfloat16, max_ctx=48, min_ctx=0, store=False)
+    say(f"planned decode S={s}")
+    dev = to_device(b)
+    plan = make_plan(dev, b.max_ctx, b.block_size)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(plan_entries(plan, s),
+                                  expected_plan(b.pool.block_tables, b.pool.context_lens, b.max_ctx, b.block_size))
+    outs = {}
+    for part, ws in ((0, None), ("planned", plan)):
+        out = torch.full_like(dev["q"], float("nan"))
+        pkv.paged_attention_decode(out, dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
+                                   dev["context_lens"], b.scale, b.max_ctx, partition_size=part,
+                                   workspace=ws, algo="mfma")
+        outs[part] = out
+    torch.cuda.synchronize()
+    assert torch.equal(outs["planned"].view(torch.int16), outs[0].view(torch.int16))
+    seqs = list(range(0, s, 97)) + [s - 1]
+    want = oracle_decode(b, store=False, seqs=seqs)
+    assert_close(outs["planned"].float().cpu().double().numpy()[seqs], want, torch.bfloat16, "planned S=5000")
+
+
 def test_stale_plan_poisons_only_the_changed_sequences():
     """A plan that no longer matches the lengths or first blocks turns those
     sequences' rows into NaN; every other row equals the single-pass result."""
