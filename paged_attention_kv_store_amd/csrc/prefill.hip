@@ -330,6 +330,21 @@ void prefill_kernel(PrefillParams p) {
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int s = 0; s < 4; ++s) kf[h][s] = bit_cast_to<bf16x8_t>(sk[swz_k(tb + 16 * h + n, 4 * s + qg)]);
+      // B operands of P.V by transposing LDS reads, issued here so that their
+      // latency overlaps the softmax below
+      const char* vrow = reinterpret_cast<const char*>(sv) + (tb + 4 * qg + (n >> 2)) * (kRowPieces * 16);
+      bf16x8_t vb[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        typedef short tr4_t __attribute__((ext_vector_type(4)));
+        const char* a = vrow + vtr_off[c];
+        const tr4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) tr4_t*)(a));
+        const tr4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) tr4_t*)(a + 16 * kRowPieces * 16));
+        vb[c] = __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo), __builtin_bit_cast(bf16x4_t, hi),
+                                        0, 1, 2, 3, 4, 5, 6, 7);
+      }
       const int keyq = kv0 + tb + 4 * qg;   // key of slot 0
       const bool full = kv0 + tb + 32 <= lim_wave;   // no key of the block is masked for this wave
       // P of both tiles; a tile without a live row keeps zero weights, so
@@ -391,25 +406,11 @@ void prefill_kernel(PrefillParams p) {
         }
         lsum[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[t], ones, lsum[t], 0, 0, 0);
       }
-      // B operands of P.V by transposing LDS reads. Within a 16-lane group
-      // a read hands lane d element d % 4 of the 8-byte pieces that lanes
-      // d / 4, d / 4 + 4, d / 4 + 8 and d / 4 + 12 address. Lane n of group
-      // qg addresses columns 16c + 4(n % 4) .. +3 of key row kb + n / 4, so
-      // it receives column 16c + n of key rows kb .. kb + 3: with kb = tb +
-      // 4qg, then kb + 16, the 8 keys of its P slots, in the same order.
-      const char* vrow = reinterpret_cast<const char*>(sv) + (tb + 4 * qg + (n >> 2)) * (kRowPieces * 16);
+      // O += P V for both tiles (operands read at the top of the step)
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        typedef short tr4_t __attribute__((ext_vector_type(4)));
-        const char* a = vrow + vtr_off[c];
-        const tr4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) tr4_t*)(a));
-        const tr4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) tr4_t*)(a + 16 * kRowPieces * 16));
-        const bf16x8_t vb = __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo), __builtin_bit_cast(bf16x4_t, hi),
-                                                    0, 1, 2, 3, 4, 5, 6, 7);
-        acc[0][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[0], vb, acc[0][c], 0, 0, 0);
-        acc[1][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[1], vb, acc[1][c], 0, 0, 0);
+        acc[0][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[0], vb[c], acc[0][c], 0, 0, 0);
+        acc[1][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[1], vb[c], acc[1][c], 0, 0, 0);
       }
     }
     wait_loads();
