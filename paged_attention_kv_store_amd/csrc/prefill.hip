@@ -373,9 +373,14 @@ void prefill_kernel(PrefillParams p) {
 #pragma unroll
           for (int u = 0; u < 8; ++u) x[u] = (keyq + 16 * (u / 4) + (u % 4) < lim) ? x[u] : neg_inf();
         }
-        // scale > 0 is finite, so a row max of -inf stays -inf
-        const float mt = max_across_rows(max8(x)) * scale;
-        if (__any(mt > m_ref[t] + kRescaleThreshold)) {
+        // scale > 0 is finite, so a row max of -inf stays -inf. A row's
+        // maximum clears the threshold exactly when the maximum of one of
+        // its four lanes does, so each lane tests its own and the row's
+        // maximum (a reduction across the lanes) is formed only when some
+        // reference rises.
+        const float lane_max = max8(x);
+        if (__any(lane_max * scale > m_ref[t] + kRescaleThreshold)) {
+          const float mt = max_across_rows(lane_max) * scale;
           const float m_new = fmaxf(m_ref[t], mt);
           alpha[t] = (m_new == neg_inf()) ? 1.f : fast_exp2(m_ref[t] - m_new);
           m_ref[t] = m_new;
