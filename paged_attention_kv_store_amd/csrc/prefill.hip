@@ -263,6 +263,7 @@ void prefill_kernel(PrefillParams p) {
   auto wait_loads = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };
 
   float m_ref[2] = {neg_inf(), neg_inf()};   // per softmax row (lane's n), scaled units
+  float nm_ref[2] = {0.f, 0.f};               // -m_ref, or 0 while the row has seen no key
   f32x4_t acc[2][8];                          // acc[t][c][r] = O[row 16t + 4qg + r][16c + n]
   f32x4_t lsum[2];                            // lsum[t][r]   = sum of P over row 16t + 4qg + r
 #pragma unroll
@@ -384,11 +385,12 @@ void prefill_kernel(PrefillParams p) {
           const float m_new = fmaxf(m_ref[t], mt);
           alpha[t] = (m_new == neg_inf()) ? 1.f : fast_exp2(m_ref[t] - m_new);
           m_ref[t] = m_new;
+          nm_ref[t] = (m_new == neg_inf()) ? 0.f : -m_new;
           grow[t] = true;
         }
         // weight 2^(scale*x - m): a masked score (-inf) gives exactly 0, since
         // scale > 0 and m is finite (0 while the row has seen no key)
-        const float nm = (m_ref[t] == neg_inf()) ? 0.f : -m_ref[t];
+        const float nm = nm_ref[t];
         uint32_t pw[4];
 #pragma unroll
         for (int h = 0; h < 4; ++h)
