@@ -273,7 +273,7 @@ void prefill_kernel(PrefillParams p) {
     for (int i = 0; i < 8; ++i) acc[t][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
   // bf16 ones: P times a ones column gives the row sums of the rounded weights
-  const bf16x8_t ones = bit_cast_to<bf16x8_t>(make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
+  bf16x8_t ones = bit_cast_to<bf16x8_t>(make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
   // keys below this bound are visible to every row of the wave
   const int lim_wave = p.causal ? min(P0 + r0 + (32 * w) / G + 1, ctx) : ctx;
   // Whether M-row tile t of the wave holds a live query row (wave-uniform).
@@ -316,6 +316,10 @@ void prefill_kernel(PrefillParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) ids_next[i] = ids_after[i];
     const int kv0 = kt * kKvTile;
+    // an empty asm that claims to modify the ones operand keeps its four
+    // registers resident; otherwise the compiler rebuilds the tuple with
+    // three moves before every row-sum step
+    asm volatile("" : "+v"(ones));
     const uint4* sk = s_k[buf];
     const uint4* sv = s_v[buf];
 
