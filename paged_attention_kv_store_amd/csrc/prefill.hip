@@ -38,6 +38,8 @@
 #include "common.h"
 #include "device_utils.h"
 
+#include <type_traits>
+
 namespace pkv {
 
 namespace {
@@ -304,8 +306,11 @@ void prefill_kernel(PrefillParams p) {
   if (FP8 && n_kv > 0) store8(0);
   __syncthreads();
 
-  for (int kt = 0; kt < n_kv; ++kt) {
-    const int buf = kt & 1;
+  // The tile loop runs two tiles per trip, one per LDS buffer, so that each
+  // copy of the body knows its buffer at compile time and the buffer offset
+  // folds into the LDS instructions' immediate fields.
+  auto tile_step = [&](int kt, auto buf_tag) {
+    constexpr int buf = decltype(buf_tag)::value;
     const bool more = kt + 1 < n_kv;
     tile_blocks(kt + 2, ids_after);
     // the other buffer was last read before the previous barrier
@@ -427,6 +432,10 @@ void prefill_kernel(PrefillParams p) {
     wait_loads();
     if (FP8 && more) store8(buf ^ 1);
     __syncthreads();
+  };
+  for (int kt = 0; kt < n_kv; kt += 2) {
+    tile_step(kt, std::integral_constant<int, 0>{});
+    if (kt + 1 < n_kv) tile_step(kt + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- normalise and write ------------------------------------------------
