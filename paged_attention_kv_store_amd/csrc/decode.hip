@@ -909,10 +909,14 @@ void decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) x[r] = (tokq + r < t1) ? sc[r] * logit_scale : neg_inf();
     // max over the tile's 16 tokens: the lane's four, then across the lane
-    // groups qg (row swaps, no LDS round trip); NaN-propagating
-    const float mt = max_across_rows(__builtin_elementwise_maximum(__builtin_elementwise_maximum(x[0], x[1]),
-                                                                   __builtin_elementwise_maximum(x[2], x[3])));
-    if (__any(mt > m_ref + kRescaleThreshold)) {
+    // groups qg (row swaps, no LDS round trip); NaN-propagating. A head's
+    // maximum clears the threshold exactly when one of its four lanes'
+    // maxima does, so the reduction across lanes runs only when a
+    // reference rises.
+    const float lane_max = __builtin_elementwise_maximum(__builtin_elementwise_maximum(x[0], x[1]),
+                                                         __builtin_elementwise_maximum(x[2], x[3]));
+    if (__any(lane_max > m_ref + kRescaleThreshold)) {
+      const float mt = max_across_rows(lane_max);
       const float m_new = fmaxf(m_ref, mt);
       const float alpha = fast_exp2(m_ref - m_new);
       l_part *= alpha;
