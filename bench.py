@@ -142,6 +142,18 @@ def time_region(fn, steps, warmup):
     return start.elapsed_time(end) / steps   # ms
 
 
+def time_each_step(fn, steps):
+    """Milliseconds of each of `steps` calls, one HIP event pair around each."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, z in evs:
+        a.record()
+        fn()
+        z.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(z) for a, z in evs]
+
+
 def gpu_hold(ms):
     """Keep the stream busy for about `ms` so that the launches queued behind
     it run back to back, independent of host launch latency."""
@@ -279,9 +291,19 @@ def cpu_baseline(b: W.PagedBatch, budget_s=12.0):
     finally:
         if limiter is not None:
             limiter.__exit__(None, None, None)
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
     return {"value": done_bytes / t_used / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{seqs} sequence decodes (layer 0's {b.num_seqs} sequences, cycled) by the "
-                      f"float64 oracle in {t_used:.1f} s on one host core ({seqs / t_used:.1f} seq/s)"}
+                      f"float64 oracle in {t_used:.1f} s on one host core of a {model} "
+                      f"({seqs / t_used:.1f} seq/s)"}
 
 
 # --------------------------------------------------------------------------
@@ -427,6 +449,7 @@ def secondary(device, steps, warmup, algo, bf16_step_ms, partition=0):
                     "decode_ms": t_dec, "decode_GBps": decode_bytes(db) / t_dec / 1e6,
                     "decode_balanced_ms": t_dec_bal, "decode_planned_ms": t_dec_plan,
                     "tokens_per_s": 4224 / ((t_store + t_pre + t_dec) * 1e-3),
+                    "prefill_tokens_per_s": 4096 / (t_pre * 1e-3),
                     "serial_step_ms": t_serial, "two_stream_step_ms": t_two,
                     "tokens_per_s_two_streams": 4224 / (t_two * 1e-3)}
     del store, prefill, dec, wl, pre, db
@@ -756,6 +779,7 @@ def main():
     log(f"timing {args.steps} steps ({len(lyr)} layers each) after {args.warmup} warmup")
     ms = time_region(run, args.steps, args.warmup)
     value = step_bytes / (ms * 1e-3) / 1e9
+    per_step = sorted(time_each_step(run, args.steps))
 
     # dominant kernel: decode (fused with the store unless --unfused), one launch per layer
     dec_bytes = decode_bytes(b0) + (0.0 if args.unfused else store_bytes(b0))
@@ -788,6 +812,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_median_min_max": [round(float(np.median(per_step)), 4), round(per_step[0], 4),
+                                       round(per_step[-1], 4)],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
