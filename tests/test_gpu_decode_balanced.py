@@ -200,31 +200,3 @@ def test_decode_store_fused_skips_negative_slots():
     assert_close(got[live], oracle_decode(b, caches=(kc, vc), seqs=live), torch.bfloat16, "stored rows")
     # the padded sequences read their (poisoned) newest row from the cache
     assert np.isnan(got[::4]).all()
-
-
-# --------------------------------------------------------------------------
-# the standard workloads at full size
-# --------------------------------------------------------------------------
-
-@pytest.mark.slow
-def test_qwen3_decode_full_layer():
-    b = W.qwen3_decode(layers=1).batches[0]
-    assert_close(gpu_decode(b, algo="mfma", partition_size=BAL), oracle_decode(b), torch.bfloat16,
-                 "qwen3 balanced")
-
-
-@pytest.mark.slow
-def test_llama_prefix_full_sampled():
-    b = W.llama_prefix().batches[0]
-    seqs = list(range(0, 256, 9)) + [255]
-    got = gpu_decode(b, algo="mfma", partition_size=BAL, store=False)
-    assert_close(got[seqs], oracle_decode(b, seqs=seqs, store=False), torch.bfloat16, "llama balanced")
-
-
-@pytest.mark.slow
-def test_long_splitk_full_sampled():
-    b = W.long_splitk().batches[0]
-    order = np.argsort(b.pool.context_lens)
-    seqs = sorted(set(order[:3].tolist() + order[-3:].tolist() + [7, 15]))
-    got = gpu_decode(b, algo="mfma", partition_size=BAL, store=False)
-    assert_close(got[seqs], oracle_decode(b, seqs=seqs, store=False), torch.bfloat16, "long balanced")

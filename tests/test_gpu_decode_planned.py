@@ -192,9 +192,8 @@ def test_planned_decode_past_the_in_kernel_ranking_limit():
         outs[part] = out
     torch.cuda.synchronize()
     assert torch.equal(outs["planned"].view(torch.int16), outs[0].view(torch.int16))
-    seqs = list(range(0, s, 97)) + [s - 1]
-    want = oracle_decode(b, store=False, seqs=seqs)
-    assert_close(outs["planned"].float().cpu().double().numpy()[seqs], want, torch.bfloat16, "planned S=5000")
+    assert_close(outs["planned"].float().cpu().double().numpy(), oracle_decode(b, store=False), torch.bfloat16,
+                 "planned S=5000")
 
 
 def test_stale_plan_poisons_only_the_changed_sequences():
@@ -287,20 +286,3 @@ def test_qwen3_layer_planned_store():
     assert_close(out.float().cpu().double().numpy(), oracle_decode(b, caches=(kc, vc)), torch.bfloat16,
                  "qwen3 planned")
 
-
-@pytest.mark.slow
-def test_llama_prefix_and_mixed_planned_sampled():
-    """More items than two per compute unit (256 x 8 and 128 x 8)."""
-    b = W.llama_prefix().batches[0]
-    dev = to_device(b)
-    plan = make_plan(dev, b.max_ctx, b.block_size)
-    out = torch.full_like(dev["q"], float("nan"))
-    pkv.paged_attention_decode(out, dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
-                               dev["context_lens"], b.scale, b.max_ctx, partition_size="planned",
-                               workspace=plan)
-    torch.cuda.synchronize()
-    seqs = list(range(0, 256, 11)) + [255]
-    want = oracle_decode(b, caches=oracle_caches(b, store=False), seqs=seqs)
-    got = out.float().cpu().double().numpy()
-    assert np.isfinite(got).all()
-    assert_close(got[seqs], want, torch.bfloat16, "llama planned")

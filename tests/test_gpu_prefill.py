@@ -114,28 +114,6 @@ def test_out_of_pool_block_poisons_its_chunk():
         assert_close(got[cu[c]:cu[c + 1]], want[cu[c]:cu[c + 1]], torch.bfloat16, f"chunk {c}")
 
 
-@pytest.mark.slow
-def test_mixed_prefill_full_sampled_rows():
-    wl = W.mixed()
-    b = wl.prefill
-    say(f"mixed prefill: ctx={b.pool.context_lens.tolist()}")
-    got = gpu_prefill(b)
-    kc, vc = oracle_caches(b)
-    # oracle on a sample of rows of every chunk: first, last, and a stride
-    cu = b.cu_seqlens_q
-    q = W.host_bits(b.q)
-    for c in range(8):
-        rows = sorted({0, 1, 63, 64, 255, 511} | set(range(7, 512, 97)))
-        ctx = int(b.pool.context_lens[c])
-        prior = ctx - 512
-        for i in rows:
-            # row i of chunk c equals decode over the first prior + i + 1 keys
-            want = oracle.paged_attention_decode(q[cu[c] + i][None], kc, vc,
-                                                 b.pool.block_tables[c:c + 1],
-                                                 np.array([prior + i + 1]), b.scale, 16)
-            assert_close(got[cu[c] + i][None], want, torch.bfloat16, f"chunk {c} row {i}")
-
-
 SHORT = [
     # (hq, hkv, rows): verification of rows-1 drafted tokens, every GQA group
     (32, 8, 2), (32, 8, 4), (32, 8, 8), (16, 8, 3), (8, 8, 5), (32, 4, 7), (8, 1, 6),
@@ -171,18 +149,3 @@ def test_short_chunks_match_decode_over_each_prefix(case):
     assert_close(got, want, torch.bfloat16, "chunk vs per-row decode oracle")
     assert cu[-1] == len(row_ctx)
 
-
-@pytest.mark.slow
-def test_spec_verify_full_sampled_seqs():
-    b = W.spec_verify().prefill
-    say(f"spec_verify: {b.num_seqs} seqs x 4 rows")
-    got = gpu_prefill(b)
-    kc, vc = oracle_caches(b)
-    q = W.host_bits(b.q)
-    cu, ctx = b.cu_seqlens_q, b.pool.context_lens
-    for c in sorted({0, 1, 63, 127} | set(range(5, 128, 11))):
-        want = oracle.paged_attention_prefill_chunk(q[cu[c]:cu[c + 1]], kc, vc,
-                                                    b.pool.block_tables[c:c + 1],
-                                                    np.array([0, 4], np.int32),
-                                                    ctx[c:c + 1], b.scale, 16)
-        assert_close(got[cu[c]:cu[c + 1]], want, torch.bfloat16, f"seq {c}")

@@ -74,11 +74,3 @@ def test_out_of_pool_block_in_the_prefix_poisons_the_group():
     assert np.isnan(got[4:]).all()
     assert_close(got[:4], oracle_decode(b, seqs=[0, 1, 2, 3], store=False), torch.bfloat16, "good group")
 
-
-@pytest.mark.slow
-def test_llama_prefix_full_sampled():
-    b = W.llama_prefix().batches[0]
-    starts = np.arange(0, 257, 8)
-    got = run_shared(b, starts, [32 * 16] * 32)
-    seqs = list(range(0, 256, 9)) + [255]
-    assert_close(got[seqs], oracle_decode(b, seqs=seqs, store=False), torch.bfloat16, "llama shared")
