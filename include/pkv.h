@@ -226,6 +226,37 @@ int pkv_paged_attention_decode_store(void* out, const void* q, void* k_cache, vo
                                      pkv_dtype dtype, int32_t algo, void* stream);
 
 /*
+ * paged_attention_decode_static: pkv_paged_attention_decode for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc). It takes no workspace and calls no
+ * allocating routine: the split-K and work-balanced modes keep their partial
+ * results and arrival counters in a scratch array that the library holds on
+ * each device it runs on (PKV_STATIC_SCRATCH_BYTES, created with the
+ * library's device code on that device and held until the process ends).
+ * Each call first clears the arrival counters it uses, with a kernel on
+ * `stream`, then runs the decode; its results are those of
+ * pkv_paged_attention_decode with the same arguments and a workspace.
+ *   partition_size: 0, a positive multiple of 16 or PKV_PARTITION_BALANCED
+ *   (PKV_PARTITION_PLANNED reads a caller's plan: PKV_EINVAL).
+ * Errors: those of pkv_paged_attention_decode, and PKV_EWORKSPACE, before any
+ * launch, when pkv_decode_workspace_size(...) for these arguments exceeds
+ * PKV_STATIC_SCRATCH_BYTES.
+ * Every call on a device shares that device's scratch, which keeps the last
+ * call's contents: calls that overlap in time on one device (on different
+ * streams, or from threads without ordering between them) race and give
+ * unspecified results. Calls on one stream are ordered and safe.
+ */
+#define PKV_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+int pkv_paged_attention_decode_static(void* out, const void* q, const void* k_cache,
+                                      const void* v_cache, const int32_t* block_tables,
+                                      const int32_t* context_lens, int32_t num_seqs,
+                                      int32_t max_blocks_per_seq, int32_t max_context_len,
+                                      int32_t num_blocks, int32_t block_size, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim, float scale,
+                                      int32_t partition_size, pkv_dtype dtype, int32_t algo,
+                                      void* stream);
+
+/*
  * E4M3 KV cache. The pages list support for quantized models among the
  * engine's features ("A vLLM engine small enough to read in one sitting",
  * section "Key highlights"); the format and scaling are this library's

@@ -32,6 +32,7 @@ from .binding import (  # noqa: F401
     paged_attention_decode,
     paged_attention_decode_fp8,
     paged_attention_decode_shared_prefix,
+    paged_attention_decode_static,
     paged_attention_decode_store,
     paged_attention_decode_store_fp8,
     paged_attention_prefill_chunk,

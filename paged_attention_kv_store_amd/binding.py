@@ -24,6 +24,7 @@ PKV_F32, PKV_BF16 = 0, 1
 DECODE_ALGOS = {"auto": 0, "valu": 1, "mfma": 2}
 PARTITION_BALANCED = -1      # partition_size selecting the work-balanced decode
 PARTITION_PLANNED = -2       # partition_size selecting the planned decode (workspace = the plan)
+STATIC_SCRATCH_BYTES = 64 << 20   # PKV_STATIC_SCRATCH_BYTES: the library's per-device decode scratch
 
 _i32 = ctypes.c_int32
 _vp = ctypes.c_void_p
@@ -41,6 +42,9 @@ _SIGNATURES = {
     "pkv_paged_attention_decode_store": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
                                           _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _i32,
                                           _vp, ctypes.c_size_t, ctypes.c_int, _i32, _vp], ctypes.c_int),
+    "pkv_paged_attention_decode_static": ([_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                           _i32, _i32, _i32, ctypes.c_float, _i32, ctypes.c_int, _i32, _vp],
+                                          ctypes.c_int),
     "pkv_kv_cache_store_fp8": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                 ctypes.c_int, _vp], ctypes.c_int),
     "pkv_paged_attention_decode_fp8": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
@@ -238,6 +242,29 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         s, block_tables.shape[1], int(max_context_len), nb, bs, hq, hkv, d, float(scale),
         part, _ptr(workspace), ws_bytes, _dtype_code(q), DECODE_ALGOS[algo],
         _stream(stream)))
+    return out
+
+
+def paged_attention_decode_static(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                                  max_context_len, partition_size=0, algo="auto", stream=None):
+    """paged_attention_decode without a workspace: split-K and work-balanced
+    modes use the library's own per-device scratch (PKV_STATIC_SCRATCH_BYTES),
+    so nothing is allocated. Calls that overlap in time on one device race."""
+    _dev(out, q, k_cache, v_cache, block_tables, context_lens)
+    _need(q.dim() == 3 and out.shape == q.shape and out.dtype == q.dtype, "q/out must be [S, Hq, D]")
+    _need(k_cache.dim() == 4 and v_cache.shape == k_cache.shape, "caches must be [NB, bs, Hkv, D]")
+    _need(q.dtype == k_cache.dtype == v_cache.dtype, "dtypes must match")
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
+          and block_tables.shape[0] == q.shape[0], "block_tables must be int32 [S, MB]")
+    _need(context_lens.dtype == torch.int32 and context_lens.shape == (q.shape[0],),
+          "context_lens must be int32 [S]")
+    _need(k_cache.shape[3] == q.shape[2], "head_dim mismatch")
+    s, hq, d = q.shape
+    nb, bs, hkv, _ = k_cache.shape
+    _check(lib().pkv_paged_attention_decode_static(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+        s, block_tables.shape[1], int(max_context_len), nb, bs, hq, hkv, d, float(scale),
+        _partition(partition_size), _dtype_code(q), DECODE_ALGOS[algo], _stream(stream)))
     return out
 
 

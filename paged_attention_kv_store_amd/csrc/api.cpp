@@ -162,7 +162,8 @@ int decode_impl(const char* fn, void* out, const void* q, const void* k_cache, c
                 int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                 float scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
                 int dtype, int32_t algo, void* stream, bool fp8 = false,
-                const float* k_scale = nullptr, const float* v_scale = nullptr) {
+                const float* k_scale = nullptr, const float* v_scale = nullptr,
+                bool clear_counters = false) {
   if (num_seqs < 0) return fail(PKV_EINVAL, "%s: num_seqs < 0", fn);
   if (int rc = check_common(fn, num_blocks, block_size, num_kv_heads, head_dim, dtype)) return rc;
   if (num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
@@ -292,6 +293,9 @@ int decode_impl(const char* fn, void* out, const void* q, const void* k_cache, c
     p.bal_pieces = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
                                             pkv::kBalMaxWaves * sizeof(int32_t));
     p.bal_piece_stride = (int32_t)pkv::bal_piece_stride(group, head_dim);
+    if (clear_counters)
+      if (hipError_t e = pkv::launch_zero_ints(p.bal_counters, pkv::kBalMaxWaves, st); e != hipSuccess)
+        return hip_status(e, fn);
     return hip_status(pkv::launch_decode_balanced(p, head_dim, st), fn);
   }
   if (nparts > 1) {
@@ -307,6 +311,10 @@ int decode_impl(const char* fn, void* out, const void* q, const void* k_cache, c
     p.ws_m = ws;
     p.ws_l = ws + cells;
     p.ws_o = ws + 2 * cells;
+    if (clear_counters)
+      if (hipError_t e = pkv::launch_zero_ints(p.part_counters, (int64_t)num_seqs * num_kv_heads, st);
+          e != hipSuccess)
+        return hip_status(e, fn);
   }
   hipError_t e = fp8 ? pkv::launch_decode_mfma_fp8(p, head_dim, st)
                  : algo == PKV_DECODE_MFMA ? pkv::launch_decode_mfma(p, head_dim, st)
@@ -350,6 +358,33 @@ extern "C" int pkv_paged_attention_decode_store(void* out, const void* q, void* 
                      slot_mapping, num_seqs, max_blocks_per_seq, max_context_len, num_blocks,
                      block_size, num_q_heads, num_kv_heads, head_dim, scale, partition_size,
                      workspace, workspace_bytes, dtype, algo, stream);
+}
+
+static_assert(PKV_STATIC_SCRATCH_BYTES == pkv::kStaticScratchBytes, "header and library agree on the scratch");
+
+extern "C" int pkv_paged_attention_decode_static(void* out, const void* q, const void* k_cache,
+                                                 const void* v_cache, const int32_t* block_tables,
+                                                 const int32_t* context_lens, int32_t num_seqs,
+                                                 int32_t max_blocks_per_seq, int32_t max_context_len,
+                                                 int32_t num_blocks, int32_t block_size,
+                                                 int32_t num_q_heads, int32_t num_kv_heads,
+                                                 int32_t head_dim, float scale, int32_t partition_size,
+                                                 pkv_dtype dtype, int32_t algo, void* stream) {
+  const char* fn = "pkv_paged_attention_decode_static";
+  if (partition_size == PKV_PARTITION_PLANNED)
+    return fail(PKV_EINVAL, "%s: the planned decode reads a caller's plan; use pkv_paged_attention_decode", fn);
+  const size_t need = pkv_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                max_context_len, partition_size);
+  if (need > pkv::kStaticScratchBytes)
+    return fail(PKV_EWORKSPACE, "%s: the call needs %zu bytes of scratch; the library's static scratch holds %zu",
+                fn, need, pkv::kStaticScratchBytes);
+  void* ws = nullptr;
+  if (need > 0)
+    if (hipError_t e = pkv::static_scratch(&ws); e != hipSuccess) return hip_status(e, fn);
+  return decode_impl(fn, out, q, k_cache, v_cache, block_tables, context_lens, nullptr, nullptr, nullptr,
+                     num_seqs, max_blocks_per_seq, max_context_len, num_blocks, block_size, num_q_heads,
+                     num_kv_heads, head_dim, scale, partition_size, ws, ws ? pkv::kStaticScratchBytes : 0,
+                     dtype, algo, stream, false, nullptr, nullptr, /*clear_counters=*/true);
 }
 
 extern "C" int pkv_kv_cache_store_fp8(const void* k, const void* v, void* k_cache, void* v_cache,

@@ -170,6 +170,14 @@ struct PrefillParams {
 // Compute units of the current device (queried once per device).
 int device_compute_units();
 
+// Bytes of the library-owned decode scratch (one array per device, held
+// until the process ends), and its device address on the current device.
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+hipError_t static_scratch(void** ptr);
+
+// p[0 .. n-1] = 0 with a kernel on `stream`.
+hipError_t launch_zero_ints(int32_t* p, int64_t n, hipStream_t stream);
+
 // dtype codes match pkv_dtype
 hipError_t launch_store(const StoreParams& p, hipStream_t stream);
 hipError_t launch_store_fp8(const StoreFp8Params& p, hipStream_t stream);

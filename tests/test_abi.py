@@ -269,3 +269,38 @@ def test_shared_prefix_rejects(over, code):
 @needs_lib
 def test_shared_prefix_workspace_size():
     assert pkv.lib().pkv_decode_shared_prefix_workspace_size(8, 32, 128) == 8 * 32 * 130 * 4 + 8 * 4
+
+
+def test_static_scratch_size_matches_the_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define PKV_STATIC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == binding.STATIC_SCRATCH_BYTES
+
+
+@needs_lib
+@pytest.mark.parametrize("over,code", [
+    (dict(S=4096, MB=2048, max_ctx=32768, Hq=32, Hkv=8, D=128, part=16, dtype=1, algo=2),
+     binding.PKV_EWORKSPACE),                       # split-K partials beyond the static scratch
+    (dict(part=-2), binding.PKV_EINVAL),            # the planned decode reads a caller's plan
+    (dict(S=-1, part=64), binding.PKV_EINVAL),
+    (dict(Hq=6, Hkv=4, part=64), binding.PKV_EINVAL),
+])
+def test_static_decode_rejects_on_the_host(over, code):
+    """The entry point without a workspace rejects these before any launch
+    (no device is touched: the pointers are placeholders)."""
+    a = dict(out=1024, q=1024, k=1024, v=1024, bt=1024, cl=1024, S=4, MB=16, max_ctx=256, NB=64, bs=16,
+             Hq=8, Hkv=4, D=64, scale=0.125, part=0, dtype=0, algo=0, stream=None)
+    a.update(over)
+    rc = pkv.lib().pkv_paged_attention_decode_static(
+        a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["S"], a["MB"], a["max_ctx"], a["NB"], a["bs"],
+        a["Hq"], a["Hkv"], a["D"], a["scale"], a["part"], a["dtype"], a["algo"], a["stream"])
+    assert rc == code, pkv.lib().pkv_last_error()
+    if code == binding.PKV_EWORKSPACE:
+        assert b"static scratch" in pkv.lib().pkv_last_error()
+
+
+@needs_lib
+def test_static_decode_empty_batch_is_a_no_op():
+    rc = pkv.lib().pkv_paged_attention_decode_static(None, None, None, None, None, None, 0, 16, 0, 64, 16, 8, 4,
+                                                     64, 0.125, 64, 0, 0, None)
+    assert rc == binding.PKV_OK
