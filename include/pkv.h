@@ -16,7 +16,8 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - All tensor pointers are DEVICE pointers owned by the caller; the library
- *    keeps no pointer after a call returns and allocates nothing.
+ *    keeps no pointer after a call returns and allocates nothing (the one
+ *    piece of device memory it owns is the static decode scratch below).
  *  - Layouts are dense and row-major:
  *        q, out (decode)     [num_seqs, num_q_heads, head_dim]
  *        q, out (prefill)    [total_q,  num_q_heads, head_dim]   (packed chunks)
@@ -28,7 +29,10 @@
  *        cu_seqlens_q        int32 [num_seqs + 1]
  *  - Position p of sequence s lives in physical block
  *    block_tables[s][p / block_size], row p % block_size. Table entries past
- *    ceil(context_lens[s] / block_size) are never read and may hold anything.
+ *    ceil(context_lens[s] / block_size) may hold anything: their values never
+ *    decide which cache memory is read (a kernel may load such an entry of
+ *    the row, ahead of knowing the length, and then discard it), and nothing
+ *    past the row's max_blocks_per_seq entries is ever loaded.
  *  - context_lens[s] counts every token of the sequence whose K/V is in the
  *    cache, including the rows stored in the same step; 0 yields zero output.
  *  - GQA: q-head h reads kv-head h / (num_q_heads / num_kv_heads).
@@ -76,7 +80,7 @@ typedef enum {
 
 /* partition_size values selecting the work-balanced decode and the planned
  * decode (see pkv_paged_attention_decode and pkv_decode_plan). */
-enum { PKV_PARTITION_BALANCED = -1, PKV_PARTITION_PLANNED = -2 };
+enum { PKV_PARTITION_BALANCED = -1, PKV_PARTITION_PLANNED = -2, PKV_PARTITION_AUTO = -3 };
 
 /* Library version as major*10000 + minor*100 + patch. */
 int pkv_version(void);
@@ -85,9 +89,13 @@ int pkv_version(void);
 const char* pkv_last_error(void);
 
 /*
- * kv_cache_store: for every token t with 0 <= slot_mapping[t] < num_blocks *
- * block_size, copy k[t] into k_cache row (slot / block_size, slot %
- * block_size) and v[t] into the same row of v_cache. Negative slots are
+ * kv_cache_store: writing the new tokens' K/V rows into the blocks that the
+ * block table assigns them ("Building a minimal vLLM implementation", section
+ * sequence.py: the block table maps a sequence's logical blocks to physical
+ * ones, and the last block is filled token by token). A slot names one pool
+ * row, slot = physical block * block_size + row. For every token t with
+ * 0 <= slot_mapping[t] < num_blocks * block_size, copy k[t] into k_cache row
+ * (slot / block_size, slot % block_size) and v[t] into the same row of v_cache. Negative slots are
  * padding and write nothing; slots past the pool are skipped. The copy is
  * bit-exact. Two tokens naming the same slot race (the result is one of
  * them); callers keep slots unique.
@@ -116,11 +124,38 @@ int pkv_kv_cache_store(const void* k, const void* v, void* k_cache, void* v_cach
  *    start whatever the sizes), then fp32 pieces of the partial results, two
  *    per wave of the largest grid (4096 waves).
  *  - PKV_PARTITION_PLANNED: pkv_decode_plan_size(num_seqs) (the plan).
+ *  - PKV_PARTITION_AUTO: that of the partition size it stands for
+ *    (pkv_decode_auto_partition).
  *  - 0 (single pass): 0.
+ * The arrival counters must be zero before a workspace's first split-K or
+ * work-balanced call: pkv_decode_workspace_init clears them.
  */
 size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_context_len,
                                  int32_t partition_size);
+
+/*
+ * Zero the arrival counters at the start of a decode workspace (its first
+ * min(workspace_bytes, 256 KiB) bytes, which hold the split-K and the
+ * work-balanced counters), with a kernel on `stream`: no memset, so the call
+ * may be captured in a graph. The rest of the workspace is scratch and needs
+ * no initial contents. Call it once on a new workspace (e.g. from
+ * torch.empty) or after a call that did not run to completion.
+ *   workspace: 4-byte aligned device buffer (NULL allowed when
+ *   workspace_bytes is 0).
+ */
+int pkv_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The partition_size that PKV_PARTITION_AUTO resolves to on the current
+ * device, from host-side sizes only: 0 (one pass) when the num_seqs *
+ * num_kv_heads items give every compute unit two workgroups or
+ * max_context_len <= 2048; otherwise split-K with 1024-token partitions,
+ * halved (down to 256) while ceil(max_context_len / partition) partitions of
+ * every item would still leave compute units without two workgroups. 0 for
+ * invalid sizes.
+ */
+int32_t pkv_decode_auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len);
 
 /*
  * Decode plan: the sequences of one decode step in order of their number of
@@ -149,7 +184,13 @@ int pkv_decode_plan(void* plan, size_t plan_bytes, const int32_t* block_tables,
                     int32_t max_context_len, int32_t block_size, void* stream);
 
 /*
- * paged_attention_decode: out[s, h] = softmax_j(scale * q[s, h] . K_s[j, g])
+ * paged_attention_decode: the decode step's attention, one query row per
+ * sequence (in decode a sequence carries only its newest token: "Building a
+ * minimal vLLM implementation", section sequence.py, the state sent to
+ * workers), over K/V gathered through its block table (same section,
+ * block_table); the same function naive attention computes ("A vLLM engine
+ * small enough to read in one sitting", sections "What it does" and "The
+ * interesting bit"): out[s, h] = softmax_j(scale * q[s, h] . K_s[j, g])
  * . V_s[j, g] over positions j < context_lens[s], g = h / (Hq / Hkv), with
  * K_s, V_s gathered through block_tables[s].
  *   max_context_len: a host-side bound >= every context_lens[s] and <=
@@ -182,6 +223,8 @@ int pkv_decode_plan(void* plan, size_t plan_bytes, const int32_t* block_tables,
  *     num_seqs, context_lens and block_tables (workspace_bytes >=
  *     pkv_decode_plan_size(num_seqs)). The results are those of
  *     partition_size 0.
+ *     PKV_PARTITION_AUTO: the partition size pkv_decode_auto_partition
+ *     returns for these sizes (one pass or split-K), with its workspace.
  *   workspace / workspace_bytes: device buffer of at least
  *     pkv_decode_workspace_size(...) bytes (may be NULL when that is 0),
  *     256-byte aligned for PKV_PARTITION_BALANCED.
@@ -236,8 +279,9 @@ int pkv_paged_attention_decode_store(void* out, const void* q, void* k_cache, vo
  * Each call first clears the arrival counters it uses, with a kernel on
  * `stream`, then runs the decode; its results are those of
  * pkv_paged_attention_decode with the same arguments and a workspace.
- *   partition_size: 0, a positive multiple of 16 or PKV_PARTITION_BALANCED
- *   (PKV_PARTITION_PLANNED reads a caller's plan: PKV_EINVAL).
+ *   partition_size: 0, a positive multiple of 16, PKV_PARTITION_BALANCED or
+ *   PKV_PARTITION_AUTO (PKV_PARTITION_PLANNED reads a caller's plan:
+ *   PKV_EINVAL).
  * Errors: those of pkv_paged_attention_decode, and PKV_EWORKSPACE, before any
  * launch, when pkv_decode_workspace_size(...) for these arguments exceeds
  * PKV_STATIC_SCRATCH_BYTES.
@@ -257,10 +301,10 @@ int pkv_paged_attention_decode_static(void* out, const void* q, const void* k_ca
                                       void* stream);
 
 /*
- * E4M3 KV cache. The pages list support for quantized models among the
- * engine's features ("A vLLM engine small enough to read in one sitting",
- * section "Key highlights"); the format and scaling are this library's
- * reading. Cache elements are OCP FP8 E4M3 codes (1 sign, 4 exponent bits
+ * E4M3 KV cache. The pages list support for quantized models among vLLM's
+ * features ("Building a minimal vLLM implementation", the feature list that
+ * opens the page) and fix nothing further; the format and scaling are this
+ * library's reading. Cache elements are OCP FP8 E4M3 codes (1 sign, 4 exponent bits
  * with bias 7, 3 mantissa bits, no infinity, 0x7f/0xff NaN, largest finite
  * 448) in the same [num_blocks, block_size, num_kv_heads, head_dim] layout,
  * one byte each. k_scale and v_scale are device float32 arrays
@@ -317,10 +361,10 @@ int pkv_paged_attention_decode_store_fp8(void* out, const void* q, void* k_cache
 
 /*
  * Shared-prefix decode. With prefix caching, sequences that start from the
- * same prompt share its blocks ("Implementation Details", section
- * "PagedAttention -- BlockPool": block hashes map equal content to one
- * cached block, and blocks are reference-counted; "A vLLM engine small
- * enough to read in one sitting", "Key highlights": prefix caching). This
+ * same prompt share its blocks ("Implementation Details", section "Getting
+ * Started": serving with prefix caching enabled; section "PagedAttention --
+ * BlockPool": a hash table looks up cached blocks by content, and blocks
+ * carry reference counts). This
  * decode reads each shared block once per group instead of once per
  * sequence; its result is that of pkv_paged_attention_decode.
  *
@@ -362,7 +406,11 @@ int pkv_paged_attention_decode_shared_prefix(void* out, const void* q, const voi
 
 /*
  * paged_attention_prefill_chunk: attention of packed query chunks over their
- * paged contexts. Chunk c owns q rows cu_seqlens_q[c] .. cu_seqlens_q[c+1]-1
+ * paged contexts: the prefill of a sequence whose first tokens are already
+ * cached ("Building a minimal vLLM implementation", section sequence.py,
+ * num_cached_tokens and num_scheduled_tokens), computing what naive causal
+ * attention computes, as the pages' flash-attention prefill does ("A vLLM
+ * engine small enough to read in one sitting", section "What it does"). Chunk c owns q rows cu_seqlens_q[c] .. cu_seqlens_q[c+1]-1
  * (L_c rows); context_lens[c] >= L_c counts its cached tokens plus its own
  * L_c rows, whose K/V must already be stored. Row i of chunk c sits at
  * position P0 + i with P0 = context_lens[c] - L_c and, when causal != 0,
@@ -388,10 +436,10 @@ int pkv_paged_attention_prefill_chunk(void* out, const void* q, const void* k_ca
 /*
  * paged_attention_prefill_chunk_fp8: paged_attention_prefill_chunk over E4M3
  * caches (the format, scales and dequantisation of paged_attention_decode_fp8;
- * cache rows as written by kv_cache_store_fp8). The quantised-model support
- * of "A vLLM engine small enough to read in one sitting", section "Key
- * highlights"; the attention is the chunked-prefill definition above applied
- * to the dequantised rows.
+ * cache rows as written by kv_cache_store_fp8). Quantized-model support is in
+ * the feature list that opens "Building a minimal vLLM implementation"; the
+ * attention is the chunked-prefill definition above applied to the
+ * dequantised rows.
  *   q, out: bf16 [total_q, num_q_heads, head_dim]; k_cache, v_cache: uint8
  *   codes [num_blocks, block_size, num_kv_heads, head_dim]; k_scale, v_scale:
  *   float32 [num_kv_heads] on the device (a row's values are code * scale).
@@ -407,6 +455,50 @@ int pkv_paged_attention_prefill_chunk_fp8(void* out, const void* q, const void* 
                                           int32_t num_blocks, int32_t block_size, int32_t num_q_heads,
                                           int32_t num_kv_heads, int32_t head_dim, float scale,
                                           int32_t causal, void* stream);
+
+/*
+ * Checks of device-held inputs, for debugging. The attention and store entry
+ * points never read block ids, lengths or slots on the host; kernels skip or
+ * poison what is out of range (a block id outside the pool turns that row's
+ * output into NaN, a slot outside the pool writes nothing, a length above
+ * max_context_len is truncated) and two tokens storing to one slot race.
+ * These calls count such violations into `report` (a device int32[4] owned
+ * by the caller, overwritten) with kernels on `stream`, touching nothing out
+ * of bounds; the caller copies the report back when it wants to look.
+ *
+ * check_paged_inputs, for a decode (cu_seqlens_q NULL) or a chunked prefill:
+ *   report[0]: sequences with context_lens[s] outside [0, max_context_len];
+ *   report[1]: entries among the first ceil(min(max(ctx, 0), max_context_len)
+ *              / block_size) of each table row outside [0, num_blocks) (the
+ *              pool's blocks, "Implementation Details", section
+ *              "PagedAttention -- BlockPool");
+ *   report[2]: chunks c whose row count L = cu_seqlens_q[c+1] - cu_seqlens_q[c]
+ *              is negative, above max_q_len or above context_lens[c], plus
+ *              cu_seqlens_q[0] != 0 and cu_seqlens_q[num_seqs] != total_q
+ *              (counted on the first and last chunk);
+ *   report[3]: the lowest sequence index with any of these, or num_seqs.
+ *   Arguments as in the attention calls (total_q and max_q_len are read only
+ *   with cu_seqlens_q).
+ */
+int pkv_check_paged_inputs(const int32_t* block_tables, const int32_t* context_lens,
+                           const int32_t* cu_seqlens_q, int32_t num_seqs, int32_t max_blocks_per_seq,
+                           int32_t max_context_len, int32_t total_q, int32_t max_q_len,
+                           int32_t num_blocks, int32_t block_size, int32_t* report, void* stream);
+
+/*
+ * check_slots, for a kv_cache_store (or a fused store) call:
+ *   report[0]: tokens whose slot is >= num_blocks * block_size;
+ *   report[1]: repeated claims: a slot named by k tokens adds k - 1;
+ *   report[2]: negative slots (padding: allowed, counted for information);
+ *   report[3]: the lowest token index whose slot is past the pool or named
+ *              more than once, or num_tokens.
+ *   workspace: pkv_check_slots_workspace_size(num_blocks, block_size) bytes,
+ *   4-byte aligned (two bitmaps of one bit per pool row; no initial contents).
+ */
+size_t pkv_check_slots_workspace_size(int32_t num_blocks, int32_t block_size);
+int pkv_check_slots(const int32_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                    int32_t block_size, void* workspace, size_t workspace_bytes, int32_t* report,
+                    void* stream);
 
 #ifdef __cplusplus
 }

@@ -4,9 +4,9 @@ TEST INFRASTRUCTURE, like the rest of this package: only the test suite, the
 smoke check and the CPU-baseline leg of the benchmark may use it, and it
 shares nothing with the HIP library.
 
-The pages list support for quantized models among the engine's features
-("A vLLM engine small enough to read in one sitting", section "Key
-highlights") and fix nothing further. The readings taken here:
+The pages list support for quantized models among vLLM's features
+("Building a minimal vLLM implementation", the feature list that opens the
+page) and fix nothing further. The readings taken here:
 
   * element format: OCP 8-bit E4M3 ("fn" variant): 1 sign bit, 4 exponent
     bits with bias 7, 3 mantissa bits; exponent field 0 holds subnormals

@@ -8,6 +8,7 @@ library; the first call does, and raises if it has not been built.
 
 from .binding import (  # noqa: F401
     DECODE_ALGOS,
+    PARTITION_AUTO,
     PARTITION_BALANCED,
     PARTITION_PLANNED,
     DecodeFp8Launch,
@@ -21,14 +22,19 @@ from .binding import (  # noqa: F401
     SharedPrefixDecodeLaunch,
     StoreFp8Launch,
     StoreLaunch,
+    check_paged_inputs,
+    check_slots,
+    decode_auto_partition,
     decode_plan,
     decode_plan_size,
+    decode_workspace_init,
     decode_workspace_size,
     kv_cache_store,
     kv_cache_store_fp8,
     lib,
     library_path,
     new_decode_plan,
+    new_decode_workspace,
     paged_attention_decode,
     paged_attention_decode_fp8,
     paged_attention_decode_shared_prefix,

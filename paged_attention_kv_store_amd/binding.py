@@ -24,6 +24,7 @@ PKV_F32, PKV_BF16 = 0, 1
 DECODE_ALGOS = {"auto": 0, "valu": 1, "mfma": 2}
 PARTITION_BALANCED = -1      # partition_size selecting the work-balanced decode
 PARTITION_PLANNED = -2       # partition_size selecting the planned decode (workspace = the plan)
+PARTITION_AUTO = -3          # partition_size chosen by the library from the host-side sizes
 STATIC_SCRATCH_BYTES = 64 << 20   # PKV_STATIC_SCRATCH_BYTES: the library's per-device decode scratch
 
 _i32 = ctypes.c_int32
@@ -35,6 +36,11 @@ _SIGNATURES = {
                            ctypes.c_int),
     "pkv_decode_workspace_size": ([_i32, _i32, _i32, _i32, _i32, _i32], ctypes.c_size_t),
     "pkv_decode_plan_size": ([_i32], ctypes.c_size_t),
+    "pkv_decode_workspace_init": ([_vp, ctypes.c_size_t, _vp], ctypes.c_int),
+    "pkv_decode_auto_partition": ([_i32, _i32, _i32], _i32),
+    "pkv_check_paged_inputs": ([_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp], ctypes.c_int),
+    "pkv_check_slots_workspace_size": ([_i32, _i32], ctypes.c_size_t),
+    "pkv_check_slots": ([_vp, _i32, _i32, _i32, _vp, ctypes.c_size_t, _vp, _vp], ctypes.c_int),
     "pkv_decode_plan": ([_vp, ctypes.c_size_t, _vp, _vp, _i32, _i32, _i32, _i32, _vp], ctypes.c_int),
     "pkv_paged_attention_decode": ([_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                     _i32, _i32, _i32, ctypes.c_float, _i32, _vp, ctypes.c_size_t,
@@ -153,6 +159,8 @@ def _partition(partition_size):
         return PARTITION_BALANCED
     if partition_size == "planned":
         return PARTITION_PLANNED
+    if partition_size == "auto":
+        return PARTITION_AUTO
     return int(partition_size)
 
 
@@ -198,14 +206,53 @@ def decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_con
                                                max_context_len, _partition(partition_size)))
 
 
-def _decode_workspace(workspace, s, hq, hkv, d, max_context_len, partition, device):
-    """The caller's workspace, or a new one when the call needs it: zero-filled
-    (the work-balanced decode requires zero counters before its first call)."""
+def decode_workspace_init(workspace, stream=None):
+    """Zero the arrival counters of a decode workspace (a uint8 device
+    tensor) with a kernel on the stream; the rest needs no initial contents."""
+    _dev(workspace)
+    _check(lib().pkv_decode_workspace_init(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                           _stream(stream)))
+    return workspace
+
+
+def decode_auto_partition(num_seqs, num_kv_heads, max_context_len):
+    """The partition_size that partition_size="auto" resolves to on the current device."""
+    return int(lib().pkv_decode_auto_partition(num_seqs, num_kv_heads, int(max_context_len)))
+
+
+def new_decode_workspace(nbytes, device, stream=None):
+    """A decode workspace of nbytes with its counters cleared (torch.empty plus
+    pkv_decode_workspace_init: one small kernel, no memset)."""
+    ws = torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+    return decode_workspace_init(ws, stream)
+
+
+# Workspaces of the one-call functions (paged_attention_decode and friends
+# without a workspace argument): one per (device, stream), grown when a call
+# needs more. Calls on one stream are ordered, so they may share it; every
+# call leaves its counters zero.
+_WS_CACHE = {}
+
+
+def _cached_workspace(need, device, stream):
+    key = (torch.device(device).index, _stream(stream).value)
+    ws = _WS_CACHE.get(key)
+    if ws is None or ws.numel() < need:
+        ws = new_decode_workspace(need, device, stream)
+        _WS_CACHE[key] = ws
+    return ws
+
+
+def _decode_workspace(workspace, s, hq, hkv, d, max_context_len, partition, device, stream=None,
+                      cached=False):
+    """The caller's workspace, or one for the call when it needs it: the
+    one-call functions reuse a cached workspace per (device, stream), the
+    prepared launches own theirs; both are cleared once when made."""
     need = decode_workspace_size(s, hq, hkv, d, max_context_len, partition) if partition else 0
     _need(partition != PARTITION_PLANNED or workspace is not None,
           "the planned decode takes its plan (written by decode_plan) as workspace")
     if need and workspace is None:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=device)
+        workspace = _cached_workspace(need, device, stream) if cached else new_decode_workspace(need, device, stream)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     return workspace, ws_bytes
 
@@ -236,7 +283,8 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     s, hq, d = q.shape
     nb, bs, hkv, _ = k_cache.shape
     part = _partition(partition_size)
-    workspace, ws_bytes = _decode_workspace(workspace, s, hq, hkv, d, max_context_len, part, q.device)
+    workspace, ws_bytes = _decode_workspace(workspace, s, hq, hkv, d, max_context_len, part, q.device, stream,
+                                            cached=True)
     _check(lib().pkv_paged_attention_decode(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
         s, block_tables.shape[1], int(max_context_len), nb, bs, hq, hkv, d, float(scale),
@@ -275,7 +323,7 @@ def paged_attention_decode_store(out, q, k_cache, v_cache, block_tables, context
     context_lens[s]-1) and run decode, in one launch; writes out and the caches."""
     DecodeStoreLaunch(out, q, k_cache, v_cache, block_tables, context_lens, k_new, v_new,
                       slot_mapping, scale, max_context_len, partition_size, algo,
-                      workspace)(stream)
+                      workspace, _cache_workspace=True)(stream)
     return out
 
 
@@ -299,7 +347,7 @@ def paged_attention_decode_fp8(out, q, k_cache, v_cache, k_scale, v_scale, block
     """Decode over E4M3 caches (uint8 [NB, bs, Hkv, D], scales float32 [Hkv]);
     q and out bf16 [S, Hq, D]."""
     DecodeFp8Launch(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, scale,
-                    max_context_len, partition_size, workspace)(stream)
+                    max_context_len, partition_size, workspace, _cache_workspace=True)(stream)
     return out
 
 
@@ -310,7 +358,8 @@ def paged_attention_decode_store_fp8(out, q, k_cache, v_cache, k_scale, v_scale,
     [S, Hkv, D], at the slot of position context_lens[s]-1) and decode over
     the E4M3 caches, in one launch."""
     DecodeStoreFp8Launch(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, k_new,
-                         v_new, slot_mapping, scale, max_context_len, partition_size, workspace)(stream)
+                         v_new, slot_mapping, scale, max_context_len, partition_size, workspace,
+                         _cache_workspace=True)(stream)
     return out
 
 
@@ -387,7 +436,7 @@ class DecodeLaunch(_Prepared):
     """paged_attention_decode with fixed tensors; owns its workspace."""
 
     def __init__(self, out, q, k_cache, v_cache, block_tables, context_lens, scale,
-                 max_context_len, partition_size=0, algo="auto", workspace=None):
+                 max_context_len, partition_size=0, algo="auto", workspace=None, _cache_workspace=False):
         _dev(out, q, k_cache, v_cache, block_tables, context_lens)
         _need(q.dim() == 3 and out.shape == q.shape and out.dtype == q.dtype, "q/out must be [S, Hq, D]")
         _need(k_cache.dim() == 4 and v_cache.shape == k_cache.shape, "caches must be [NB, bs, Hkv, D]")
@@ -400,7 +449,7 @@ class DecodeLaunch(_Prepared):
         nb, bs, hkv, _ = k_cache.shape
         part = _partition(partition_size)
         workspace, ws_bytes = _decode_workspace(workspace, s, hq, hkv, d, max_context_len, part,
-                                                q.device)
+                                                q.device, cached=_cache_workspace)
         self._keep = (out, q, k_cache, v_cache, block_tables, context_lens, workspace)
         self._fn = "pkv_paged_attention_decode"
         self._args = (_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
@@ -488,9 +537,9 @@ class DecodeStoreLaunch(_Prepared):
 
     def __init__(self, out, q, k_cache, v_cache, block_tables, context_lens, k_new, v_new,
                  slot_mapping, scale, max_context_len, partition_size=0, algo="auto",
-                 workspace=None):
+                 workspace=None, _cache_workspace=False):
         base = DecodeLaunch(out, q, k_cache, v_cache, block_tables, context_lens, scale,
-                            max_context_len, partition_size, algo, workspace)
+                            max_context_len, partition_size, algo, workspace, _cache_workspace)
         _dev(k_new, v_new, slot_mapping)
         s, _, d = q.shape
         hkv = k_cache.shape[2]
@@ -524,7 +573,7 @@ class DecodeFp8Launch(_Prepared):
     """paged_attention_decode_fp8 with fixed tensors; owns its split-K workspace."""
 
     def __init__(self, out, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
-                 scale, max_context_len, partition_size=0, workspace=None):
+                 scale, max_context_len, partition_size=0, workspace=None, _cache_workspace=False):
         _dev(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens)
         _check_fp8_cache(k_cache, v_cache, k_scale, v_scale)
         _need(q.dim() == 3 and out.shape == q.shape and q.dtype == out.dtype == torch.bfloat16,
@@ -538,7 +587,7 @@ class DecodeFp8Launch(_Prepared):
         nb, bs, hkv, _ = k_cache.shape
         part = _partition(partition_size)
         workspace, ws_bytes = _decode_workspace(workspace, s, hq, hkv, d, max_context_len, part,
-                                                q.device)
+                                                q.device, cached=_cache_workspace)
         self._keep = (out, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, workspace)
         self._fn = "pkv_paged_attention_decode_fp8"
         self._args = (_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
@@ -551,9 +600,10 @@ class DecodeStoreFp8Launch(_Prepared):
     """paged_attention_decode_store_fp8 with fixed tensors; owns its split-K workspace."""
 
     def __init__(self, out, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, k_new,
-                 v_new, slot_mapping, scale, max_context_len, partition_size=0, workspace=None):
+                 v_new, slot_mapping, scale, max_context_len, partition_size=0, workspace=None,
+                 _cache_workspace=False):
         base = DecodeFp8Launch(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
-                               scale, max_context_len, partition_size, workspace)
+                               scale, max_context_len, partition_size, workspace, _cache_workspace)
         _dev(k_new, v_new, slot_mapping)
         s, _, d = q.shape
         hkv = k_cache.shape[2]
@@ -597,3 +647,44 @@ class SharedPrefixDecodeLaunch(_Prepared):
                       _ptr(context_lens), _ptr(group_starts), _ptr(group_prefix_lens), ng,
                       int(max_group_size), int(max_prefix_len), s, block_tables.shape[1],
                       int(max_context_len), nb, bs, hq, hkv, d, float(scale), _ptr(workspace), ws_bytes)
+
+
+# --------------------------------------------------------------------------
+# Checks of device-held inputs (debugging): each returns the device report
+# (int32 [4]); see include/pkv.h for what each entry counts.
+# --------------------------------------------------------------------------
+
+def check_paged_inputs(block_tables, context_lens, num_blocks, block_size, max_context_len,
+                       cu_seqlens_q=None, total_q=0, max_q_len=0, report=None, stream=None):
+    """Count lengths outside [0, max_context_len], used table entries outside
+    the pool and (with cu_seqlens_q) impossible chunk row counts."""
+    _dev(block_tables, context_lens)
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2, "block_tables must be int32 [S, MB]")
+    n = block_tables.shape[0]
+    _need(context_lens.dtype == torch.int32 and context_lens.shape == (n,), "context_lens must be int32 [S]")
+    if cu_seqlens_q is not None:
+        _dev(cu_seqlens_q)
+        _need(cu_seqlens_q.dtype == torch.int32 and cu_seqlens_q.shape == (n + 1,),
+              "cu_seqlens_q must be int32 [S+1]")
+    if report is None:
+        report = torch.empty(4, dtype=torch.int32, device=block_tables.device)
+    _check(lib().pkv_check_paged_inputs(_ptr(block_tables), _ptr(context_lens), _ptr(cu_seqlens_q), n,
+                                        block_tables.shape[1], int(max_context_len), int(total_q),
+                                        int(max_q_len), int(num_blocks), int(block_size), _ptr(report),
+                                        _stream(stream)))
+    return report
+
+
+def check_slots(slot_mapping, num_blocks, block_size, workspace=None, report=None, stream=None):
+    """Count slots past the pool, repeated claims of a slot and padding slots."""
+    _dev(slot_mapping)
+    _need(slot_mapping.dtype == torch.int32 and slot_mapping.dim() == 1, "slot_mapping must be int32 [T]")
+    need = int(lib().pkv_check_slots_workspace_size(int(num_blocks), int(block_size)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=slot_mapping.device)
+    if report is None:
+        report = torch.empty(4, dtype=torch.int32, device=slot_mapping.device)
+    _check(lib().pkv_check_slots(_ptr(slot_mapping), slot_mapping.shape[0], int(num_blocks), int(block_size),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(report),
+                                 _stream(stream)))
+    return report

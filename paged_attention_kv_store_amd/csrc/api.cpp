@@ -48,6 +48,23 @@ void partitioning(int32_t max_ctx, int32_t partition_size, int32_t* part, int64_
   }
 }
 
+// The partition size PKV_PARTITION_AUTO stands for. Single pass when the
+// (sequence, kv-head) items give every compute unit two workgroups, or when
+// contexts are short enough that the longest item is not the tail; otherwise
+// split-K with 1024-token partitions (halved down to 256 while the longest
+// context's partitions still could not fill two workgroups per unit).
+// Measured on one MI355X: 256 items of up to 32K tokens take 384 us in one
+// pass and 213 us with 1024- or 2048-token partitions; 1024 and 2048 items of
+// up to 4K tokens are fastest in one pass (split-K at 2048 tokens adds 12-14%).
+int32_t auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ctx) {
+  const int64_t items = (int64_t)num_seqs * num_kv_heads;
+  const int64_t slots = 2 * (int64_t)pkv::device_compute_units();
+  if (items >= slots || max_ctx <= 2048 || items > pkv::kSplitMaxItems) return 0;
+  int32_t part = 1024;
+  while (part > 256 && items * ceil_div(max_ctx, part) < slots) part /= 2;
+  return ceil_div(max_ctx, part) > 1 ? part : 0;
+}
+
 int check_common(const char* fn, int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
                  int32_t head_dim, int dtype) {
   if (elt_size(dtype) == 0) return fail(PKV_EINVAL, "%s: unknown dtype %d", fn, dtype);
@@ -133,6 +150,7 @@ extern "C" size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_head
   if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_context_len < 0 ||
       num_q_heads % num_kv_heads != 0)
     return 0;
+  if (partition_size == PKV_PARTITION_AUTO) partition_size = auto_partition(num_seqs, num_kv_heads, max_context_len);
   if (partition_size == PKV_PARTITION_BALANCED) {
     // one arrival counter per wave, then two pieces per wave, for the largest grid
     const int64_t stride = pkv::bal_piece_stride(num_q_heads / num_kv_heads, head_dim);
@@ -149,6 +167,23 @@ extern "C" size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_head
   // l, o of every (sequence, q-head, partition)
   return (size_t)pkv::kSplitMaxItems * sizeof(int32_t) +
          (size_t)num_seqs * num_q_heads * nparts * (head_dim + 2) * sizeof(float);
+}
+
+extern "C" int32_t pkv_decode_auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len) {
+  if (num_seqs <= 0 || num_kv_heads <= 0 || max_context_len < 0) return 0;
+  return auto_partition(num_seqs, num_kv_heads, max_context_len);
+}
+
+extern "C" int pkv_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "pkv_decode_workspace_init";
+  if (workspace_bytes == 0) return PKV_OK;
+  if (!workspace) return fail(PKV_EINVAL, "%s: null workspace", fn);
+  if (!aligned(workspace, 4)) return fail(PKV_EINVAL, "%s: workspace must be 4-byte aligned", fn);
+  // the split-K counter block is the longer of the two counter regions
+  const size_t bytes = workspace_bytes < (size_t)pkv::kSplitMaxItems * 4 ? workspace_bytes
+                                                                          : (size_t)pkv::kSplitMaxItems * 4;
+  return hip_status(pkv::launch_zero_ints(reinterpret_cast<int32_t*>(workspace), (int64_t)(bytes / 4),
+                                          (hipStream_t)stream), fn);
 }
 
 namespace {
@@ -178,11 +213,12 @@ int decode_impl(const char* fn, void* out, const void* q, const void* k_cache, c
   if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
     return fail(PKV_EINVAL, "%s: max_context_len %d outside [0, max_blocks_per_seq * block_size = %lld]", fn,
                 max_context_len, (long long)max_blocks_per_seq * block_size);
+  if (partition_size == PKV_PARTITION_AUTO) partition_size = auto_partition(num_seqs, num_kv_heads, max_context_len);
   const bool balanced = partition_size == PKV_PARTITION_BALANCED;
   const bool planned = partition_size == PKV_PARTITION_PLANNED;
   if (!balanced && !planned && (partition_size < 0 || partition_size % 16 != 0))
     return fail(PKV_EINVAL, "%s: partition_size %d must be 0, a positive multiple of 16, "
-                "PKV_PARTITION_BALANCED or PKV_PARTITION_PLANNED", fn, partition_size);
+                "PKV_PARTITION_BALANCED, PKV_PARTITION_PLANNED or PKV_PARTITION_AUTO", fn, partition_size);
   if (!std::isfinite(scale)) return fail(PKV_EINVAL, "%s: scale is not finite", fn);
   if (algo == PKV_DECODE_AUTO) algo = dtype == PKV_BF16 ? PKV_DECODE_MFMA : PKV_DECODE_VALU;
   if (fp8) {
@@ -685,4 +721,66 @@ extern "C" int pkv_paged_attention_decode_shared_prefix(
   b.pair_span = 0;
   b.plan = nullptr;
   return hip_status(pkv::launch_decode_mfma(b, head_dim, st), fn);
+}
+
+extern "C" int pkv_check_paged_inputs(const int32_t* block_tables, const int32_t* context_lens,
+                                      const int32_t* cu_seqlens_q, int32_t num_seqs,
+                                      int32_t max_blocks_per_seq, int32_t max_context_len, int32_t total_q,
+                                      int32_t max_q_len, int32_t num_blocks, int32_t block_size,
+                                      int32_t* report, void* stream) {
+  const char* fn = "pkv_check_paged_inputs";
+  if (num_seqs < 0 || total_q < 0 || max_q_len < 0) return fail(PKV_EINVAL, "%s: negative size", fn);
+  if (num_blocks <= 0 || block_size <= 0 || max_blocks_per_seq <= 0)
+    return fail(PKV_EINVAL, "%s: num_blocks, block_size and max_blocks_per_seq must be positive", fn);
+  if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
+    return fail(PKV_EINVAL, "%s: max_context_len outside [0, max_blocks_per_seq * block_size]", fn);
+  if (!report || !aligned(report, 4)) return fail(PKV_EINVAL, "%s: report must be a 4-byte aligned device array", fn);
+  if (num_seqs > 0 && (!block_tables || !context_lens)) return fail(PKV_EINVAL, "%s: null pointer", fn);
+  if (!aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(cu_seqlens_q, 4))
+    return fail(PKV_EINVAL, "%s: index arrays must be 4-byte aligned", fn);
+  pkv::CheckParams p;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.cu_seqlens_q = cu_seqlens_q;
+  p.num_seqs = num_seqs;
+  p.max_blocks = max_blocks_per_seq;
+  p.max_ctx = max_context_len;
+  p.num_blocks = num_blocks;
+  p.block_size = block_size;
+  p.total_q = total_q;
+  p.max_q_len = max_q_len;
+  p.report = report;
+  return hip_status(pkv::launch_check_tables(p, (hipStream_t)stream), fn);
+}
+
+extern "C" size_t pkv_check_slots_workspace_size(int32_t num_blocks, int32_t block_size) {
+  if (num_blocks <= 0 || block_size <= 0) return 0;
+  const int64_t words = ((int64_t)num_blocks * block_size + 31) / 32;
+  return (size_t)(2 * words * 4);
+}
+
+extern "C" int pkv_check_slots(const int32_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                               int32_t block_size, void* workspace, size_t workspace_bytes, int32_t* report,
+                               void* stream) {
+  const char* fn = "pkv_check_slots";
+  if (num_tokens < 0) return fail(PKV_EINVAL, "%s: num_tokens < 0", fn);
+  if (num_blocks <= 0 || block_size <= 0)
+    return fail(PKV_EINVAL, "%s: num_blocks and block_size must be positive", fn);
+  if (!report || !aligned(report, 4)) return fail(PKV_EINVAL, "%s: report must be a 4-byte aligned device array", fn);
+  if (num_tokens > 0 && !slot_mapping) return fail(PKV_EINVAL, "%s: null slot_mapping", fn);
+  if (!aligned(slot_mapping, 4)) return fail(PKV_EINVAL, "%s: slot_mapping must be 4-byte aligned", fn);
+  const size_t need = pkv_check_slots_workspace_size(num_blocks, block_size);
+  if (!workspace || workspace_bytes < need)
+    return fail(PKV_EWORKSPACE, "%s: needs %zu workspace bytes, got %zu", fn, need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 4)) return fail(PKV_EINVAL, "%s: workspace must be 4-byte aligned", fn);
+  pkv::SlotCheckParams p;
+  const int64_t words = ((int64_t)num_blocks * block_size + 31) / 32;
+  p.slot_mapping = slot_mapping;
+  p.num_tokens = num_tokens;
+  p.num_slots = (int64_t)num_blocks * block_size;
+  p.seen = reinterpret_cast<uint32_t*>(workspace);
+  p.dup = p.seen + words;
+  p.report = report;
+  return hip_status(pkv::launch_check_slots(p, (hipStream_t)stream), fn);
 }

@@ -167,6 +167,35 @@ struct PrefillParams {
   const float* v_scale;
 };
 
+// Checks of device-held inputs (debugging aids; see check.hip).
+//   report[0] lengths outside [0, max_ctx], [1] used table entries outside
+//   the pool, [2] chunks with an impossible row count, [3] the lowest
+//   offending sequence (num_seqs if none).
+struct CheckParams {
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* cu_seqlens_q;   // null: decode (no chunks)
+  int32_t num_seqs;
+  int32_t max_blocks;
+  int32_t max_ctx;
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t total_q;
+  int32_t max_q_len;
+  int32_t* report;
+};
+//   report[0] slots past the pool, [1] repeated claims of a slot, [2]
+//   negative (padding) slots, [3] the lowest offending token (num_tokens if
+//   none). seen, dup: bitmaps of ceil(num_slots / 32) words each, dup = seen + words.
+struct SlotCheckParams {
+  const int32_t* slot_mapping;
+  int32_t num_tokens;
+  int64_t num_slots;
+  uint32_t* seen;
+  uint32_t* dup;
+  int32_t* report;
+};
+
 // Compute units of the current device (queried once per device).
 int device_compute_units();
 
@@ -188,5 +217,7 @@ hipError_t launch_decode_balanced(const DecodeParams& p, int head_dim, hipStream
 hipError_t launch_decode_plan(const PlanParams& p, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_prefill_fp8(const PrefillParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_check_tables(const CheckParams& p, hipStream_t stream);
+hipError_t launch_check_slots(const SlotCheckParams& p, hipStream_t stream);
 
 }  // namespace pkv

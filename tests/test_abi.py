@@ -78,7 +78,7 @@ def _decode(lib, **over):
     (dict(part=-1, dtype=1), binding.PKV_EWORKSPACE),
     (dict(part=-1, dtype=1, ws=1040, ws_bytes=1 << 30), binding.PKV_EINVAL),   # 256-byte alignment
     (dict(part=-1, dtype=1, out=1032), binding.PKV_EINVAL),          # out 16-byte aligned
-    (dict(part=-3), binding.PKV_EINVAL),
+    (dict(part=-4), binding.PKV_EINVAL),
     (dict(part=-2), binding.PKV_EUNSUPPORTED),                       # planned needs the MFMA kernel
     (dict(part=-2, dtype=1), binding.PKV_EWORKSPACE),                # ... and its plan
     (dict(part=-2, dtype=1, ws=1024, ws_bytes=4 * 32 - 1), binding.PKV_EWORKSPACE),
@@ -304,3 +304,65 @@ def test_static_decode_empty_batch_is_a_no_op():
     rc = pkv.lib().pkv_paged_attention_decode_static(None, None, None, None, None, None, 0, 16, 0, 64, 16, 8, 4,
                                                      64, 0.125, 64, 0, 0, None)
     assert rc == binding.PKV_OK
+
+
+@needs_lib
+def test_auto_partition_rule():
+    """PKV_PARTITION_AUTO: one pass when the items fill two workgroups per
+    compute unit or contexts are short; else split-K at 1024 tokens, halved
+    while the longest context's partitions cannot fill the units. (Without a
+    GPU the library assumes 256 compute units.)"""
+    cus = 256
+    auto = pkv.decode_auto_partition
+    assert auto(60, 8, 1024) == 0                 # short contexts
+    assert auto(256, 8, 4096) == 0                # 2048 items
+    assert auto(64, 8, 32768) == 0                # 512 items = 2 per unit
+    assert auto(32, 8, 32768) == 1024             # 256 items, 32 partitions each
+    assert auto(1, 8, 4096) == 256                # 8 items: 1024 -> 512 -> 256
+    assert auto(1, 1, 3000) == 256                # the floor, even if the units stay idle
+    assert auto(4, 8, 8192) == 512                # 32 items x 8 partitions = 256 < 512 -> halve once
+    # (the three lines above depend on the unit count; recompute the rule here)
+    for s, hkv, ctx in [(32, 8, 32768), (1, 8, 4096), (4, 8, 8192), (2, 4, 2100), (100, 2, 5000)]:
+        items, slots = s * hkv, 2 * cus
+        want = 0
+        if items < slots and ctx > 2048:
+            part = 1024
+            while part > 256 and items * -(-ctx // part) < slots:
+                part //= 2
+            want = part if -(-ctx // part) > 1 else 0
+        assert auto(s, hkv, ctx) == want, (s, hkv, ctx)
+    assert pkv.lib().pkv_decode_auto_partition(0, 8, 100) == 0
+    # the workspace of "auto" is that of the partition size it resolves to
+    assert pkv.decode_workspace_size(32, 32, 8, 128, 32768, "auto") == \
+        pkv.decode_workspace_size(32, 32, 8, 128, 32768, 1024)
+    assert pkv.decode_workspace_size(60, 16, 8, 128, 1024, "auto") == 0
+
+
+@needs_lib
+def test_workspace_init_rejects():
+    lib = pkv.lib()
+    assert lib.pkv_decode_workspace_init(None, 0, None) == binding.PKV_OK
+    assert lib.pkv_decode_workspace_init(None, 64, None) == binding.PKV_EINVAL
+    assert lib.pkv_decode_workspace_init(1026, 64, None) == binding.PKV_EINVAL
+
+
+@needs_lib
+def test_checks_reject_on_the_host():
+    lib = pkv.lib()
+    E = binding.PKV_EINVAL
+    # block_tables, context_lens, cu, S, MB, max_ctx, total_q, max_q_len, NB, bs, report, stream
+    assert lib.pkv_check_paged_inputs(1024, 1024, None, -1, 16, 256, 0, 0, 64, 16, 1024, None) == E
+    assert lib.pkv_check_paged_inputs(1024, 1024, None, 4, 16, 257, 0, 0, 64, 16, 1024, None) == E
+    assert lib.pkv_check_paged_inputs(1024, 1024, None, 4, 16, 256, 0, 0, 0, 16, 1024, None) == E
+    assert lib.pkv_check_paged_inputs(1024, 1024, None, 4, 16, 256, 0, 0, 64, 16, None, None) == E
+    assert lib.pkv_check_paged_inputs(None, 1024, None, 4, 16, 256, 0, 0, 64, 16, 1024, None) == E
+    assert lib.pkv_check_paged_inputs(1024, 1026, None, 4, 16, 256, 0, 0, 64, 16, 1024, None) == E
+    assert lib.pkv_check_slots_workspace_size(64, 16) == 2 * 32 * 4
+    assert lib.pkv_check_slots_workspace_size(3, 16) == 2 * 2 * 4
+    assert lib.pkv_check_slots_workspace_size(0, 16) == 0
+    # slot_mapping, T, NB, bs, workspace, ws_bytes, report, stream
+    assert lib.pkv_check_slots(1024, -1, 64, 16, 1024, 256, 1024, None) == E
+    assert lib.pkv_check_slots(1024, 4, 64, 16, 1024, 255, 1024, None) == binding.PKV_EWORKSPACE
+    assert lib.pkv_check_slots(1024, 4, 64, 16, None, 256, 1024, None) == binding.PKV_EWORKSPACE
+    assert lib.pkv_check_slots(1024, 4, 64, 16, 1024, 256, None, None) == E
+    assert lib.pkv_check_slots(None, 4, 64, 16, 1024, 256, 1024, None) == E

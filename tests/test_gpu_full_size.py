@@ -65,8 +65,8 @@ def _ids(m):
 
 # ---- decode: the Qwen3-shaped layer (60 seqs, ctx U{64..1024}, 16 q / 8 kv) ------------
 
-QWEN3_MODES = [("mfma", 0), ("mfma", "planned"), ("mfma", 256), ("mfma", "balanced"), ("valu", 0),
-               ("valu", 256)]
+QWEN3_MODES = [("mfma", 0), ("mfma", "planned"), ("mfma", 256), ("mfma", "balanced"), ("mfma", "auto"),
+               ("valu", 0), ("valu", 256)]
 
 
 @pytest.mark.parametrize("mode", QWEN3_MODES, ids=_ids)
@@ -78,7 +78,8 @@ def test_qwen3_layer_every_row(mode):
 
 # ---- decode: the prefix-shared batch (256 seqs, ctx U{512..4096}, 32 q / 8 kv) ------------
 
-LLAMA_MODES = [("mfma", 0), ("mfma", "planned"), ("mfma", 512), ("mfma", "balanced"), ("valu", 0)]
+LLAMA_MODES = [("mfma", 0), ("mfma", "planned"), ("mfma", 512), ("mfma", "balanced"), ("mfma", "auto"),
+               ("valu", 0)]
 
 
 @pytest.mark.parametrize("mode", LLAMA_MODES + [("shared_prefix", 0)], ids=_ids)
@@ -102,7 +103,7 @@ def test_llama_prefix_every_row(mode):
 # ---- decode: long contexts (32 seqs, ctx log-uniform 1K..32K, 32 q / 8 kv) ----------------
 
 LONG_MODES = [("mfma", 512), ("mfma", 1024), ("mfma", 0), ("mfma", "planned"), ("mfma", "balanced"),
-              ("valu", 512)]
+              ("mfma", "auto"), ("valu", 512), ("valu", "auto")]
 
 
 @pytest.mark.parametrize("mode", LONG_MODES, ids=_ids)
@@ -133,7 +134,8 @@ def _mixed_entry():
     return pre, dec, dev, ddev, want_pre, want_dec
 
 
-MIXED_DECODE_MODES = [("mfma", 0), ("mfma", "planned"), ("mfma", "balanced"), ("mfma", 512), ("valu", 0)]
+MIXED_DECODE_MODES = [("mfma", 0), ("mfma", "planned"), ("mfma", "balanced"), ("mfma", 512), ("mfma", "auto"),
+                      ("valu", 0)]
 
 
 @pytest.mark.parametrize("mode", MIXED_DECODE_MODES, ids=_ids)
@@ -207,7 +209,7 @@ def test_spec_verify_every_row():
 
 # ---- the Qwen3-shaped layer over E4M3 caches ------------------------------------------------
 
-@pytest.mark.parametrize("part", [0, "planned", 256])
+@pytest.mark.parametrize("part", [0, "planned", 256, "auto"])
 def test_qwen3_fp8_layer_every_row(part):
     def make():
         b = W.qwen3_decode_fp8(layers=1).batches[0]
