@@ -20,13 +20,17 @@ Also on the same JSON line: the roofline of the dominant kernel (decode,
 HBM-bound) from HIP events around each launch on the launch stream, the HBM
 traffic that rocprofv3 counters measured for that kernel (from
 profiles/decode_qwen3_traffic.json, null if the kernel source changed since),
-a plain-copy bandwidth measured in the same run, tokens/s, the other
-standard workloads (prefix-shared batch, long-context split-K, mixed chunked
-prefill + decode with the prefill's matrix-core utilisation, verification
-of 4 drafted-token rows per sequence, the headline step over an E4M3
-cache), a parity sample against the CPU oracle, and the oracle itself timed
-on a bounded sample of the headline workload on one host core (a baseline,
-not a target).
+the bandwidth a plain streaming-read kernel reaches in the same run (over
+4 GiB, and over 28 buffers of one decode layer's bytes launched back to back,
+the achievable ceiling for a launch of that size), tokens/s, the other
+standard workloads (prefix-shared batch, long-context decode in the
+automatic partition mode, mixed chunked prefill + decode with the prefill's
+matrix-core utilisation and a cold-cache store, verification of 4
+drafted-token rows per sequence, the headline step over an E4M3 cache), a
+parity sample against the CPU oracle, and the oracle itself timed on the
+host's cores (a worker pool started before the GPU is touched) for a few
+seconds per workload, on the input bits the GPU used (a baseline, not a
+target).
 
 Other modes: --pmc-pass runs only the headline decode launches and one
 calibration copy of known size (for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE);
@@ -182,11 +186,76 @@ def time_each_launch(fns, rounds):
     return a.elapsed_time(z) / (rounds * len(fns))
 
 
-def copy_bandwidth(device, nbytes=2 << 30):
-    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=device).normal_()
-    dst = torch.empty_like(src)
-    ms = time_region(lambda: dst.copy_(src), 10, 3)
-    return 2 * nbytes / (ms * 1e-3) / 1e9
+PROBE_LIB = os.path.join(ROOT, "paged_attention_kv_store_amd", "libpkv_probe.so")
+_probe = None
+
+
+def probe_lib():
+    """libpkv_probe.so: the streaming-read kernel (a measurement aid)."""
+    global _probe
+    if _probe is None:
+        import ctypes
+        if not os.path.exists(PROBE_LIB):
+            raise RuntimeError(f"{PROBE_LIB} is not built; run paged_attention_kv_store_amd/build.py")
+        _probe = ctypes.CDLL(PROBE_LIB)
+        _probe.pkv_probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.c_void_p, ctypes.c_void_p]
+        _probe.pkv_probe_hbm_read.restype = ctypes.c_int
+    return _probe
+
+
+def hbm_read(buf, workgroups, in_flight, sink):
+    rc = probe_lib().pkv_probe_hbm_read(buf.data_ptr(), buf.numel() * buf.element_size(), workgroups, in_flight,
+                                        sink.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    if rc != 0:
+        raise RuntimeError(f"pkv_probe_hbm_read: HIP error {rc}")
+
+
+PROBE_SHAPES = [(512, 8), (1024, 4), (2048, 8), (2048, 16), (4096, 16)]   # (workgroups, loads in flight)
+
+
+def read_ceiling(device, layer_bytes, layers):
+    """Bandwidth of a plain streaming read (in-tree kernel, every byte read
+    once with 16-byte loads), the best of a few launch shapes: over one 4 GiB
+    buffer, and over `layers` distinct buffers of one decode layer's bytes
+    launched back to back (as the step's decode launches are)."""
+    sink = torch.zeros(8192, dtype=torch.int32, device=device)
+    big = torch.empty(4 << 30, dtype=torch.uint8, device=device).fill_(1)
+    best_big = min(time_each_launch([lambda wg=wg, f=f: hbm_read(big, wg, f, sink)], 5)
+                   for wg, f in PROBE_SHAPES)
+    del big
+    torch.cuda.empty_cache()
+    nb = int(layer_bytes) // 16 * 16
+    bufs = [torch.empty(nb, dtype=torch.uint8, device=device).fill_(1) for _ in range(layers)]
+    best_layer = min(time_each_launch([lambda b=b, wg=wg, f=f: hbm_read(b, wg, f, sink) for b in bufs], 4)
+                     for wg, f in PROBE_SHAPES)
+    del bufs
+    torch.cuda.empty_cache()
+    return {"kernel": "hbm_read_kernel (paged_attention_kv_store_amd/probe/hbm_read.hip), best of "
+                      + ", ".join(f"{wg} workgroups x {f} loads in flight" for wg, f in PROBE_SHAPES),
+            "GBps_4GiB": round((4 << 30) / (best_big * 1e-3) / 1e9, 1),
+            "GBps_layer_bytes": round(nb / (best_layer * 1e-3) / 1e9, 1),
+            "layer_bytes_us": round(best_layer * 1e3, 2), "layer_bytes": nb, "layer_buffers": layers}
+
+
+def cold_store_ms(store, device, rounds=10):
+    """Median time of one store launch after a 1 GiB streaming read has
+    replaced the last-level cache's contents (so neither the new rows nor the
+    cache rows it writes are resident), one event pair around the store."""
+    sink = torch.zeros(8192, dtype=torch.int32, device=device)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=device).fill_(1)
+    times = []
+    for _ in range(rounds):
+        hbm_read(flush, 2048, 8, sink)
+        a = torch.cuda.Event(enable_timing=True)
+        z = torch.cuda.Event(enable_timing=True)
+        a.record()
+        store()
+        z.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(z))
+    del flush
+    return float(np.median(times))
 
 
 # --------------------------------------------------------------------------
@@ -266,44 +335,121 @@ def load_traffic(dec_bytes):
 # CPU baseline: the oracle on a bounded sample of the headline workload
 # --------------------------------------------------------------------------
 
-def cpu_baseline(b: W.PagedBatch, budget_s=12.0):
-    import oracle
-    try:
-        from threadpoolctl import threadpool_limits
-    except Exception:  # pragma: no cover
-        threadpool_limits = None
-    q = W.host_bits(b.q)
-    kc, vc = W.host_bits(b.k_cache), W.host_bits(b.v_cache)
-    bt, ctx = b.pool.block_tables, b.pool.context_lens
-    e = b.q.element_size()
-    done_bytes, t_used, seqs = 0.0, 0.0, 0
-    limiter = threadpool_limits(limits=1) if threadpool_limits else None
-    try:
-        t0 = time.perf_counter()
-        while t_used <= budget_s:
-            s = seqs % b.num_seqs
-            oracle.paged_attention_decode(q[s:s + 1], kc, vc, bt[s:s + 1], ctx[s:s + 1], b.scale,
-                                          b.block_size)
-            c = int(ctx[s])
-            done_bytes += c * b.num_kv_heads * b.head_dim * e * 2 + 2 * b.num_q_heads * b.head_dim * e
-            seqs += 1
-            t_used = time.perf_counter() - t0
-    finally:
-        if limiter is not None:
-            limiter.__exit__(None, None, None)
-    model = "unknown CPU"
+def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
                 if line.startswith("model name"):
-                    model = line.split(":", 1)[1].strip()
-                    break
+                    return line.split(":", 1)[1].strip()
     except OSError:  # pragma: no cover
         pass
-    return {"value": done_bytes / t_used / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{seqs} sequence decodes (layer 0's {b.num_seqs} sequences, cycled) by the "
-                      f"float64 oracle in {t_used:.1f} s on one host core of a {model} "
-                      f"({seqs / t_used:.1f} seq/s)"}
+    return "unknown CPU"
+
+
+def baseline_workers():
+    # the host share of one GPU is 16 threads; never more than the affinity allows
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+class OracleBaseline:
+    """The float64 oracle timed on the host's cores (oracle/baseline.py, a
+    helper process whose worker pool starts before this process touches the
+    GPU). Each workload's inputs are copied back from the GPU, so the oracle
+    times the very bits the kernels read."""
+
+    def __init__(self, budget_s):
+        import subprocess
+        self.workers = baseline_workers()
+        self.budget_s = budget_s
+        self.proc = subprocess.Popen([sys.executable, "-m", "oracle.baseline", str(self.workers)], cwd=ROOT,
+                                     stdin=subprocess.PIPE, stdout=subprocess.PIPE, text=True)
+        self.ready = None
+        self.results = {}
+
+    def _reply(self):
+        line = self.proc.stdout.readline()
+        if not line:
+            raise RuntimeError("the oracle baseline helper ended")
+        return json.loads(line)
+
+    def run(self, name, kind, arrays, scale, block_size, work, unit, describe):
+        """Time the oracle on a sample of one workload. arrays: host numpy
+        (bf16 as uint16 bits); work(units) -> (algorithmic work of the sample,
+        tokens or rows of the sample)."""
+        import shutil
+        import tempfile
+        if self.ready is None:
+            self.ready = self._reply()
+        d = tempfile.mkdtemp(prefix="pkv_baseline_")
+        try:
+            for k, a in arrays.items():
+                np.save(os.path.join(d, k + ".npy"), np.ascontiguousarray(a), allow_pickle=False)
+            req = {"kind": kind, "dir": d, "scale": scale, "block_size": block_size, "budget_s": self.budget_s}
+            self.proc.stdin.write(json.dumps(req) + "\n")
+            self.proc.stdin.flush()
+            rep = self._reply()
+        finally:
+            shutil.rmtree(d, ignore_errors=True)
+        if "error" in rep:
+            raise RuntimeError(f"oracle baseline on {name}: {rep['error']}")
+        amount, items = work(rep["units"])
+        self.results[name] = {"value": round(amount / rep["seconds"], 3), "unit": unit,
+                              "items_per_s": round(items / rep["seconds"], 2),
+                              "seconds": round(rep["seconds"], 2),
+                              "sample": f"{describe(rep['units'])}, {rep['passes']:.2f} passes"}
+        return self.results[name]
+
+    def close(self):
+        try:
+            self.proc.stdin.write("quit\n")
+            self.proc.stdin.flush()
+            self.proc.wait(timeout=60)
+        except Exception:  # pragma: no cover
+            self.proc.kill()
+
+
+def decode_arrays(b, k_cache=None, v_cache=None):
+    """Host copies of a decode batch's inputs as the GPU holds them."""
+    return {"q": W.host_bits(b.q), "k_cache": W.host_bits(b.k_cache if k_cache is None else k_cache),
+            "v_cache": W.host_bits(b.v_cache if v_cache is None else v_cache),
+            "block_tables": np.ascontiguousarray(b.pool.block_tables), "context_lens": b.pool.context_lens}
+
+
+def baseline_decode(base, name, b, k_cache=None, v_cache=None):
+    if base is None:
+        return
+    hkv, d, e = b.num_kv_heads, b.head_dim, b.k_cache.element_size()
+    ctx = b.pool.context_lens.astype(np.int64)
+
+    def work(units):
+        seqs = [u[0] for u in units]
+        return float(sum(ctx[s] * hkv * d * e * 2 + 2 * b.num_q_heads * d * b.q.element_size() for s in seqs)) / 1e9, \
+            float(len(seqs))
+    base.run(name, "decode", decode_arrays(b, k_cache, v_cache), b.scale, b.block_size, work, "GB/s",
+             lambda units: f"{len(units)} sequence decodes of the {b.num_seqs} sequences in index order, "
+                           f"cycled (float64 oracle, all q-heads)")
+
+
+def baseline_prefill(base, name, b):
+    if base is None:
+        return
+    cu, ctx = b.cu_seqlens_q, b.pool.context_lens.astype(np.int64)
+    g = b.num_q_heads // b.num_kv_heads
+
+    def work(units):
+        fl = 0.0
+        rows = 0
+        for c, _h in units:
+            L = int(cu[c + 1] - cu[c])
+            prior = int(ctx[c]) - L
+            fl += (L * prior + L * (L + 1) // 2) * g * 4 * b.head_dim
+            rows += L
+        return fl / 1e12, rows / b.num_kv_heads
+    arrays = decode_arrays(b)
+    arrays["cu_seqlens_q"] = np.asarray(cu, np.int32)
+    base.run(name, "prefill", arrays, b.scale, b.block_size, work, "TFLOP/s",
+             lambda units: f"{len(units)} (chunk, kv-head) slices of the {len(cu) - 1} chunks x "
+                           f"{b.num_kv_heads} kv-heads, chunk by chunk, cycled (float64 oracle, causal)")
 
 
 # --------------------------------------------------------------------------
@@ -367,7 +513,7 @@ def fp8_step(device, steps, warmup, bf16_step_ms, partition=0):
             "partition": partition, "cache": "E4M3 codes, per-kv-head scales; store fused into decode"}
 
 
-def secondary(device, steps, warmup, algo, bf16_step_ms, partition=0):
+def secondary(device, steps, warmup, algo, bf16_step_ms, partition=0, base=None):
     res = {"qwen3_fp8": fp8_step(device, steps, warmup, bf16_step_ms, partition)}
     torch.cuda.empty_cache()
     b = W.llama_prefix(device=device).batches[0]
@@ -388,19 +534,26 @@ def secondary(device, steps, warmup, algo, bf16_step_ms, partition=0):
                                torch.full((b.num_seqs // 8,), 32 * b.block_size, dtype=torch.int32,
                                           device=device),
                                b.scale, b.max_ctx, 8, 32 * b.block_size), steps, warmup)}
+    baseline_decode(base, "llama_prefix", b)
     del dec, b
     b = W.long_splitk(device=device).batches[0]
     bt = torch.as_tensor(b.pool.block_tables, device=device)
     cl = torch.as_tensor(b.pool.context_lens, device=device)
+    auto_part = pkv.decode_auto_partition(b.num_seqs, b.num_kv_heads, b.max_ctx)
     dec = pkv.DecodeLaunch(torch.empty_like(b.q), b.q, b.k_cache, b.v_cache, bt, cl, b.scale,
-                           b.max_ctx, partition_size=512, algo=algo)
+                           b.max_ctx, partition_size="auto", algo=algo)
     ms = time_region(dec, steps, warmup)
+    dec512 = pkv.DecodeLaunch(torch.empty_like(b.q), b.q, b.k_cache, b.v_cache, bt, cl, b.scale,
+                              b.max_ctx, partition_size=512, algo=algo)
+    ms512 = time_region(dec512, steps, warmup)
     by = decode_bytes(b)
     res["long_splitk"] = {"ms": ms, "GBps": by / ms / 1e6, "pct_hbm_peak": 100 * by / ms / 1e6 / HBM_PEAK_GBS,
-                          "tokens_per_s": b.num_seqs / (ms * 1e-3), "partition": 512,
+                          "tokens_per_s": b.num_seqs / (ms * 1e-3), "partition": "auto",
+                          "auto_partition_size": auto_part, "splitk_512_ms": ms512,
                           "balanced_ms": balanced_ms(b, bt, cl, steps, warmup),
                           "planned_ms": planned_ms(b, bt, cl, steps, warmup)}
-    del dec, b
+    baseline_decode(base, "long_splitk", b)
+    del dec, dec512, b
     wl = W.mixed(device=device)
     pre, db = wl.prefill, wl.batches[0]
     store = pkv.StoreLaunch(pre.k_new, pre.v_new, pre.k_cache, pre.v_cache, pre.slot_mapping)
@@ -442,8 +595,10 @@ def secondary(device, steps, warmup, algo, bf16_step_ms, partition=0):
                             torch.as_tensor(db.pool.context_lens, device=device), steps, warmup)
     t_dec_plan = planned_ms(db, torch.as_tensor(db.pool.block_tables, device=device),
                             torch.as_tensor(db.pool.context_lens, device=device), steps, warmup)
+    t_store_cold = cold_store_ms(store, device)
     fl = prefill_flops(pre)
     res["mixed"] = {"store_ms": t_store, "store_GBps": store_bytes(pre) / t_store / 1e6,
+                    "store_cold_ms": t_store_cold, "store_cold_GBps": store_bytes(pre) / t_store_cold / 1e6,
                     "prefill_ms": t_pre, "prefill_TFLOPs": fl / t_pre / 1e9,
                     "prefill_mfma_util_pct": 100 * fl / t_pre / 1e9 / BF16_MFMA_PEAK_TFLOPS,
                     "decode_ms": t_dec, "decode_GBps": decode_bytes(db) / t_dec / 1e6,
@@ -452,6 +607,8 @@ def secondary(device, steps, warmup, algo, bf16_step_ms, partition=0):
                     "prefill_tokens_per_s": 4096 / (t_pre * 1e-3),
                     "serial_step_ms": t_serial, "two_stream_step_ms": t_two,
                     "tokens_per_s_two_streams": 4224 / (t_two * 1e-3)}
+    baseline_decode(base, "mixed_decode", db)
+    baseline_prefill(base, "mixed_prefill", pre)
     del store, prefill, dec, wl, pre, db
     torch.cuda.empty_cache()
     # the same chunked prefill over E4M3 caches (its own draws, same lengths and tables)
@@ -481,6 +638,7 @@ def secondary(device, steps, warmup, algo, bf16_step_ms, partition=0):
     by = decode_bytes(sv)
     res["spec_verify"] = {"ms": ms, "GBps": by / ms / 1e6, "pct_hbm_peak": 100 * by / ms / 1e6 / HBM_PEAK_GBS,
                           "rows_per_s": sv.q.shape[0] / (ms * 1e-3), "rows_per_seq": 4}
+    baseline_prefill(base, "spec_verify", sv)
     return res
 
 
@@ -719,6 +877,8 @@ def main():
                     help="store and decode as two launches per layer instead of the fused call")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=3.0,
+                    help="seconds of wall time the oracle baseline spends on each workload")
     ap.add_argument("--pmc-pass", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--summarize-trace", nargs=4, metavar=("STATS_CSV", "TRACE_CSV", "OUT_MD", "COMMAND"))
@@ -739,6 +899,8 @@ def main():
         print("bench.py measures one GPU: this library has no multi-GPU path "
               "(decode would shard by sequence or kv-head with no exchange)", file=sys.stderr)
         sys.exit(2)
+    # the oracle baseline's worker processes start before anything touches the GPU
+    base = None if args.no_cpu_baseline else OracleBaseline(args.cpu_budget)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     device = torch.device("cuda:0")
     torch.cuda.set_device(device)
@@ -786,7 +948,7 @@ def main():
     dec_ms = time_each_launch([ly.decode if args.unfused else ly.fused for ly in lyr], 4)
     store_ms = time_each_launch([ly.store for ly in lyr], 2)
     plan_us = time_each_launch([plan_launch], 20) * 1e3 if plan_launch is not None else None
-    copy_gbps = copy_bandwidth(device)
+    ceiling = read_ceiling(device, dec_bytes, len(lyr))
     achieved = dec_bytes / (dec_ms * 1e-3) / 1e9
 
     # parity sample of layer 0's output against the oracle
@@ -830,28 +992,40 @@ def main():
                    "parallelism": "single GPU"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(b0.num_seqs / (ms * 1e-3), 1),
-        "copy_GBps_measured": round(copy_gbps, 1),
+        "hbm_read_ceiling": ceiling,
         "roofline": {"bound": "hbm",
                      "kernel": "decode_mfma_kernel (one layer per launch%s)" % (
                          "" if args.unfused else ", store fused"),
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(dec_bytes),
                      "avg_launch_us": round(dec_ms * 1e3, 2),
-                     "algorithmic_bytes_per_launch": dec_bytes},
+                     "algorithmic_bytes_per_launch": dec_bytes,
+                     "frac_of_read_ceiling_same_bytes": round(achieved / ceiling["GBps_layer_bytes"], 4)},
         "store_avg_launch_us": round(store_ms * 1e3, 2),
         "plan_avg_launch_us": None if plan_us is None else round(plan_us, 2),
         "parity_sample_max_abs_err": parity_err,
     }
+    if base is not None:
+        log("oracle baseline on the host: the headline's layer 0")
+        baseline_decode(base, "qwen3_decode", b0)
     if not args.no_secondary:
         del lyr, wl
         if not args.eager:
             del graph, run
         torch.cuda.empty_cache()
         log("secondary workloads")
-        result["secondary"] = secondary(device, max(5, args.steps // 2), 3, args.algo, ms, args.partition)
-    if not args.no_cpu_baseline:
-        log("oracle baseline on the host")
-        result["cpu_baseline"] = cpu_baseline(W.qwen3_decode(device="cpu", layers=1).batches[0])
+        result["secondary"] = secondary(device, max(5, args.steps // 2), 3, args.algo, ms, args.partition, base)
+    if base is not None:
+        base.close()
+        head = base.results["qwen3_decode"]
+        result["cpu_baseline"] = {
+            "value": head["value"], "unit": head["unit"], "cores": base.workers, "kind": "oracle",
+            "sample": f"the float64 oracle (numpy, one BLAS thread per worker process, {base.workers} worker "
+                      f"processes) on the host's {cpu_model()}, on the GPU's own input bits: "
+                      f"{head['sample']}, of the headline's layer 0 in {head['seconds']} s "
+                      f"({head['items_per_s']} sequences/s); each workload below likewise for about "
+                      f"{args.cpu_budget:g} s",
+            "per_workload": base.results}
     print(json.dumps(result), flush=True)
 
 

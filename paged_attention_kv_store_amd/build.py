@@ -87,5 +87,24 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     return LIB
 
 
+PROBE_SRC = os.path.join(PKG, "probe", "hbm_read.hip")
+PROBE_LIB = os.path.join(PKG, "libpkv_probe.so")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """The benchmark's streaming-read kernel (a measurement aid, kept out of
+    libpkv.so): libpkv_probe.so."""
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [HIPCC, *FLAGS, "-shared", PROBE_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {PROBE_SRC}:\n{res.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_probe(verbose="-v" in sys.argv))
