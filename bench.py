@@ -655,16 +655,9 @@ def calib_bytes():
     return 2 * CALIB_TOKENS * row + 4 * CALIB_TOKENS, 2 * CALIB_TOKENS * row
 
 
-def pmc_pass(device, layers, partition):
-    """The headline's launches once each (decode with the store fused, as
-    timed), then a plain copy of known size: a kv_cache_store of 65536 new
-    rows into a pool of exactly as many slots (identity slots), i.e. 256 MiB
-    read and 256 MiB written."""
-    wl, lyr, plan_launch = build_headline(device, layers, partition, "auto")
-    torch.cuda.synchronize()
-    for ly in lyr:
-        ly.fused()
-    torch.cuda.synchronize()
+def _calibration_store(device):
+    """A plain copy of known size: kv_cache_store of 65536 new rows into a pool
+    of exactly as many slots (identity slots), 256 MiB read and written."""
     k = torch.empty((CALIB_TOKENS, 8, 128), dtype=torch.bfloat16, device=device).normal_()
     v = torch.empty_like(k).normal_()
     kc = torch.empty((CALIB_TOKENS // 16, 16, 8, 128), dtype=torch.bfloat16, device=device)
@@ -673,8 +666,154 @@ def pmc_pass(device, layers, partition):
     torch.cuda.synchronize()
     pkv.kv_cache_store(k, v, kc, vc, slots)
     torch.cuda.synchronize()
-    print(json.dumps({"pmc_pass": "done", "decode_launches": len(lyr),
-                      "calibration_read_write_bytes": calib_bytes()}))
+
+
+def split_partial_bytes(b, part):
+    """Bytes of split-K partials written and read back: (max, sum, D outputs)
+    in fp32 per (sequence, q-head, partition) of sequences with more than one
+    partition."""
+    if not part:
+        return 0.0
+    parts = -(-b.pool.context_lens.astype(np.int64) // part)
+    n = int(parts[parts > 1].sum())
+    return float(2 * n * b.num_q_heads * (b.head_dim + 2) * 4)
+
+
+def pmc_pass(device, layers, partition):
+    """Every bandwidth workload's launches, in a fixed order, for rocprofv3
+    --pmc FETCH_SIZE / WRITE_SIZE runs, then a plain copy of known size (the
+    calibration). Prints the manifest the summary walks: for each segment,
+    this library's dispatches in launch order and the algorithmic bytes of
+    one call. Repeated launches of a batch read more bytes than the 256 MB
+    last-level cache holds, except where noted."""
+    segs = []
+
+    def seg(name, calls, per_call, algo_bytes, desc, report=True, extra=0.0):
+        segs.append({"name": name, "calls": calls, "dispatches_per_call": per_call,
+                     "algorithmic_bytes_per_call": float(algo_bytes), "implementation_bytes_per_call": float(extra),
+                     "desc": desc, "report": report})
+
+    wl, lyr, plan_launch = build_headline(device, layers, partition, "auto")
+    b0 = wl.batches[0]
+    torch.cuda.synchronize()
+    if plan_launch is not None:
+        plan_launch()
+        # build_headline made the plan once already
+        seg("qwen3_plan", 2, 1, 0, "decode_plan_kernel", report=False)
+    for ly in lyr:
+        ly.fused()
+    torch.cuda.synchronize()
+    seg("qwen3_decode", len(lyr), 1, decode_bytes(b0) + store_bytes(b0),
+        f"decode_mfma_kernel, partition {partition}, store fused; {len(lyr)} distinct layers")
+    del wl, lyr, plan_launch
+    torch.cuda.empty_cache()
+
+    wl = W.qwen3_decode_fp8(device=device, layers=layers)
+    b8 = wl.batches[0]
+    bt = torch.as_tensor(b8.pool.block_tables, device=device)
+    cl = torch.as_tensor(b8.pool.context_lens, device=device)
+    plan = pkv.new_decode_plan(b8.num_seqs, device)
+    calls = [pkv.DecodeStoreFp8Launch(torch.empty_like(b.q), b.q, b.k_cache, b.v_cache, b.k_scale, b.v_scale, bt, cl,
+                                      b.k_new, b.v_new, b.slot_mapping, b.scale, b.max_ctx,
+                                      partition_size="planned", workspace=plan) for b in wl.batches]
+    torch.cuda.synchronize()
+    pkv.decode_plan(plan, bt, cl, b8.max_ctx, b8.block_size)
+    seg("qwen3_fp8_plan", 1, 1, 0, "decode_plan_kernel", report=False)
+    for c in calls:
+        c()
+    torch.cuda.synchronize()
+    seg("qwen3_fp8_decode", len(calls), 1, decode_bytes(b8) + store_bytes(b8),
+        f"decode_mfma_kernel over E4M3 caches, planned, store fused; {len(calls)} distinct layers")
+    del wl, calls, plan, bt, cl
+    torch.cuda.empty_cache()
+
+    b = W.llama_prefix(device=device).batches[0]
+    bt = torch.as_tensor(b.pool.block_tables, device=device)
+    cl = torch.as_tensor(b.pool.context_lens, device=device)
+    dec = pkv.DecodeLaunch(torch.empty_like(b.q), b.q, b.k_cache, b.v_cache, bt, cl, b.scale, b.max_ctx,
+                           partition_size=0)
+    shared = pkv.SharedPrefixDecodeLaunch(
+        torch.empty_like(b.q), b.q, b.k_cache, b.v_cache, bt, cl,
+        torch.arange(0, b.num_seqs + 1, 8, dtype=torch.int32, device=device),
+        torch.full((b.num_seqs // 8,), 32 * b.block_size, dtype=torch.int32, device=device), b.scale, b.max_ctx, 8,
+        32 * b.block_size)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dec()
+    torch.cuda.synchronize()
+    ub = decode_bytes(b, unique_blocks=True)
+    seg("llama_prefix_decode", 3, 1, ub, "decode_mfma_kernel, one pass; algorithmic bytes count shared blocks once "
+        f"(logical bytes {decode_bytes(b):.4g})")
+    for _ in range(3):
+        shared()
+    torch.cuda.synchronize()
+    sp_extra = float(2 * b.num_seqs * b.num_q_heads * (b.head_dim + 2) * 4 + 8 * b.num_seqs)
+    seg("llama_prefix_shared", 3, 2, ub, "prefill_kernel (prefix partials) + decode_mfma_kernel (own tokens, merged)",
+        extra=sp_extra)
+    del b, bt, cl, dec, shared
+    torch.cuda.empty_cache()
+
+    b = W.long_splitk(device=device).batches[0]
+    bt = torch.as_tensor(b.pool.block_tables, device=device)
+    cl = torch.as_tensor(b.pool.context_lens, device=device)
+    part = pkv.decode_auto_partition(b.num_seqs, b.num_kv_heads, b.max_ctx)
+    dec = pkv.DecodeLaunch(torch.empty_like(b.q), b.q, b.k_cache, b.v_cache, bt, cl, b.scale, b.max_ctx,
+                           partition_size="auto")
+    torch.cuda.synchronize()
+    seg("long_workspace_init", 1, 1, 0, "zero_ints_kernel (the new workspace's counters)", report=False)
+    for _ in range(3):
+        dec()
+    torch.cuda.synchronize()
+    seg("long_splitk_auto", 3, 1, decode_bytes(b), f"decode_mfma_kernel, split-K at {part} tokens (auto), merged "
+        "in the same launch", extra=split_partial_bytes(b, part))
+    del b, bt, cl, dec
+    torch.cuda.empty_cache()
+
+    wl = W.mixed(device=device)
+    pre, db = wl.prefill, wl.batches[0]
+    pkv.kv_cache_store(pre.k_new, pre.v_new, pre.k_cache, pre.v_cache, pre.slot_mapping)
+    torch.cuda.synchronize()
+    seg("mixed_store", 1, 1, store_bytes(pre), "kv_store_kernel, 4224 new rows")
+    prefill = pkv.PrefillLaunch(torch.empty_like(pre.q), pre.q, pre.k_cache, pre.v_cache,
+                                torch.as_tensor(pre.pool.block_tables, device=device),
+                                torch.as_tensor(pre.cu_seqlens_q, device=device),
+                                torch.as_tensor(pre.pool.context_lens, device=device), pre.scale, 512, pre.max_ctx)
+    dec = pkv.DecodeLaunch(torch.empty_like(db.q), db.q, db.k_cache, db.v_cache,
+                           torch.as_tensor(db.pool.block_tables, device=device),
+                           torch.as_tensor(db.pool.context_lens, device=device), db.scale, db.max_ctx)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        prefill()
+    torch.cuda.synchronize()
+    seg("mixed_prefill", 2, 1, decode_bytes(pre), "prefill_kernel, 8 chunks x 512 causal rows (algorithmic bytes: "
+        "each chunk's K/V once, q, out; the kernel re-reads them per q-tile, mostly from L2)")
+    for _ in range(3):
+        dec()
+    torch.cuda.synchronize()
+    seg("mixed_decode", 3, 1, decode_bytes(db), "decode_mfma_kernel, one pass, 128 sequences")
+    del wl, pre, db, prefill, dec
+    torch.cuda.empty_cache()
+
+    sv = W.spec_verify(device=device).prefill
+    pkv.kv_cache_store(sv.k_new, sv.v_new, sv.k_cache, sv.v_cache, sv.slot_mapping)
+    torch.cuda.synchronize()
+    seg("spec_verify_store", 1, 1, store_bytes(sv), "kv_store_kernel, 512 new rows", report=False)
+    verify = pkv.PrefillLaunch(torch.empty_like(sv.q), sv.q, sv.k_cache, sv.v_cache,
+                               torch.as_tensor(sv.pool.block_tables, device=device),
+                               torch.as_tensor(sv.cu_seqlens_q, device=device),
+                               torch.as_tensor(sv.pool.context_lens, device=device), sv.scale, 4, sv.max_ctx)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        verify()
+    torch.cuda.synchronize()
+    seg("spec_verify", 3, 1, decode_bytes(sv), "prefill_kernel, 128 sequences x 4 causal rows")
+    del sv, verify
+    torch.cuda.empty_cache()
+
+    _calibration_store(device)
+    seg("calibration", 1, 1, 0, "kv_store_kernel, 65536 rows of 2 KiB, identity slots", report=False)
+    print(json.dumps({"pmc_pass": "done", "segments": segs, "calibration_read_write_bytes": calib_bytes(),
+                      "decode_source_hash": decode_source_hash()}))
 
 
 PREFILL_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU",
@@ -751,45 +890,88 @@ def summarize_prefill_pmc(counter_csv, trace_csv, out_md, command):
     print(f"wrote {out_md}")
 
 
-def summarize_pmc(fetch_csv, write_csv):
-    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the decode launches, each
-    scaled by (known bytes / counter reading) of the calibration store, which
-    is the last kv_store_kernel dispatch of a --pmc-pass run."""
-    def per_kernel(path, counter):
-        dec, store = [], []
-        for r in csv.DictReader(open(path)):
-            if r.get("Counter_Name") != counter:
-                continue
-            name, val = r["Kernel_Name"], float(r["Counter_Value"]) * 1024.0   # KiB -> bytes
-            if "decode_mfma_kernel" in name:
-                dec.append(val)
-            elif "kv_store_kernel" in name:
-                store.append((int(r["Dispatch_Id"]), val))
-        return dec, max(store)[1]
-    f_dec, f_cal = per_kernel(fetch_csv, "FETCH_SIZE")
-    w_dec, w_cal = per_kernel(write_csv, "WRITE_SIZE")
-    read_known, write_known = calib_bytes()
-    fr, fw = read_known / f_cal, write_known / w_cal
-    wl = W.qwen3_decode(device="cpu", layers=1)
+def summarize_pmc(fetch_csv, write_csv, manifest, command):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of every segment of a
+    --pmc-pass run, each scaled by (known bytes / counter reading) of the
+    calibration copy that ends the pass. Writes profiles/decode_qwen3_traffic.*
+    (the headline decode, read back by the benchmark while the decode
+    source is unchanged) and profiles/hbm_traffic_all_workloads.md."""
+    man = None
+    for line in open(manifest):
+        line = line.strip()
+        if line.startswith("{") and '"pmc_pass"' in line:
+            man = json.loads(line)
+    if man is None:
+        raise RuntimeError(f"{manifest}: no pmc-pass manifest line")
+
+    def ours(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r.get("Counter_Name") == counter and "pkv::" in r["Kernel_Name"]]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        return [(r["Kernel_Name"].split("(")[0].replace("void ", ""), float(r["Counter_Value"]) * 1024.0)
+                for r in rows]
+    fetch, write = ours(fetch_csv, "FETCH_SIZE"), ours(write_csv, "WRITE_SIZE")
+    need = sum(sg["calls"] * sg["dispatches_per_call"] for sg in man["segments"])
+    if len(fetch) != need or len(write) != need:
+        raise RuntimeError(f"expected {need} dispatches of this library, found {len(fetch)} / {len(write)}")
+    read_known, write_known = man["calibration_read_write_bytes"]
+    fr, fw = read_known / fetch[-1][1], write_known / write[-1][1]
+    rows, i = [], 0
+    for sg in man["segments"]:
+        n = sg["calls"] * sg["dispatches_per_call"]
+        f_seg, w_seg = fetch[i:i + n], write[i:i + n]
+        i += n
+        if not sg["report"]:
+            continue
+        kernels = sorted(set(k for k, _ in f_seg))
+        f_call = sum(v for _, v in f_seg) * fr / sg["calls"]
+        w_call = sum(v for _, v in w_seg) * fw / sg["calls"]
+        rows.append(dict(sg, kernels=kernels, fetch=f_call, write=w_call, fetch_raw=sum(v for _, v in f_seg) / sg["calls"],
+                         write_raw=sum(v for _, v in w_seg) / sg["calls"]))
+    head = next(r for r in rows if r["name"] == "qwen3_decode")
     out = {
         "kernel": "decode_mfma_kernel (planned single pass, store of the 60 new rows fused), qwen3-shaped layer",
-        "decode_source_hash": decode_source_hash(),
-        "fetch_bytes_raw_per_launch": float(np.mean(f_dec)),
-        "write_bytes_raw_per_launch": float(np.mean(w_dec)),
-        "calibration": {"kernel": "kv_store_kernel, 65536 rows of 2 KiB, identity slots",
-                        "read_bytes": read_known, "write_bytes": write_known,
-                        "fetch_raw": f_cal, "write_raw": w_cal,
+        "decode_source_hash": man["decode_source_hash"],
+        "fetch_bytes_raw_per_launch": head["fetch_raw"], "write_bytes_raw_per_launch": head["write_raw"],
+        "calibration": {"kernel": "kv_store_kernel, 65536 rows of 2 KiB, identity slots", "read_bytes": read_known,
+                        "write_bytes": write_known, "fetch_raw": fetch[-1][1], "write_raw": write[-1][1],
                         "fetch_factor": fr, "write_factor": fw},
-        "hbm_bytes_per_launch": float(np.mean(f_dec)) * fr + float(np.mean(w_dec)) * fw,
-        "algorithmic_bytes_per_launch": decode_bytes(wl.batches[0]) + store_bytes(wl.batches[0]),
-        "launches_averaged": len(f_dec),
+        "hbm_bytes_per_launch": head["fetch"] + head["write"],
+        "algorithmic_bytes_per_launch": head["algorithmic_bytes_per_call"],
+        "launches_averaged": head["calls"],
+        "command": command,
     }
+    if out["decode_source_hash"] != decode_source_hash():
+        raise RuntimeError("the decode sources changed since the counter pass")
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1)
     with open(TRAFFIC_FILE[:-5] + ".md", "w") as f:
         f.write(traffic_markdown(out))
+    lines = ["# HBM traffic of every bandwidth workload (rocprofv3 counters)", "",
+             "Counters FETCH_SIZE and WRITE_SIZE per dispatch of this library's kernels, in two passes over the same",
+             "launches, each scaled by the reading of a plain copy of known size that ends the pass",
+             f"(fetch factor {fr:.3f}, write factor {fw:.3f}); per call (a call of the shared-prefix decode is two",
+             "dispatches). Algorithmic bytes are those the benchmark divides by time; implementation bytes are what",
+             "the method does not need but this implementation moves on purpose (split-K and shared-prefix partials,",
+             "written and read back).", "", "Commands (from the repository root on one MI355X):", "", "```", command,
+             "```", "",
+             "| workload | kernels | calls | HBM read / call | HBM write / call | algorithmic / call | implementation extra | traffic / (algorithmic + extra) |",
+             "|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        tot = r["fetch"] + r["write"]
+        base = r["algorithmic_bytes_per_call"] + r["implementation_bytes_per_call"]
+        lines.append(f"| {r['name']}: {r['desc']} | {', '.join('`' + k + '`' for k in r['kernels'])} | {r['calls']} | "
+                     f"{r['fetch']:,.0f} | {r['write']:,.0f} | {r['algorithmic_bytes_per_call']:,.0f} | "
+                     f"{r['implementation_bytes_per_call']:,.0f} | {tot / base:.3f} |")
+    lines += ["", "Repeated calls of one batch (every workload but the two 28-layer steps) read the same bytes again;",
+              "every such batch is larger than the 256 MB last-level cache except the store, whose line is therefore",
+              "a warm figure. The shared-prefix row's algorithmic bytes count each shared block once, as the",
+              "prefix-shared decode's line in the benchmark does."]
+    md = os.path.join(os.path.dirname(TRAFFIC_FILE), "hbm_traffic_all_workloads.md")
+    with open(md, "w") as f:
+        f.write("\n".join(lines) + "\n")
     print(json.dumps(out))
+    print(f"wrote {md}")
 
 
 def traffic_markdown(t):
@@ -802,12 +984,10 @@ store of the 60 new K/V rows fused into it, as the benchmark's step launches it)
 {t['launches_averaged']} launches on distinct layer caches (4.7 GB in total, so the 256 MB last-level cache
 cannot hold them).
 
-Commands (from the repository root on one MI355X):
+Commands (on one MI355X; R is the repository root):
 
 ```
-rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch_out> -o run -- python3 bench.py --pmc-pass
-rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write_out> -o run -- python3 bench.py --pmc-pass
-python3 bench.py --summarize-pmc <fetch_out>/run_counter_collection.csv <write_out>/run_counter_collection.csv
+{t['command']}
 ```
 
 Calibration: the last dispatch of each pass is a plain copy of known size, a `kv_store_kernel`
@@ -880,7 +1060,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=3.0,
                     help="seconds of wall time the oracle baseline spends on each workload")
     ap.add_argument("--pmc-pass", action="store_true")
-    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "PASS_STDOUT", "COMMAND"))
     ap.add_argument("--summarize-trace", nargs=4, metavar=("STATS_CSV", "TRACE_CSV", "OUT_MD", "COMMAND"))
     ap.add_argument("--prefill-pmc-pass", action="store_true")
     ap.add_argument("--summarize-prefill-pmc", nargs=4, metavar=("COUNTER_CSV", "TRACE_CSV", "OUT_MD", "COMMAND"))
