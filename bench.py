@@ -214,28 +214,38 @@ def hbm_read(buf, workgroups, in_flight, sink):
 PROBE_SHAPES = [(512, 8), (1024, 4), (2048, 8), (2048, 16), (4096, 16)]   # (workgroups, loads in flight)
 
 
-def read_ceiling(device, layer_bytes, layers):
+def read_ceiling(device, layer_bytes, layers, fp8_layer_bytes=None):
     """Bandwidth of a plain streaming read (in-tree kernel, every byte read
     once with 16-byte loads), the best of a few launch shapes: over one 4 GiB
     buffer, and over `layers` distinct buffers of one decode layer's bytes
-    launched back to back (as the step's decode launches are)."""
+    launched back to back (as the step's decode launches are); the same for
+    the E4M3 layer's bytes when given."""
     sink = torch.zeros(8192, dtype=torch.int32, device=device)
     big = torch.empty(4 << 30, dtype=torch.uint8, device=device).fill_(1)
     best_big = min(time_each_launch([lambda wg=wg, f=f: hbm_read(big, wg, f, sink)], 5)
                    for wg, f in PROBE_SHAPES)
     del big
     torch.cuda.empty_cache()
-    nb = int(layer_bytes) // 16 * 16
-    bufs = [torch.empty(nb, dtype=torch.uint8, device=device).fill_(1) for _ in range(layers)]
-    best_layer = min(time_each_launch([lambda b=b, wg=wg, f=f: hbm_read(b, wg, f, sink) for b in bufs], 4)
-                     for wg, f in PROBE_SHAPES)
-    del bufs
-    torch.cuda.empty_cache()
-    return {"kernel": "hbm_read_kernel (paged_attention_kv_store_amd/probe/hbm_read.hip), best of "
-                      + ", ".join(f"{wg} workgroups x {f} loads in flight" for wg, f in PROBE_SHAPES),
-            "GBps_4GiB": round((4 << 30) / (best_big * 1e-3) / 1e9, 1),
-            "GBps_layer_bytes": round(nb / (best_layer * 1e-3) / 1e9, 1),
-            "layer_bytes_us": round(best_layer * 1e3, 2), "layer_bytes": nb, "layer_buffers": layers}
+
+    def per_layer(nbytes):
+        nb = int(nbytes) // 16 * 16
+        bufs = [torch.empty(nb, dtype=torch.uint8, device=device).fill_(1) for _ in range(layers)]
+        best = min(time_each_launch([lambda b=b, wg=wg, f=f: hbm_read(b, wg, f, sink) for b in bufs], 4)
+                   for wg, f in PROBE_SHAPES)
+        del bufs
+        torch.cuda.empty_cache()
+        return nb, best
+    nb, best_layer = per_layer(layer_bytes)
+    out = {"kernel": "hbm_read_kernel (paged_attention_kv_store_amd/probe/hbm_read.hip), best of "
+                     + ", ".join(f"{wg} workgroups x {f} loads in flight" for wg, f in PROBE_SHAPES),
+           "GBps_4GiB": round((4 << 30) / (best_big * 1e-3) / 1e9, 1),
+           "GBps_layer_bytes": round(nb / (best_layer * 1e-3) / 1e9, 1),
+           "layer_bytes_us": round(best_layer * 1e3, 2), "layer_bytes": nb, "layer_buffers": layers}
+    if fp8_layer_bytes:
+        nb8, best8 = per_layer(fp8_layer_bytes)
+        out.update({"GBps_fp8_layer_bytes": round(nb8 / (best8 * 1e-3) / 1e9, 1),
+                    "fp8_layer_bytes_us": round(best8 * 1e3, 2), "fp8_layer_bytes": nb8})
+    return out
 
 
 def cold_store_ms(store, device, rounds=10):
@@ -890,6 +900,27 @@ def summarize_prefill_pmc(counter_csv, trace_csv, out_md, command):
     print(f"wrote {out_md}")
 
 
+def summarize_counters(kernel, out_md, title, command, *csvs):
+    """Means per dispatch of every counter that rocprofv3 --pmc runs recorded
+    for kernels whose name contains `kernel`, and each wave-cycle counter as a
+    share of SQ_WAVE_CYCLES."""
+    vals = {}
+    for path in csvs:
+        for r in csv.DictReader(open(path)):
+            if kernel in r["Kernel_Name"]:
+                vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    mean = {k: float(np.mean(v)) for k, v in vals.items()}
+    lines = [f"# {title}", "", "Commands (on one MI355X; R is the repository root):", "", "```", command, "```", "",
+             "| counter | mean per dispatch | share of SQ_WAVE_CYCLES |", "|---|---|---|"]
+    wc = mean.get("SQ_WAVE_CYCLES")
+    for k in sorted(mean):
+        share = f"{100 * mean[k] / wc:.1f}%" if wc and (k.startswith("SQ_WAIT") or k.startswith("SQ_ACTIVE_INST")) else ""
+        lines.append(f"| {k} | {mean[k]:.4g} | {share} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote {out_md}")
+
+
 def summarize_pmc(fetch_csv, write_csv, manifest, command):
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of every segment of a
     --pmc-pass run, each scaled by (known bytes / counter reading) of the
@@ -1064,6 +1095,8 @@ def main():
     ap.add_argument("--summarize-trace", nargs=4, metavar=("STATS_CSV", "TRACE_CSV", "OUT_MD", "COMMAND"))
     ap.add_argument("--prefill-pmc-pass", action="store_true")
     ap.add_argument("--summarize-prefill-pmc", nargs=4, metavar=("COUNTER_CSV", "TRACE_CSV", "OUT_MD", "COMMAND"))
+    ap.add_argument("--summarize-counters", nargs="+", metavar="ARG",
+                    help="KERNEL OUT_MD TITLE COMMAND CSV [CSV ...]: means of the counters of one kernel")
     args = ap.parse_args()
 
     if args.summarize_pmc:
@@ -1074,6 +1107,9 @@ def main():
         return
     if args.summarize_prefill_pmc:
         summarize_prefill_pmc(*args.summarize_prefill_pmc)
+        return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this library has no multi-GPU path "
@@ -1128,7 +1164,11 @@ def main():
     dec_ms = time_each_launch([ly.decode if args.unfused else ly.fused for ly in lyr], 4)
     store_ms = time_each_launch([ly.store for ly in lyr], 2)
     plan_us = time_each_launch([plan_launch], 20) * 1e3 if plan_launch is not None else None
-    ceiling = read_ceiling(device, dec_bytes, len(lyr))
+    # the E4M3 layer moves the same rows with one byte per cache element
+    kv_elems = float(b0.pool.context_lens.astype(np.int64).sum()) * b0.num_kv_heads * b0.head_dim
+    stored = float(int((b0.slot_mapping >= 0).sum().item())) * b0.num_kv_heads * b0.head_dim
+    fp8_bytes = decode_bytes(b0) + store_bytes(b0) - 2 * kv_elems - 2 * stored
+    ceiling = read_ceiling(device, dec_bytes, len(lyr), fp8_bytes)
     achieved = dec_bytes / (dec_ms * 1e-3) / 1e9
 
     # parity sample of layer 0's output against the oracle
