@@ -135,7 +135,9 @@ __device__ void merge_and_write(const DecodeParams& p, int s, int g, int part, i
     }
     if (poisoned) L = __builtin_nanf("");
     if (n_parts <= 1) {
-      store_out<T>(p.out, (head0 + h) * D + d, O / L);
+      // with a shared prefix, a row with no key at all (an empty context) is
+      // zero, as the decode without one writes it
+      store_out<T>(p.out, (head0 + h) * D + d, (pre && M == neg_inf() && !poisoned) ? 0.f : O / L);
     } else {
       const int64_t base = (head0 + h) * p.num_partitions + part;
       coherent_store(p.ws_o + base * D + d, O);
@@ -259,7 +261,8 @@ __device__ __forceinline__ bool decode_item(const DecodeParams& p, int& g, int& 
   return true;
 }
 
-// Work item by size (single pass, no shared prefix). Two workgroups of this
+// Work item by size (single pass; after a shared prefix, sized by the tokens
+// past it, see stage_tiles). Two workgroups of this
 // kernel fit a compute unit, and with C units workgroup b and workgroup
 // b + C are placed on the same one (the dispatcher fills every unit once,
 // then again in the same order). Item x = sequence * kv_heads + kv-head;
@@ -282,7 +285,9 @@ constexpr int kRankMaxSeqs = 4096;
 // Tiles of every sequence (capped), staged in LDS once per ranking workgroup.
 __device__ __forceinline__ void stage_tiles(const DecodeParams& p, uint16_t* tiles) {
   for (int i = threadIdx.x; i < p.num_seqs; i += kThreads) {
-    const int c = clamp_ctx(p.context_lens[i], p.max_ctx);
+    int c = clamp_ctx(p.context_lens[i], p.max_ctx);
+    // the shared-prefix decode's own pass reads only the tokens past the prefix
+    if (p.seq_prefix != nullptr) c = max(c - p.seq_prefix[i], 0);
     tiles[i] = (uint16_t)min((c + kTile - 1) / kTile, kRankBuckets - 1);
   }
   __syncthreads();
@@ -1527,9 +1532,7 @@ static hipError_t launch_mfma_d(const DecodeParams& p, hipStream_t stream) {
   if (p.plan != nullptr)
     q.pair_span = cus;   // the plan holds the ranks: no limit from ranking in LDS
   else
-    q.pair_span = (p.num_partitions == 1 && p.seq_prefix == nullptr && p.num_seqs <= kRankMaxSeqs &&
-                   cus <= kRankMaxSeqs)
-                      ? cus : 0;
+    q.pair_span = (p.num_partitions == 1 && p.num_seqs <= kRankMaxSeqs && cus <= kRankMaxSeqs) ? cus : 0;
   const int64_t items = (int64_t)p.num_seqs * p.num_kv_heads;
   if (q.pair_span > 0 && items > q.pair_span && items <= 2 * (int64_t)q.pair_span)
     grid = dim3((unsigned)(2 * q.pair_span));   // a second workgroup on every unit

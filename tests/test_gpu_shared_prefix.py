@@ -74,3 +74,64 @@ def test_out_of_pool_block_in_the_prefix_poisons_the_group():
     assert np.isnan(got[4:]).all()
     assert_close(got[:4], oracle_decode(b, seqs=[0, 1, 2, 3], store=False), torch.bfloat16, "good group")
 
+
+
+def test_empty_contexts_give_zero_rows():
+    """A sequence with no token (a group of one, prefix 0) gives a zero row,
+    as the plain decode does; its neighbours are unaffected."""
+    b = W.random_decode_batch(2400, 12, 32, 8, 128, torch.bfloat16, max_ctx=250, min_ctx=1, store=False,
+                              share_group=4, shared_blocks=2)
+    b.pool.context_lens[9] = 0
+    starts = [0, 4, 8, 9, 10, 11, 12]
+    prefixes = [32, 32, 0, 0, 0, 0]
+    got = run_shared(b, starts, prefixes)
+    assert (got[9] == 0).all()
+    assert_close(got, oracle_decode(b, store=False), torch.bfloat16, "with an empty context")
+
+
+def test_repeated_calls_on_one_workspace_agree_exactly():
+    """The workspace carries nothing from one call to the next: repeated
+    calls give the same bits."""
+    b = W.random_decode_batch(2500, 48, 32, 8, 128, torch.bfloat16, max_ctx=900, min_ctx=0, store=False,
+                              share_group=8, shared_blocks=20)
+    dev = to_device(b)
+    starts = np.arange(0, 49, 8)
+    prefixes = [320] * 6
+    first = run_shared(b, starts, prefixes, dev)
+    assert_close(first, oracle_decode(b, store=False), torch.bfloat16, "first call")
+    for i in range(4):
+        assert np.array_equal(run_shared(b, starts, prefixes, dev), first), f"call {i + 2} differs"
+
+
+def test_graph_replays_match_eager():
+    """Both passes captured in one graph, replayed several times with eager
+    calls and synchronisation in between."""
+    b = W.random_decode_batch(2600, 24, 32, 8, 128, torch.bfloat16, max_ctx=600, min_ctx=0, store=False,
+                              share_group=6, shared_blocks=10)
+    dev = to_device(b)
+    starts = np.arange(0, 25, 6)
+    prefixes = [160] * 4
+    want = oracle_decode(b, store=False)
+    eager = run_shared(b, starts, prefixes, dev)
+    assert_close(eager, want, torch.bfloat16, "eager")
+    gs = torch.as_tensor(np.asarray(starts, np.int32), device="cuda")
+    gp = torch.as_tensor(np.asarray(prefixes, np.int32), device="cuda")
+    out = torch.zeros_like(dev["q"])
+    launch = pkv.SharedPrefixDecodeLaunch(out, dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
+                                          dev["context_lens"], gs, gp, b.scale, b.max_ctx, 6, 160)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        launch(s)                      # warm-up on the capture stream
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        launch(s)
+    torch.cuda.synchronize()
+    for i in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.float().cpu().double().numpy()
+        assert np.array_equal(got, eager), f"replay {i} differs from the eager call"
+        run_shared(b, starts, prefixes, dev)    # eager work between replays
