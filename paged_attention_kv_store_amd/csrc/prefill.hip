@@ -357,27 +357,36 @@ void prefill_kernel(PrefillParams p) {
       }
       const int keyq = kv0 + tb + 4 * qg;   // key of slot 0
       const bool full = kv0 + tb + 32 <= lim_wave;   // no key of the block is masked for this wave
-      // P of both tiles; a tile without a live row keeps zero weights, so
-      // the P.V steps below run for both tiles without a variant for one
-      // (its rows are never written). One instruction sequence for every
-      // wave also keeps the accumulators in place: a variant per tile count
-      // cost register copies on the common path.
-      bf16x8_t pa[2] = {bit_cast_to<bf16x8_t>(make_uint4(0, 0, 0, 0)), bit_cast_to<bf16x8_t>(make_uint4(0, 0, 0, 0))};
-      bool grow[2] = {false, false};          // the tile's reference max rises (wave-uniform)
-      float alpha[2];                         // and the factor of the lane's softmax row
+      // Scores of both tiles first, as four independent accumulation chains
+      // (tile, 16-key half): the K fragments are dead before any softmax
+      // starts, and the chains do not wait on each other. A tile without a
+      // live row has zero q, so its scores are computed and ignored.
+      // (Bit-identical to scoring and finishing one tile at a time, and 2-3%
+      // faster on the mixed prefill in interleaved A/B runs.)
+      f32x4_t sc[2][2];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        if (t == 1 && !live1) break;
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) sc[t][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            sc[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[h][s], qf[t][s], sc[t][h], 0, 0, 0);
+
+      // Softmax weights of tile t as the A operand of P.V; rescales tile t's
+      // sums and accumulators where its reference max rises, then adds its
+      // P.V and row sums. Tile 0's products are issued before tile 1's
+      // softmax, which needs none of their results.
+      auto tile_softmax_pv = [&](auto t_tag) {
+        constexpr int t = decltype(t_tag)::value;
         float x[8];   // raw scores q.k
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int s = 0; s < 4; ++s)
-            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[h][s], qf[t][s], sc, 0, 0, 0);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) x[4 * h + r] = sc[r];
-        }
+          for (int r = 0; r < 4; ++r) x[4 * h + r] = sc[t][h][r];
         if (!full) {
           const int lim = p.causal ? min(qpos[t] + 1, ctx) : ctx;   // visible keys < lim
 #pragma unroll
@@ -392,10 +401,16 @@ void prefill_kernel(PrefillParams p) {
         if (__any(lane_max * scale > m_ref[t] + kRescaleThreshold)) {
           const float mt = max_across_rows(lane_max) * scale;
           const float m_new = fmaxf(m_ref[t], mt);
-          alpha[t] = (m_new == neg_inf()) ? 1.f : fast_exp2(m_ref[t] - m_new);
+          const float alpha = (m_new == neg_inf()) ? 1.f : fast_exp2(m_ref[t] - m_new);
           m_ref[t] = m_new;
           nm_ref[t] = (m_new == neg_inf()) ? 0.f : -m_new;
-          grow[t] = true;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float a = __shfl(alpha, 4 * qg + r, 64);   // factor of row 4qg + r
+            lsum[t][r] *= a;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[t][i][r] *= a;
+          }
         }
         // weight 2^(scale*x - m): a masked score (-inf) gives exactly 0, since
         // scale > 0 and m is finite (0 while the row has seen no key)
@@ -404,30 +419,15 @@ void prefill_kernel(PrefillParams p) {
 #pragma unroll
         for (int h = 0; h < 4; ++h)
           pw[h] = pack_bf16x2(fast_exp2(fmaf(x[2 * h], scale, nm)), fast_exp2(fmaf(x[2 * h + 1], scale, nm)));
-        pa[t] = bit_cast_to<bf16x8_t>(make_uint4(pw[0], pw[1], pw[2], pw[3]));
-      }
-      // Rescale where the reference rose, once both tiles' scores are done
-      // (fewer registers live here than inside the softmax above).
+        const bf16x8_t pa = bit_cast_to<bf16x8_t>(make_uint4(pw[0], pw[1], pw[2], pw[3]));
+        lsum[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, ones, lsum[t], 0, 0, 0);
+        // O += P V (operands read at the top of the step)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        if (t == 1 && !live1) break;
-        if (grow[t]) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float a = __shfl(alpha[t], 4 * qg + r, 64);   // factor of row 4qg + r
-            lsum[t][r] *= a;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[t][i][r] *= a;
-          }
-        }
-        lsum[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[t], ones, lsum[t], 0, 0, 0);
-      }
-      // O += P V for both tiles (operands read at the top of the step)
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        acc[0][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[0], vb[c], acc[0][c], 0, 0, 0);
-        acc[1][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[1], vb[c], acc[1][c], 0, 0, 0);
-      }
+        for (int c = 0; c < 8; ++c)
+          acc[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb[c], acc[t][c], 0, 0, 0);
+      };
+      tile_softmax_pv(std::integral_constant<int, 0>{});
+      if (live1) tile_softmax_pv(std::integral_constant<int, 1>{});
     }
     wait_loads();
     if (FP8 && more) store8(buf ^ 1);
