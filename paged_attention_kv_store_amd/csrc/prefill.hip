@@ -51,6 +51,11 @@ constexpr int kMRows = 32 * kPW;      // M rows per workgroup
 constexpr int kKvTile = 64;           // keys per LDS tile
 constexpr int kRowPieces = kD * 2 / 16;   // 16-byte pieces per K/V row (16)
 constexpr int kXcds = 8;              // accelerator complex dies, each with its own L2
+// Raw byte-addressed buffer descriptors for the whole-tile gather: the
+// record count never limits a load (offsets stay below 16 pool rows), and
+// the last word is the plain-buffer configuration of this GPU family.
+constexpr int kBufferRecords = 0x7fffffff;
+constexpr int kBufferConfig = 0x00020000;
 
 // LDS position (in 16-byte units) of piece c of key row t in a tile: piece
 // c ^ sk(t) for K, c ^ sv(t) for V, where sk(t) = t mod 16 and sv(t) =
@@ -200,8 +205,40 @@ void prefill_kernel(PrefillParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) ids[i] = bt[min(kv0 + 16 * i, max(ctx - 1, 0)) >> lbs];
   };
+  // Within a tile the swizzle of row 16i + lrow depends only on lrow, so a
+  // lane's byte offset from the start of its block row is the same for every
+  // load of every whole tile (32 bits: 15 rows of a pool row plus 256 bytes).
+  const uint32_t koff_lane = (uint32_t)lrow * (uint32_t)row_bytes + ((lane & 15) ^ k_swizzle(lrow)) * 16;
+  const uint32_t voff_lane = (uint32_t)lrow * (uint32_t)row_bytes + ((lane & 15) ^ v_swizzle(lrow)) * 16;
   auto gather = [&](int kt, int buf, const int (&ids)[4]) {
     const int kv0 = kt * kKvTile;
+    if (kv0 + kKvTile <= ctx) {
+      // whole tile: each load's block row is workgroup-uniform, so its
+      // address is a scalar base plus the lane's constant offset
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int blk = __builtin_amdgcn_readfirstlane(ids[i]);
+        if ((unsigned)blk >= (unsigned)p.num_blocks) {
+          blk = 0;
+          bad = true;
+        }
+        // pool rows fit 32 bits (checked on the host)
+        const uint32_t row = ((uint32_t)blk << lbs) + (uint32_t)((kv0 + 16 * i) & (bs - 1));
+        const uint64_t off = (uint64_t)row * (uint64_t)(uint32_t)row_bytes;
+        const int lds_pos = (16 * i + 4 * w) * kRowPieces;
+        // buffer descriptors based at the block row: the lane's offset is
+        // the 32-bit vector offset, nothing is added per lane
+        const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<char*>(kbase + off), (short)0, kBufferRecords, kBufferConfig);
+        const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<char*>(vbase + off), (short)0, kBufferRecords, kBufferConfig);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            kr, (void __attribute__((address_space(3)))*)(&s_k[buf][lds_pos]), 16, koff_lane, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            vr, (void __attribute__((address_space(3)))*)(&s_v[buf][lds_pos]), 16, voff_lane, 0, 0, 0);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       int blk = ids[i];
