@@ -502,11 +502,15 @@ def mixed_prefill_fp8(seed: int = 4, device="cpu") -> PagedBatch:
 
 def random_prefill_batch(seed, num_chunks, num_q_heads, num_kv_heads, head_dim,
                          dtype, max_rows, max_prior, min_rows=1,
-                         block_size=BLOCK_SIZE, device="cpu", scale=None) -> PagedBatch:
-    """Small random prefill chunks (rows U{min..max}, prior U{0..max_prior})."""
+                         block_size=BLOCK_SIZE, device="cpu", scale=None, priors=None) -> PagedBatch:
+    """Small random prefill chunks (rows U{min..max}, prior U{0..max_prior},
+    or the given prior lengths)."""
     (rng,) = _streams(seed, 1)
     rows = rng.integers(min_rows, max_rows, size=num_chunks, endpoint=True).astype(np.int32)
     prior = rng.integers(0, max_prior, size=num_chunks, endpoint=True).astype(np.int32)
+    if priors is not None:
+        prior = np.asarray(priors, np.int32)
+        assert prior.shape == (num_chunks,)
     ctx = (rows + prior).astype(np.int32)
     pool = make_pool(rng, ctx, block_size=block_size, reserve=2)
     slots = np.concatenate(

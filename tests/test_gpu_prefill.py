@@ -116,6 +116,24 @@ def test_out_of_pool_block_poisons_its_chunk():
         assert_close(got[cu[c]:cu[c + 1]], want[cu[c]:cu[c + 1]], torch.bfloat16, f"chunk {c}")
 
 
+# prior lengths putting each chunk's last rows at every offset just past a
+# 16-key tile boundary (and past a 64-key round of the four waves): an early
+# row's causal limit then falls before the whole last tile
+TILE_EDGE_PRIORS = [0, 1, 13, 14, 15, 30, 31, 45, 46, 47, 61, 62, 63, 126, 127, 240]
+
+
+@pytest.mark.parametrize("case", [(16, 8, 3), (32, 8, 4), (64, 8, 2), (8, 8, 16), (8, 8, 5), (32, 8, 1)],
+                         ids=lambda c: f"{c[0]}x{c[1]}-L{c[2]}")
+def test_short_chunks_at_tile_edges(case):
+    """Rows of a short chunk whose causal limits end before the last key
+    tile (the chunk's rows times the group fill at most one matrix tile)."""
+    hq, hkv, rows = case
+    b = W.random_prefill_batch(700 + hq + rows, len(TILE_EDGE_PRIORS), hq, hkv, 128, torch.bfloat16,
+                               max_rows=rows, min_rows=rows, max_prior=0, priors=TILE_EDGE_PRIORS)
+    say(f"tile-edge short chunks {case} ctx={b.pool.context_lens.tolist()}")
+    assert_close(gpu_prefill(b), oracle_prefill(b), torch.bfloat16, f"L={rows}")
+
+
 SHORT = [
     # (hq, hkv, rows): verification of rows-1 drafted tokens, every GQA group
     (32, 8, 2), (32, 8, 4), (32, 8, 8), (16, 8, 3), (8, 8, 5), (32, 4, 7), (8, 1, 6),
