@@ -229,7 +229,9 @@ int pkv_decode_plan(void* plan, size_t plan_bytes, const int32_t* block_tables,
  *     pkv_decode_workspace_size(...) bytes (may be NULL when that is 0),
  *     256-byte aligned for PKV_PARTITION_BALANCED.
  *   algo: pkv_decode_algo. The MFMA kernel needs bf16 and
- *     num_q_heads / num_kv_heads <= 16.
+ *     num_q_heads / num_kv_heads <= 16; the VALU kernel takes groups up to
+ *     16 for fp32 and up to 8 for bf16 (PKV_DECODE_AUTO picks MFMA for bf16,
+ *     VALU for fp32, so every group up to 16 runs in the default mode).
  * Supported: head_dim in {64, 128}; block_size a multiple of 16 up to 256;
  * num_q_heads / num_kv_heads <= 16.
  */

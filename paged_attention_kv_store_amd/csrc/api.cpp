@@ -232,7 +232,10 @@ int decode_impl(const char* fn, void* out, const void* q, const void* k_cache, c
     if (dtype != PKV_BF16) return fail(PKV_EUNSUPPORTED, "%s: the MFMA kernel needs bf16", fn);
     if (group > 16) return fail(PKV_EUNSUPPORTED, "%s: GQA group %d > 16", fn, group);
   } else if (algo == PKV_DECODE_VALU) {
-    if (group > 8) return fail(PKV_EUNSUPPORTED, "%s: the VALU kernel supports GQA groups up to 8", fn);
+    const int max_group = dtype == PKV_F32 ? 16 : 8;   // per-head state in registers: 4 or 8 elements a lane
+    if (group > max_group)
+      return fail(PKV_EUNSUPPORTED, "%s: the VALU kernel supports GQA groups up to %d for this dtype", fn,
+                  max_group);
   } else {
     return fail(PKV_EINVAL, "%s: unknown algo %d", fn, algo);
   }

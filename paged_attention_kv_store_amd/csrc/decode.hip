@@ -20,7 +20,7 @@
 // Two kernel families compute the same thing:
 //  * decode_valu_kernel: lanes split a cache row into 16-byte pieces; q.k dot
 //    products are vector FMAs finished by xor-shuffle sums across the lanes of
-//    a row; P.V is vector FMAs. Any dtype, G <= 8.
+//    a row; P.V is vector FMAs. Any dtype; G <= 8 for bf16, G <= 16 for fp32.
 //  * decode_mfma_kernel (bf16): q.k for the 16 tile tokens x the G heads is a
 //    16x16x32 bf16 matrix-core product per 32 dims of head_dim (the G heads
 //    are padded to 16 columns); P.V is 16x16x16 bf16 matrix-core steps with
@@ -1513,6 +1513,20 @@ static hipError_t launch_valu_g(const DecodeParams& p, hipStream_t stream) {
     PKV_G(1) PKV_G(2) PKV_G(3) PKV_G(4) PKV_G(5) PKV_G(6) PKV_G(7) PKV_G(8)
 #undef PKV_G
     default:
+      // groups 9..16 for fp32 caches (bf16 ones use the MFMA kernel there);
+      // the per-head state of 16 heads fits the registers at 4 elements per
+      // lane, not at the 8 of bf16
+      if constexpr (sizeof(T) == 4) {
+        switch (p.group) {
+#define PKV_G(GV) \
+  case GV: hipLaunchKernelGGL((decode_valu_kernel<T, D, GV>), grid, dim3(kThreads), 0, stream, p); break;
+          PKV_G(9) PKV_G(10) PKV_G(11) PKV_G(12) PKV_G(13) PKV_G(14) PKV_G(15) PKV_G(16)
+#undef PKV_G
+          default:
+            return hipErrorInvalidValue;
+        }
+        break;
+      }
       return hipErrorInvalidValue;
   }
   return hipGetLastError();
