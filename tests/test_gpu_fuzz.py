@@ -221,3 +221,167 @@ def test_prefill_bf16_and_fp8(case):
                                           d8["v_scale"], bt8, cu8, cl8, b8.scale, mq8, b8.max_ctx, causal=causal)
     torch.cuda.synchronize()
     assert_close(out8.float().cpu().double().numpy(), want8, torch.bfloat16, f"fp8 causal={causal}")
+
+
+def _draw_fused(i):
+    dtype = [torch.float32, torch.bfloat16, "e4m3"][int(_rng.integers(0, 3))]
+    hkv = int(_rng.choice([1, 2, 4, 8]))
+    g = int(_rng.choice([1, 2, 3, 4, 8, 16]))
+    if dtype == "e4m3":
+        g = int(_rng.choice([1, 2, 4, 8]))
+    d = 64 if _rng.random() < 0.3 else 128
+    bs = int(_rng.choice([16, 32, 64, 128]))
+    s = int(_rng.integers(1, 90))
+    max_ctx = int(_rng.choice(_EDGE_CTX))
+    split = 16 * int(_rng.choice([1, 3, 8, 32]))
+    return (i, dtype, s, g * hkv, hkv, d, bs, max_ctx, split)
+
+
+FUSED = [_draw_fused(i) for i in range(14)]
+
+
+@pytest.mark.parametrize("case", FUSED, ids=_ids)
+def test_fused_store_and_decode_every_mode(case):
+    """One new row per sequence stored at position ctx-1 and used from
+    registers in the same launch: caches bit-exact, outputs within tolerance."""
+    i, dtype, s, hq, hkv, d, bs, max_ctx, split = case
+    e4m3 = dtype == "e4m3"
+    if e4m3:
+        b = W.random_decode_batch_fp8(9600 + i, s, hq, hkv, d, max_ctx=max_ctx, min_ctx=1, block_size=bs)
+        kc, vc = FP8.kv_cache_store_fp8(W.host_bits(b.k_new), W.host_bits(b.v_new), W.host_bits(b.k_cache),
+                                        W.host_bits(b.v_cache), W.host_bits(b.slot_mapping),
+                                        W.host_bits(b.k_scale), W.host_bits(b.v_scale), bs)
+        want = FP8.paged_attention_decode_fp8(W.host_bits(b.q), kc, vc, W.host_bits(b.k_scale),
+                                              W.host_bits(b.v_scale), b.pool.block_tables, b.pool.context_lens,
+                                              b.scale, bs)
+        tol_dtype = torch.bfloat16
+    else:
+        b = W.random_decode_batch(9700 + i, s, hq, hkv, d, dtype, max_ctx=max_ctx, min_ctx=1, block_size=bs)
+        kc, vc = oracle_caches(b)
+        want = oracle_decode(b, caches=(kc, vc))
+        tol_dtype = dtype
+    say(f"fuzz fused {case} ctx={b.pool.context_lens.tolist()[:12]}...")
+
+    def fused(partition):
+        def run():
+            dv = {k: getattr(b, k).to("cuda") for k in ("q", "k_cache", "v_cache", "k_new", "v_new",
+                                                        "slot_mapping")}
+            bt = torch.as_tensor(b.pool.block_tables, device="cuda")
+            cl = torch.as_tensor(b.pool.context_lens, device="cuda")
+            ws = None
+            if partition == "planned":
+                ws = pkv.new_decode_plan(s, "cuda")
+                pkv.decode_plan(ws, bt, cl, b.max_ctx, bs)
+            out = torch.full_like(dv["q"], float("nan"))
+            if e4m3:
+                pkv.paged_attention_decode_store_fp8(out, dv["q"], dv["k_cache"], dv["v_cache"],
+                                                     b.k_scale.to("cuda"), b.v_scale.to("cuda"), bt, cl,
+                                                     dv["k_new"], dv["v_new"], dv["slot_mapping"], b.scale,
+                                                     b.max_ctx, partition_size=partition, workspace=ws)
+            else:
+                pkv.paged_attention_decode_store(out, dv["q"], dv["k_cache"], dv["v_cache"], bt, cl, dv["k_new"],
+                                                 dv["v_new"], dv["slot_mapping"], b.scale, b.max_ctx,
+                                                 partition_size=partition, workspace=ws)
+            torch.cuda.synchronize()
+            assert W.host_bits(dv["k_cache"]).tobytes() == kc.tobytes(), "K cache differs from the oracle's store"
+            assert W.host_bits(dv["v_cache"]).tobytes() == vc.tobytes(), "V cache differs from the oracle's store"
+            return out.float().cpu().double().numpy()
+        return run
+
+    ran = []
+    for name, part in [("default", 0), (f"split {split}", split), ("planned", "planned"),
+                       ("balanced", "balanced")]:
+        got = _run(name, fused(part))
+        if got is None:
+            assert name != "default", "the default mode must support every shape drawn here"
+            continue
+        assert_close(got, want, tol_dtype, name)
+        ran.append(name)
+    say(f"  modes run: {ran}")
+
+
+def _draw_store(i):
+    dtype = [torch.float32, torch.bfloat16, "e4m3"][int(_rng.integers(0, 3))]
+    hkv = int(_rng.choice([1, 2, 3, 8]))
+    d = int(_rng.choice([32, 40, 64, 128, 256]))
+    bs = int(_rng.choice([1, 8, 16, 32, 256]))
+    nb = int(_rng.integers(1, 200))
+    t = int(_rng.integers(0, min(nb * bs, 3000) + 1))
+    pad = float(_rng.choice([0.0, 0.1, 0.5]))
+    return (i, dtype, hkv, d, bs, nb, t, pad)
+
+
+STORE = [_draw_store(i) for i in range(16)]
+
+
+@pytest.mark.parametrize("case", STORE, ids=_ids)
+def test_store_random_slots(case):
+    """Distinct random slots (a share of them -1, skipped) across the pool:
+    the caches match the oracle's store bit for bit, padding included."""
+    i, dtype, hkv, d, bs, nb, t, pad = case
+    rng = np.random.default_rng(9400 + i)
+    slots = rng.permutation(nb * bs)[:t].astype(np.int32)
+    slots[rng.random(t) < pad] = -1
+    gen = torch.Generator().manual_seed(9400 + i)
+    src = torch.float32 if dtype == torch.float32 else torch.bfloat16
+    k = torch.randn(t, hkv, d, generator=gen).to(src)
+    v = torch.randn(t, hkv, d, generator=gen).to(src)
+    say(f"fuzz store {case}")
+    if dtype == "e4m3":
+        kc0 = torch.randint(0, 256, (nb, bs, hkv, d), generator=gen, dtype=torch.uint8)
+        vc0 = torch.randint(0, 256, (nb, bs, hkv, d), generator=gen, dtype=torch.uint8)
+        ks = (torch.rand(hkv, generator=gen) * 0.1 + 0.01).float()
+        vs = (torch.rand(hkv, generator=gen) * 0.1 + 0.01).float()
+        kc, vc = kc0.cuda(), vc0.cuda()
+        pkv.kv_cache_store_fp8(k.cuda(), v.cuda(), kc, vc, torch.as_tensor(slots).cuda(), ks.cuda(), vs.cuda())
+        wk, wv = FP8.kv_cache_store_fp8(W.host_bits(k), W.host_bits(v), kc0.numpy(), vc0.numpy(), slots,
+                                        ks.numpy(), vs.numpy(), bs)
+    else:
+        kc0 = torch.randn(nb, bs, hkv, d, generator=gen).to(dtype)
+        vc0 = torch.randn(nb, bs, hkv, d, generator=gen).to(dtype)
+        kc, vc = kc0.cuda(), vc0.cuda()
+        pkv.kv_cache_store(k.cuda(), v.cuda(), kc, vc, torch.as_tensor(slots).cuda())
+        wk, wv = oracle.kv_cache_store(W.host_bits(k), W.host_bits(v), W.host_bits(kc0), W.host_bits(vc0), slots, bs)
+    torch.cuda.synchronize()
+    assert W.host_bits(kc.cpu()).tobytes() == np.asarray(wk).tobytes()
+    assert W.host_bits(vc.cpu()).tobytes() == np.asarray(wv).tobytes()
+
+
+def _draw_shared(i):
+    hkv = int(_rng.choice([1, 2, 4, 8]))
+    g = int(_rng.choice([1, 2, 4, 8]))
+    bs = int(_rng.choice([16, 32, 64]))
+    groups = int(_rng.integers(1, 9))
+    size = int(_rng.integers(1, 20))
+    shared = int(_rng.integers(0, 12))
+    max_ctx = shared * bs + int(_rng.choice([0, 1, 17, 300, 900]))
+    return (i, g * hkv, hkv, bs, groups, size, shared, max_ctx)
+
+
+SHARED = [_draw_shared(i) for i in range(10)]
+
+
+@pytest.mark.parametrize("case", SHARED, ids=_ids)
+def test_shared_prefix_random_groups(case):
+    """Groups of consecutive sequences sharing their first blocks; each group's
+    declared prefix is a random whole number of those blocks (possibly 0)."""
+    i, hq, hkv, bs, groups, size, shared, max_ctx = case
+    n = groups * size
+    b = W.random_decode_batch(9200 + i, n, hq, hkv, 128, torch.bfloat16, max_ctx=max(max_ctx, 1), min_ctx=0,
+                              block_size=bs, store=False, share_group=size, shared_blocks=shared)
+    rng = np.random.default_rng(9200 + i)
+    starts = np.arange(0, n + 1, size).astype(np.int32)
+    ctx = b.pool.context_lens
+    prefixes = []
+    for j in range(groups):
+        most = min(shared * bs, int(ctx[starts[j]:starts[j + 1]].min()))
+        prefixes.append(bs * int(rng.integers(0, most // bs + 1)))
+    say(f"fuzz shared {case} prefixes={prefixes} ctx={ctx.tolist()[:12]}...")
+    dv = to_device(b)
+    out = torch.full_like(dv["q"], float("nan"))
+    pkv.paged_attention_decode_shared_prefix(out, dv["q"], dv["k_cache"], dv["v_cache"], dv["block_tables"],
+                                             dv["context_lens"], torch.as_tensor(starts, device="cuda"),
+                                             torch.as_tensor(np.asarray(prefixes, np.int32), device="cuda"),
+                                             b.scale, b.max_ctx, size, max(prefixes))
+    torch.cuda.synchronize()
+    assert_close(out.float().cpu().double().numpy(), oracle_decode(b, store=False), torch.bfloat16, "shared")
