@@ -389,7 +389,7 @@ int pkv_paged_attention_decode_store_fp8(void* out, const void* q, void* k_cache
  *   workspace: pkv_decode_shared_prefix_workspace_size(...) bytes, 16-byte
  *   aligned: m, l [num_seqs, num_q_heads], o [num_seqs, num_q_heads,
  *   head_dim] fp32, then int32 [num_seqs]; scratch, no initial contents.
- * Supported: bf16, head_dim 128, GQA group in {1, 2, 4, 8}, block_size a
+ * Supported: bf16, head_dim 128, GQA group in {1, 2, 4, 8, 16}, block_size a
  * power of two in [16, 256], num_blocks * block_size < 2^32.
  */
 size_t pkv_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_q_heads,
@@ -421,7 +421,7 @@ int pkv_paged_attention_decode_shared_prefix(void* out, const void* q, const voi
  *   total_q: rows of q and out; max_q_len >= every L_c (sizes the grid);
  *   max_context_len >= every context_lens[c], <= max_blocks_per_seq * block_size.
  * Supported: bf16, head_dim 128, block_size a power of two in [16, 256],
- * num_q_heads / num_kv_heads in {1, 2, 4, 8}, num_blocks * block_size < 2^32
+ * num_q_heads / num_kv_heads in {1, 2, 4, 8, 16}, num_blocks * block_size < 2^32
  * (PKV_EUNSUPPORTED otherwise).
  */
 int pkv_paged_attention_prefill_chunk(void* out, const void* q, const void* k_cache,

@@ -508,8 +508,8 @@ static int prefill_impl(const char* fn, void* out, const void* q, const void* k_
   if (dtype != PKV_BF16)
     return fail(PKV_EUNSUPPORTED, fp8 ? "%s: q and out must be bf16" : "%s: prefill supports bf16 only", fn);
   if (head_dim != 128) return fail(PKV_EUNSUPPORTED, "%s: prefill supports head_dim 128 only", fn);
-  if (group != 1 && group != 2 && group != 4 && group != 8)
-    return fail(PKV_EUNSUPPORTED, "%s: GQA group %d not in {1, 2, 4, 8}", fn, group);
+  if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16)
+    return fail(PKV_EUNSUPPORTED, "%s: GQA group %d not in {1, 2, 4, 8, 16}", fn, group);
   if (block_size < 16 || block_size > 256 || (block_size & (block_size - 1)) != 0)
     return fail(PKV_EUNSUPPORTED, "%s: block_size %d must be a power of two in [16, 256]", fn, block_size);
   if ((int64_t)block_size * num_kv_heads * head_dim * (fp8 ? 1 : 2) >= ((int64_t)1 << 31))
@@ -617,8 +617,8 @@ extern "C" int pkv_paged_attention_decode_shared_prefix(
                 num_q_heads, num_kv_heads);
   const int group = num_q_heads / num_kv_heads;
   if (head_dim != 128) return fail(PKV_EUNSUPPORTED, "%s: head_dim 128 only", fn);
-  if (group != 1 && group != 2 && group != 4 && group != 8)
-    return fail(PKV_EUNSUPPORTED, "%s: GQA group %d not in {1, 2, 4, 8}", fn, group);
+  if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16)
+    return fail(PKV_EUNSUPPORTED, "%s: GQA group %d not in {1, 2, 4, 8, 16}", fn, group);
   if (block_size < 16 || block_size > 256 || (block_size & (block_size - 1)) != 0)
     return fail(PKV_EUNSUPPORTED, "%s: block_size %d must be a power of two in [16, 256]", fn, block_size);
   if ((int64_t)block_size * num_kv_heads * head_dim * 2 >= ((int64_t)1 << 31))

@@ -539,6 +539,7 @@ static hipError_t launch_prefill_t(const PrefillParams& p, int head_dim, hipStre
     case 2: hipLaunchKernelGGL((prefill_kernel<2, FP8>), grid, dim3(kPThreads), 0, stream, q); break;
     case 4: hipLaunchKernelGGL((prefill_kernel<4, FP8>), grid, dim3(kPThreads), 0, stream, q); break;
     case 8: hipLaunchKernelGGL((prefill_kernel<8, FP8>), grid, dim3(kPThreads), 0, stream, q); break;
+    case 16: hipLaunchKernelGGL((prefill_kernel<16, FP8>), grid, dim3(kPThreads), 0, stream, q); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

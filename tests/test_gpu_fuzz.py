@@ -62,7 +62,7 @@ FP8_DECODE = [_draw_fp8(i) for i in range(10)]
 
 def _draw_prefill(i):
     hkv = int(_rng.choice([1, 2, 4, 8]))
-    g = int(_rng.choice([1, 2, 4, 8]))
+    g = int(_rng.choice([1, 2, 4, 8, 16]))
     bs = int(_rng.choice([16, 32, 64, 128, 256]))
     chunks = int(_rng.integers(1, 9))
     max_rows = int(_rng.choice([1, 2, 4, 7, 33, 130, 300]))
@@ -349,7 +349,7 @@ def test_store_random_slots(case):
 
 def _draw_shared(i):
     hkv = int(_rng.choice([1, 2, 4, 8]))
-    g = int(_rng.choice([1, 2, 4, 8]))
+    g = int(_rng.choice([1, 2, 4, 8, 16]))
     bs = int(_rng.choice([16, 32, 64]))
     groups = int(_rng.integers(1, 9))
     size = int(_rng.integers(1, 20))

@@ -38,6 +38,7 @@ def oracle_prefill(b, caches=None, causal=True, rows=None):
 
 CASES = [
     # (hq, hkv, chunks, max_rows, max_prior)
+    (128, 8, 3, 70, 300),      # G = 16: 8 query rows per workgroup
     (32, 8, 3, 150, 300),
     (16, 8, 4, 70, 90),
     (8, 8, 2, 200, 20),
