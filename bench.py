@@ -566,17 +566,21 @@ def secondary(device, steps, warmup, algo, bf16_step_ms, partition=0, base=None)
     dec = pkv.DecodeLaunch(torch.empty_like(b.q), b.q, b.k_cache, b.v_cache, bt, cl, b.scale,
                            b.max_ctx, partition_size="auto", algo=algo)
     ms = time_region(dec, steps, warmup)
-    dec512 = pkv.DecodeLaunch(torch.empty_like(b.q), b.q, b.k_cache, b.v_cache, bt, cl, b.scale,
-                              b.max_ctx, partition_size=512, algo=algo)
-    ms512 = time_region(dec512, steps, warmup)
+    split_ms = {}
+    for part in (512, 1024, 2048):
+        d = pkv.DecodeLaunch(torch.empty_like(b.q), b.q, b.k_cache, b.v_cache, bt, cl, b.scale,
+                             b.max_ctx, partition_size=part, algo=algo)
+        split_ms[str(part)] = time_region(d, steps, warmup)
+        del d
     by = decode_bytes(b)
     res["long_splitk"] = {"ms": ms, "GBps": by / ms / 1e6, "pct_hbm_peak": 100 * by / ms / 1e6 / HBM_PEAK_GBS,
                           "tokens_per_s": b.num_seqs / (ms * 1e-3), "partition": "auto",
-                          "auto_partition_size": auto_part, "splitk_512_ms": ms512,
+                          "auto_choice": "balanced" if auto_part == pkv.PARTITION_BALANCED else auto_part,
+                          "splitk_ms": split_ms,
                           "balanced_ms": balanced_ms(b, bt, cl, steps, warmup),
                           "planned_ms": planned_ms(b, bt, cl, steps, warmup)}
     baseline_decode(base, "long_splitk", b)
-    del dec, dec512, b
+    del dec, b
     wl = W.mixed(device=device)
     pre, db = wl.prefill, wl.batches[0]
     store = pkv.StoreLaunch(pre.k_new, pre.v_new, pre.k_cache, pre.v_cache, pre.slot_mapping)
@@ -787,8 +791,12 @@ def pmc_pass(device, layers, partition):
     for _ in range(3):
         dec()
     torch.cuda.synchronize()
-    seg("long_splitk_auto", 3, 1, decode_bytes(b), f"decode_mfma_kernel, split-K at {part} tokens (auto), merged "
-        "in the same launch", extra=split_partial_bytes(b, part))
+    if part == pkv.PARTITION_BALANCED:
+        seg("long_splitk_auto", 3, 1, decode_bytes(b), "decode_balanced_kernel (auto's choice): equal tile shares "
+            "per wave, split items merged in the same launch (their pieces not counted as extra)")
+    else:
+        seg("long_splitk_auto", 3, 1, decode_bytes(b), f"decode_mfma_kernel, split-K at {part} tokens (auto), "
+            "merged in the same launch", extra=split_partial_bytes(b, part))
     del b, bt, cl, dec
     torch.cuda.empty_cache()
 

@@ -124,8 +124,8 @@ int pkv_kv_cache_store(const void* k, const void* v, void* k_cache, void* v_cach
  *    start whatever the sizes), then fp32 pieces of the partial results, two
  *    per wave of the largest grid (4096 waves).
  *  - PKV_PARTITION_PLANNED: pkv_decode_plan_size(num_seqs) (the plan).
- *  - PKV_PARTITION_AUTO: that of the partition size it stands for
- *    (pkv_decode_auto_partition).
+ *  - PKV_PARTITION_AUTO: the larger of those of the choices it stands for
+ *    (pkv_decode_auto_partition, and its split-K fallback).
  *  - 0 (single pass): 0.
  * The arrival counters must be zero before a workspace's first split-K or
  * work-balanced call: pkv_decode_workspace_init clears them.
@@ -148,12 +148,17 @@ int pkv_decode_workspace_init(void* workspace, size_t workspace_bytes, void* str
 
 /*
  * The partition_size that PKV_PARTITION_AUTO resolves to on the current
- * device, from host-side sizes only: 0 (one pass) when the num_seqs *
- * num_kv_heads items give every compute unit two workgroups or
- * max_context_len <= 2048; otherwise split-K with 1024-token partitions,
- * halved (down to 256) while ceil(max_context_len / partition) partitions of
- * every item would still leave compute units without two workgroups. 0 for
- * invalid sizes.
+ * device, from host-side sizes only (C = the device's compute units, items =
+ * num_seqs * num_kv_heads):
+ *  - 0 (one pass) when items >= 2C or max_context_len <= 2048;
+ *  - PKV_PARTITION_BALANCED when 2 * items >= C (and the work-balanced
+ *    limits hold: at most 8192 sequences, fewer than 2^30 tiles). A call the
+ *    work-balanced decode does not take (fp32 caches or the VALU kernel,
+ *    E4M3 caches) splits instead, at the size of the next rule;
+ *  - otherwise split-K at the power of two in [512, 2048] nearest above
+ *    items * max_context_len / C tokens (about one partition per compute
+ *    unit), or 0 when one partition holds max_context_len.
+ * 0 for invalid sizes.
  */
 int32_t pkv_decode_auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len);
 
@@ -223,8 +228,8 @@ int pkv_decode_plan(void* plan, size_t plan_bytes, const int32_t* block_tables,
  *     num_seqs, context_lens and block_tables (workspace_bytes >=
  *     pkv_decode_plan_size(num_seqs)). The results are those of
  *     partition_size 0.
- *     PKV_PARTITION_AUTO: the partition size pkv_decode_auto_partition
- *     returns for these sizes (one pass or split-K), with its workspace.
+ *     PKV_PARTITION_AUTO: the choice pkv_decode_auto_partition returns for
+ *     these sizes (one pass, work-balanced or split-K), with its workspace.
  *   workspace / workspace_bytes: device buffer of at least
  *     pkv_decode_workspace_size(...) bytes (may be NULL when that is 0),
  *     256-byte aligned for PKV_PARTITION_BALANCED.

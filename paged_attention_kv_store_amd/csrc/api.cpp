@@ -56,13 +56,34 @@ void partitioning(int32_t max_ctx, int32_t partition_size, int32_t* part, int64_
 // Measured on one MI355X: 256 items of up to 32K tokens take 384 us in one
 // pass and 213 us with 1024- or 2048-token partitions; 1024 and 2048 items of
 // up to 4K tokens are fastest in one pass (split-K at 2048 tokens adds 12-14%).
+// The split-K partition for a batch too small to fill the GPU in one pass:
+// about one partition per compute unit, as a power of two within
+// [512, 2048] tokens (fewer, longer partitions leave fewer partials to
+// merge; shorter ones leave compute units idle). 0 when one partition holds
+// the longest context.
+int32_t auto_split(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ctx) {
+  const int64_t items = (int64_t)num_seqs * num_kv_heads;
+  const int64_t per_unit = ceil_div(items * max_ctx, (int64_t)pkv::device_compute_units());
+  int32_t part = 512;
+  while (part < 2048 && part < per_unit) part *= 2;
+  return ceil_div(max_ctx, part) > 1 ? part : 0;
+}
+
+// PKV_PARTITION_AUTO (measured on full-size batches of 1 to 64 sequences of
+// up to 32K tokens, uniform, log-uniform and equal lengths): one pass when
+// the items give every compute unit two workgroups or contexts are short;
+// the work-balanced decode for mid-sized batches (from half a workgroup per
+// compute unit), whose equal shares absorb the spread of lengths that the
+// host cannot see; split-K (auto_split) for the smallest batches, where the
+// work-balanced decode would split each item between too many waves.
 int32_t auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ctx) {
   const int64_t items = (int64_t)num_seqs * num_kv_heads;
-  const int64_t slots = 2 * (int64_t)pkv::device_compute_units();
-  if (items >= slots || max_ctx <= 2048 || items > pkv::kSplitMaxItems) return 0;
-  int32_t part = 1024;
-  while (part > 256 && items * ceil_div(max_ctx, part) < slots) part /= 2;
-  return ceil_div(max_ctx, part) > 1 ? part : 0;
+  const int64_t cus = pkv::device_compute_units();
+  if (items >= 2 * cus || max_ctx <= 2048 || items > pkv::kSplitMaxItems) return 0;
+  if (2 * items >= cus && num_seqs <= pkv::kBalMaxSeqs &&
+      items * ceil_div(max_ctx, 16) < ((int64_t)1 << 30))
+    return PKV_PARTITION_BALANCED;
+  return auto_split(num_seqs, num_kv_heads, max_ctx);
 }
 
 int check_common(const char* fn, int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
@@ -150,7 +171,16 @@ extern "C" size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_head
   if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_context_len < 0 ||
       num_q_heads % num_kv_heads != 0)
     return 0;
-  if (partition_size == PKV_PARTITION_AUTO) partition_size = auto_partition(num_seqs, num_kv_heads, max_context_len);
+  if (partition_size == PKV_PARTITION_AUTO) {
+    // a work-balanced choice falls back to split-K for calls the
+    // work-balanced decode does not take (fp32, E4M3): room for either
+    const int32_t a = auto_partition(num_seqs, num_kv_heads, max_context_len);
+    const size_t wa = pkv_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, a);
+    if (a != PKV_PARTITION_BALANCED) return wa;
+    const size_t ws = pkv_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                                                auto_split(num_seqs, num_kv_heads, max_context_len));
+    return wa > ws ? wa : ws;
+  }
   if (partition_size == PKV_PARTITION_BALANCED) {
     // one arrival counter per wave, then two pieces per wave, for the largest grid
     const int64_t stride = pkv::bal_piece_stride(num_q_heads / num_kv_heads, head_dim);
@@ -213,7 +243,12 @@ int decode_impl(const char* fn, void* out, const void* q, const void* k_cache, c
   if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
     return fail(PKV_EINVAL, "%s: max_context_len %d outside [0, max_blocks_per_seq * block_size = %lld]", fn,
                 max_context_len, (long long)max_blocks_per_seq * block_size);
-  if (partition_size == PKV_PARTITION_AUTO) partition_size = auto_partition(num_seqs, num_kv_heads, max_context_len);
+  if (partition_size == PKV_PARTITION_AUTO) {
+    partition_size = auto_partition(num_seqs, num_kv_heads, max_context_len);
+    const bool mfma = algo == PKV_DECODE_MFMA || (algo == PKV_DECODE_AUTO && dtype == PKV_BF16);
+    if (partition_size == PKV_PARTITION_BALANCED && (fp8 || !mfma || dtype != PKV_BF16))
+      partition_size = auto_split(num_seqs, num_kv_heads, max_context_len);
+  }
   const bool balanced = partition_size == PKV_PARTITION_BALANCED;
   const bool planned = partition_size == PKV_PARTITION_PLANNED;
   if (!balanced && !planned && (partition_size < 0 || partition_size % 16 != 0))

@@ -309,32 +309,46 @@ def test_static_decode_empty_batch_is_a_no_op():
 @needs_lib
 def test_auto_partition_rule():
     """PKV_PARTITION_AUTO: one pass when the items fill two workgroups per
-    compute unit or contexts are short; else split-K at 1024 tokens, halved
-    while the longest context's partitions cannot fill the units. (Without a
-    GPU the library assumes 256 compute units.)"""
+    compute unit or contexts are short; the work-balanced decode from half a
+    workgroup per unit; below that split-K at the power of two in [512, 2048]
+    nearest above one partition per unit. (Without a GPU the library assumes
+    256 compute units.)"""
     cus = 256
     auto = pkv.decode_auto_partition
+    bal = binding.PARTITION_BALANCED
     assert auto(60, 8, 1024) == 0                 # short contexts
     assert auto(256, 8, 4096) == 0                # 2048 items
     assert auto(64, 8, 32768) == 0                # 512 items = 2 per unit
-    assert auto(32, 8, 32768) == 1024             # 256 items, 32 partitions each
-    assert auto(1, 8, 4096) == 256                # 8 items: 1024 -> 512 -> 256
-    assert auto(1, 1, 3000) == 256                # the floor, even if the units stay idle
-    assert auto(4, 8, 8192) == 512                # 32 items x 8 partitions = 256 < 512 -> halve once
-    # (the three lines above depend on the unit count; recompute the rule here)
-    for s, hkv, ctx in [(32, 8, 32768), (1, 8, 4096), (4, 8, 8192), (2, 4, 2100), (100, 2, 5000)]:
-        items, slots = s * hkv, 2 * cus
-        want = 0
-        if items < slots and ctx > 2048:
-            part = 1024
-            while part > 256 and items * -(-ctx // part) < slots:
-                part //= 2
+    assert auto(32, 8, 32768) == bal              # 256 items: one per unit
+    assert auto(16, 8, 8192) == bal               # 128 items: half a workgroup per unit
+    assert auto(8, 8, 8192) == 2048               # 64 items x 8192 / 256 units = 2048 tokens
+    assert auto(1, 8, 32768) == 1024              # 8 x 32768 / 256
+    assert auto(1, 8, 4096) == 512                # the floor
+    assert auto(1, 1, 3000) == 512
+    assert auto(2, 8, 32768) == 2048              # 16 x 32768 / 256 = 2048
+    assert auto(4, 8, 32768) == 2048              # the ceiling (4096 would be one per unit)
+    # (recompute the rule here for more sizes)
+    for s, hkv, ctx in [(32, 8, 32768), (1, 8, 4096), (4, 8, 8192), (2, 4, 2100), (100, 2, 5000),
+                        (15, 8, 9000), (17, 8, 3000), (3, 2, 40000)]:
+        items = s * hkv
+        if items >= 2 * cus or ctx <= 2048:
+            want = 0
+        elif 2 * items >= cus:
+            want = bal
+        else:
+            part = 512
+            while part < 2048 and part < -(-items * ctx // cus):
+                part *= 2
             want = part if -(-ctx // part) > 1 else 0
         assert auto(s, hkv, ctx) == want, (s, hkv, ctx)
     assert pkv.lib().pkv_decode_auto_partition(0, 8, 100) == 0
-    # the workspace of "auto" is that of the partition size it resolves to
-    assert pkv.decode_workspace_size(32, 32, 8, 128, 32768, "auto") == \
-        pkv.decode_workspace_size(32, 32, 8, 128, 32768, 1024)
+    # the workspace of "auto" covers the choice and, for a work-balanced
+    # choice, the split-K fallback of calls that cannot take it
+    assert pkv.decode_workspace_size(8, 32, 8, 128, 8192, "auto") == \
+        pkv.decode_workspace_size(8, 32, 8, 128, 8192, 2048)
+    both = max(pkv.decode_workspace_size(32, 32, 8, 128, 32768, "balanced"),
+               pkv.decode_workspace_size(32, 32, 8, 128, 32768, 2048))
+    assert pkv.decode_workspace_size(32, 32, 8, 128, 32768, "auto") == both
     assert pkv.decode_workspace_size(60, 16, 8, 128, 1024, "auto") == 0
 
 

@@ -162,13 +162,31 @@ def test_workspace_init_and_decode_in_a_graph():
         assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {r}"
 
 
-def test_auto_picks_split_k_for_few_long_sequences():
+def test_auto_choices_on_this_device():
+    """On the MI355X (256 compute units): the long-context batch (256 items)
+    takes the work-balanced decode, a few sequences split-K, large or short
+    batches one pass."""
     b = W.long_splitk().batches[0]
     part = pkv.decode_auto_partition(b.num_seqs, b.num_kv_heads, b.max_ctx)
     say(f"auto partition for 32 seqs x 8 kv-heads up to {b.max_ctx} tokens: {part}")
-    assert part == 1024
+    assert part == pkv.PARTITION_BALANCED
+    assert pkv.decode_auto_partition(2, 8, 32768) == 2048
     assert pkv.decode_auto_partition(60, 8, 1024) == 0
     assert pkv.decode_auto_partition(256, 8, 4096) == 0
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_auto_work_balanced_choice_and_its_fallback(dtype):
+    """A mid-sized batch of long contexts: bf16 runs the work-balanced decode,
+    fp32 (vector kernel) the split-K fallback, both in auto's workspace."""
+    b = W.random_decode_batch(5450, 20, 32, 8, 128, dtype, max_ctx=6000, min_ctx=0, store=False)
+    assert pkv.decode_auto_partition(b.num_seqs, b.num_kv_heads, b.max_ctx) == pkv.PARTITION_BALANCED
+    dev = to_device(b)
+    out = torch.full_like(dev["q"], float("nan"))
+    pkv.paged_attention_decode(out, dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
+                               dev["context_lens"], b.scale, b.max_ctx, partition_size="auto")
+    torch.cuda.synchronize()
+    assert_close(out.float().cpu().double().numpy(), oracle_decode(b, store=False), dtype, f"auto {dtype}")
 
 
 @pytest.mark.parametrize("algo,dtype", [("valu", torch.float32), ("mfma", torch.bfloat16)])
