@@ -912,7 +912,7 @@ def summarize_prefill_pmc(counter_csv, trace_csv, out_md, command):
         f"| LDS bank-conflict cycles | {mean['SQ_LDS_BANK_CONFLICT']:.4g} |",
         f"| GRBM_GUI_ACTIVE | {mean['GRBM_GUI_ACTIVE']:.4g} |", "",
         "The busy fraction counts the row-sum MFMA (P times a ones column) too, which the useful",
-        "FLOPs leave out: two of every 26 MFMAs of a full 32-key step. Under this load the engine",
+        "FLOPs leave out: two of every 34 MFMAs of a full 32-key step. Under this load the engine",
         "runs below its 2.4 GHz peak clock, so the fraction of the cycles it actually ran is the",
         "higher of the two busy figures; the useful rate is against the 2.4 GHz vendor peak.",
     ]
