@@ -9,7 +9,9 @@
 // G q-heads that share the kv-head are packed with the query rows into the
 // matrix rows ("M rows": m = query_row * G + head), so a workgroup covers
 // 128 M rows = 128/G query rows and each K/V byte staged in LDS serves all G
-// heads. Wave w owns M rows 32w .. 32w+31 as two 16-row tiles.
+// heads. Wave w owns two 16-row tiles of M rows: tile t holds rows
+// 16(w + 4t) .. 16(w + 4t) + 15, so the rows of a short chunk (a few query
+// rows) spread over the waves instead of filling the first wave's tiles.
 //
 // The keys are walked in 64-token tiles gathered through the block table
 // straight into LDS with direct-to-LDS loads (double-buffered: the next
@@ -160,13 +162,13 @@ void prefill_kernel(PrefillParams p) {
   const uint32_t qsign = eff < 0.f ? 0x80008000u : 0u;
 
   // ---- the wave's Q rows (B operand of S^T = K Q^T) ----------------------
-  // tile t, lane l: M row mr = 32w + 16t + l%16 (query row r0 + mr/G, head
+  // tile t, lane l: M row mr = 16(w + 4t) + l%16 (query row r0 + mr/G, head
   // mr%G); step s holds head_dim elements [32s + 8qg, 32s + 8qg + 8).
   bf16x8_t qf[2][4];
   int qpos[2];          // absolute position of the lane's softmax row
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const int mr = 32 * w + 16 * t + n;
+    const int mr = 16 * (w + kPW * t) + n;
     const int qi = r0 + mr / G;
     qpos[t] = P0 + qi;
     const bool live = qi < L;
@@ -303,8 +305,8 @@ void prefill_kernel(PrefillParams p) {
 
   float m_ref[2] = {neg_inf(), neg_inf()};   // per softmax row (lane's n), scaled units
   float nm_ref[2] = {0.f, 0.f};               // -m_ref, or 0 while the row has seen no key
-  f32x4_t acc[2][8];                          // acc[t][c][r] = O[row 16t + 4qg + r][16c + n]
-  f32x4_t lsum[2];                            // lsum[t][r]   = sum of P over row 16t + 4qg + r
+  f32x4_t acc[2][8];                          // acc[t][c][r] = O[row 4qg + r of tile t][16c + n]
+  f32x4_t lsum[2];                            // lsum[t][r]   = sum of P over row 4qg + r of tile t
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     lsum[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -314,13 +316,13 @@ void prefill_kernel(PrefillParams p) {
   // bf16 ones: P times a ones column gives the row sums of the rounded weights
   bf16x8_t ones = bit_cast_to<bf16x8_t>(make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
   // keys below this bound are visible to every row of the wave
-  const int lim_wave = p.causal ? min(P0 + r0 + (32 * w) / G + 1, ctx) : ctx;
+  const int lim_wave = p.causal ? min(P0 + r0 + (16 * w) / G + 1, ctx) : ctx;
   // Whether M-row tile t of the wave holds a live query row (wave-uniform).
   // Short chunks (a few query rows, as in verifying drafted tokens) leave
   // most tiles empty; their matrix work is skipped, while the wave still
   // takes its share of the cooperative gather and every barrier.
-  const bool live0 = r0 + (32 * w) / G < L;
-  const bool live1 = r0 + (32 * w + 16) / G < L;
+  const bool live0 = r0 + (16 * w) / G < L;
+  const bool live1 = r0 + (16 * (w + kPW)) / G < L;
 
   // byte offset, within key row kb + n / 4 of a V tile, of the 8-byte piece
   // lane n reads for column block c: columns 16c + 4(n % 4), i.e. half n % 2
@@ -482,7 +484,7 @@ void prefill_kernel(PrefillParams p) {
   const bool poisoned = s_bad != 0;
   const float vsc = FP8 ? p.v_scale[g] : 1.f;   // E4M3: the kv-head's V scale
   if (p.part_m != nullptr) {
-    // partials for a later merge: row 16t + 4qg + r's reference max sits in
+    // partials for a later merge: row 4qg + r of tile t has its reference max in
     // the lane whose n is 4qg + r; sums are replicated over n
     if (g == 0 && qt == 0 && w == 0)
       for (int i = lane; i < L; i += 64) p.seq_prefix[q_start + i] = ctx;
@@ -491,7 +493,7 @@ void prefill_kernel(PrefillParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float m = __shfl(m_ref[t], 4 * qg + r, 64);
-        const int mr = 32 * w + 16 * t + 4 * qg + r;
+        const int mr = 16 * (w + kPW * t) + 4 * qg + r;
         const int qi = r0 + mr / G;
         if (qi >= L) continue;
         const int64_t row = (int64_t)(q_start + qi) * p.num_q_heads + g * G + mr % G;
@@ -510,7 +512,7 @@ void prefill_kernel(PrefillParams p) {
   for (int t = 0; t < 2; ++t) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int mr = 32 * w + 16 * t + 4 * qg + r;
+      const int mr = 16 * (w + kPW * t) + 4 * qg + r;
       const int qi = r0 + mr / G;
       if (qi >= L) continue;
       const float inv = poisoned ? __builtin_nanf("") : vsc / lsum[t][r];
