@@ -265,3 +265,46 @@ def test_prefill_fp8_out_of_pool_block_poisons_its_chunk():
     for c in (0, 2):
         assert_close(got[cu[c]:cu[c + 1]], want[cu[c]:cu[c + 1]], torch.bfloat16, f"chunk {c}")
 
+
+
+def test_store_and_prefill_fp8_graph_replays_match_eager():
+    """The quantising store and the E4M3 prefill captured in one HIP graph:
+    four replays (output reset to NaN, eager work in between) give the eager
+    call's bits, which match the oracle."""
+    b = W.random_prefill_batch_fp8(613, 4, 32, 8, 128, max_rows=150, max_prior=400)
+    say(f"graph prefill fp8 rows={np.diff(b.cu_seqlens_q).tolist()} ctx={b.pool.context_lens.tolist()}")
+    d = _dev(b)
+    out = torch.full_like(d["q"], float("nan"))
+    cu = torch.as_tensor(b.cu_seqlens_q, device="cuda")
+    store = pkv.StoreFp8Launch(d["k_new"], d["v_new"], d["k_cache"], d["v_cache"], d["slot_mapping"],
+                               d["k_scale"], d["v_scale"])
+    pre = pkv.PrefillFp8Launch(out, d["q"], d["k_cache"], d["v_cache"], d["k_scale"], d["v_scale"],
+                               d["block_tables"], cu, d["context_lens"], b.scale,
+                               int(np.diff(b.cu_seqlens_q).max()), b.max_ctx, causal=True)
+
+    def step():
+        store()
+        pre()
+
+    step()
+    torch.cuda.synchronize()
+    want = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    scratch = torch.zeros(1 << 20, device="cuda")
+    for i in range(4):
+        out.fill_(float("nan"))
+        scratch.add_(1.0)   # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), want.view(torch.int16)), f"replay {i}"
+    assert_close(want.float().cpu().double().numpy(), _oracle_prefill(b, _oracle_caches(b)), torch.bfloat16,
+                 "graph prefill fp8")

@@ -170,3 +170,49 @@ def test_short_chunks_match_decode_over_each_prefix(case):
     assert_close(got, want, torch.bfloat16, "chunk vs per-row decode oracle")
     assert cu[-1] == len(row_ctx)
 
+
+
+def _replays_match(step, out, label):
+    """Runs `step` eagerly, warms it on a side stream, captures it in a HIP
+    graph and replays it four times (output reset to NaN and other eager
+    work on the stream in between): every replay must give the eager bits."""
+    step()
+    torch.cuda.synchronize()
+    want = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    scratch = torch.zeros(1 << 20, device="cuda")
+    for i in range(4):
+        out.fill_(float("nan"))
+        scratch.add_(1.0)   # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), want.view(torch.int16)), f"{label}: replay {i}"
+    return want
+
+
+def test_store_and_prefill_graph_replays_match_eager():
+    """The store of the chunks' rows and the prefill over them in one graph."""
+    b = W.random_prefill_batch(611, 4, 32, 8, 128, torch.bfloat16, max_rows=150, max_prior=400)
+    say(f"graph prefill rows={np.diff(b.cu_seqlens_q).tolist()} ctx={b.pool.context_lens.tolist()}")
+    dev = to_device(b)
+    out = torch.full_like(dev["q"], float("nan"))
+    store = pkv.StoreLaunch(dev["k_new"], dev["v_new"], dev["k_cache"], dev["v_cache"], dev["slot_mapping"])
+    pre = pkv.PrefillLaunch(out, dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
+                            dev["cu_seqlens_q"], dev["context_lens"], b.scale,
+                            int(np.diff(b.cu_seqlens_q).max()), b.max_ctx, causal=True)
+
+    def step():
+        store()
+        pre()
+
+    want = _replays_match(step, out, "bf16 prefill")
+    assert_close(want.float().cpu().double().numpy(), oracle_prefill(b), torch.bfloat16, "graph prefill")
