@@ -214,6 +214,10 @@ def probe_lib():
         _probe.pkv_probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int32,
                                               ctypes.c_void_p, ctypes.c_void_p]
         _probe.pkv_probe_hbm_read.restype = ctypes.c_int
+        _probe.pkv_probe_paged_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                                ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                                ctypes.c_void_p]
+        _probe.pkv_probe_paged_read.restype = ctypes.c_int
     return _probe
 
 
@@ -258,6 +262,49 @@ def read_ceiling(device, layer_bytes, layers, fp8_layer_bytes=None):
         nb8, best8 = per_layer(fp8_layer_bytes)
         out.update({"GBps_fp8_layer_bytes": round(nb8 / (best8 * 1e-3) / 1e9, 1),
                     "fp8_layer_bytes_us": round(best8 * 1e3, 2), "fp8_layer_bytes": nb8})
+    return out
+
+
+def paged_tile_offsets(b, slice_bytes, device):
+    """Byte offset of the first row slice of every 16-token tile of a decode
+    layer, kv-head first, then sequence, then tile: the tiles the decode reads,
+    for rows of num_kv_heads slices of `slice_bytes` each."""
+    bt, ctx, bs, hkv = b.pool.block_tables, b.pool.context_lens.astype(np.int64), b.block_size, b.num_kv_heads
+    pitch = hkv * slice_bytes
+    seq = np.repeat(np.arange(len(ctx)), (ctx + 15) // 16)
+    tok0 = np.concatenate([16 * np.arange((c + 15) // 16) for c in ctx]).astype(np.int64)
+    rows = bt[seq, tok0 // bs].astype(np.int64) * bs + tok0 % bs
+    offs = (rows[None, :] * pitch + np.arange(hkv, dtype=np.int64)[:, None] * slice_bytes).reshape(-1)
+    return torch.as_tensor(offs, dtype=torch.int64, device=device), pitch
+
+
+def paged_read_ceiling(device, batches):
+    """Time of a plain read of one decode layer's K/V tiles in the decode's
+    access pattern (16-row tiles of one kv-head's row slices at the cache's
+    row pitch, through the block table), split evenly over the waves, with
+    nothing computed: in-tree kernel, over the layers' distinct caches launched
+    back to back, the best of three grid sizes. Also for rows of one-byte
+    elements (the E4M3 layer's pattern), read from the first half of the same
+    caches."""
+    sink = torch.zeros(8192, dtype=torch.int32, device=device)
+    b0 = batches[0]
+    out = {"kernel": "paged_read_kernel (paged_attention_kv_store_amd/probe/hbm_read.hip): the layer's "
+                     "16-token K and V tiles as the decode reads them, split evenly over the waves, "
+                     "nothing computed; best of 512, 1024 and 2048 workgroups of 4 waves"}
+    for name, slice_bytes in (("", b0.head_dim * 2), ("fp8_", b0.head_dim)):
+        offs, pitch = paged_tile_offsets(b0, slice_bytes, device)
+        stream = torch.cuda.current_stream().cuda_stream
+
+        def launch(b, wg):
+            rc = probe_lib().pkv_probe_paged_read(b.k_cache.data_ptr(), b.v_cache.data_ptr(), offs.data_ptr(),
+                                                  offs.numel(), pitch, slice_bytes, wg, sink.data_ptr(), stream)
+            if rc != 0:
+                raise RuntimeError(f"pkv_probe_paged_read: HIP error {rc}")
+        best = min(time_each_launch([lambda b=b, wg=wg: launch(b, wg) for b in batches], 4) for wg in (512, 1024, 2048))
+        nbytes = offs.numel() * 16 * slice_bytes * 2
+        out[name + "paged_read_us"] = round(best * 1e3, 2)
+        out[name + "paged_read_bytes"] = int(nbytes)
+        out[name + "GBps_paged_read"] = round(nbytes / (best * 1e-3) / 1e9, 1)
     return out
 
 
@@ -1190,6 +1237,7 @@ def main():
     stored = float(int((b0.slot_mapping >= 0).sum().item())) * b0.num_kv_heads * b0.head_dim
     fp8_bytes = decode_bytes(b0) + store_bytes(b0) - 2 * kv_elems - 2 * stored
     ceiling = read_ceiling(device, dec_bytes, len(lyr), fp8_bytes)
+    ceiling["paged_read"] = paged_read_ceiling(device, wl.batches)
     achieved = dec_bytes / (dec_ms * 1e-3) / 1e9
 
     # parity sample of layer 0's output against the oracle
@@ -1241,7 +1289,8 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(dec_bytes),
                      "avg_launch_us": round(dec_ms * 1e3, 2),
                      "algorithmic_bytes_per_launch": dec_bytes,
-                     "frac_of_read_ceiling_same_bytes": round(achieved / ceiling["GBps_layer_bytes"], 4)},
+                     "frac_of_read_ceiling_same_bytes": round(achieved / ceiling["GBps_layer_bytes"], 4),
+                     "frac_of_paged_read_time": round(ceiling["paged_read"]["paged_read_us"] / (dec_ms * 1e3), 4)},
         "store_avg_launch_us": round(store_ms * 1e3, 2),
         "plan_avg_launch_us": None if plan_us is None else round(plan_us, 2),
         "parity_sample_max_abs_err": parity_err,
@@ -1256,6 +1305,10 @@ def main():
         torch.cuda.empty_cache()
         log("secondary workloads")
         result["secondary"] = secondary(device, max(5, args.steps // 2), 3, args.algo, ms, args.partition, base)
+        f8 = result["secondary"].get("qwen3_fp8")
+        if f8 and f8.get("decode_avg_launch_us"):
+            f8["frac_of_paged_read_time"] = round(ceiling["paged_read"]["fp8_paged_read_us"] /
+                                                  f8["decode_avg_launch_us"], 4)
     if base is not None:
         base.close()
         head = base.results["qwen3_decode"]
