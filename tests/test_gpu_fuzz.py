@@ -13,6 +13,8 @@ must run in at least its default mode. Outputs start as NaN, so a row that no
 workgroup writes fails.
 """
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -26,7 +28,10 @@ from tests.gpu_helpers import assert_close, oracle_caches, oracle_decode, say, t
 
 pytestmark = pytest.mark.gpu
 
-_rng = np.random.default_rng(20261203)
+# The draws are fixed; PKV_FUZZ_SEED and PKV_FUZZ_MULT (default 1) draw
+# another set, PKV_FUZZ_MULT times as many cases of every kind, for longer runs.
+_rng = np.random.default_rng(int(os.environ.get("PKV_FUZZ_SEED", "20261203")))
+_MULT = max(1, int(os.environ.get("PKV_FUZZ_MULT", "1")))
 _EDGE_CTX = [1, 15, 16, 17, 63, 64, 65, 255, 256, 257, 700, 1300, 2100]
 
 
@@ -43,7 +48,7 @@ def _draw_decode(i):
     return (i, dtype, s, g * hkv, hkv, d, bs, max_ctx, min_ctx, split)
 
 
-DECODE = [_draw_decode(i) for i in range(24)]
+DECODE = [_draw_decode(i) for i in range(24 * _MULT)]
 
 
 def _draw_fp8(i):
@@ -57,7 +62,7 @@ def _draw_fp8(i):
     return (i, s, g * hkv, hkv, d, bs, max_ctx, split)
 
 
-FP8_DECODE = [_draw_fp8(i) for i in range(10)]
+FP8_DECODE = [_draw_fp8(i) for i in range(10 * _MULT)]
 
 
 def _draw_prefill(i):
@@ -71,7 +76,7 @@ def _draw_prefill(i):
     return (i, g * hkv, hkv, bs, chunks, max_rows, max_prior, causal)
 
 
-PREFILL = [_draw_prefill(i) for i in range(16)]
+PREFILL = [_draw_prefill(i) for i in range(16 * _MULT)]
 
 
 def oracle_prefill(b, causal):
@@ -237,7 +242,7 @@ def _draw_fused(i):
     return (i, dtype, s, g * hkv, hkv, d, bs, max_ctx, split)
 
 
-FUSED = [_draw_fused(i) for i in range(14)]
+FUSED = [_draw_fused(i) for i in range(14 * _MULT)]
 
 
 @pytest.mark.parametrize("case", FUSED, ids=_ids)
@@ -311,7 +316,7 @@ def _draw_store(i):
     return (i, dtype, hkv, d, bs, nb, t, pad)
 
 
-STORE = [_draw_store(i) for i in range(16)]
+STORE = [_draw_store(i) for i in range(16 * _MULT)]
 
 
 @pytest.mark.parametrize("case", STORE, ids=_ids)
@@ -358,7 +363,7 @@ def _draw_shared(i):
     return (i, g * hkv, hkv, bs, groups, size, shared, max_ctx)
 
 
-SHARED = [_draw_shared(i) for i in range(10)]
+SHARED = [_draw_shared(i) for i in range(10 * _MULT)]
 
 
 @pytest.mark.parametrize("case", SHARED, ids=_ids)
