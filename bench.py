@@ -308,6 +308,23 @@ def paged_read_ceiling(device, batches):
     return out
 
 
+def paged_read_ms(b, device):
+    """Time of a plain read of one batch's K/V tiles in the decode's order
+    (kv-head first, as `paged_read_ceiling`), split evenly over the waves,
+    nothing computed: the best of three grid sizes, ten launches each (the
+    bandwidth batches exceed the last-level cache)."""
+    sink = torch.zeros(8192, dtype=torch.int32, device=device)
+    offs, pitch = paged_tile_offsets(b, b.head_dim * 2, device)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def launch(wg):
+        rc = probe_lib().pkv_probe_paged_read(b.k_cache.data_ptr(), b.v_cache.data_ptr(), offs.data_ptr(), offs.numel(),
+                                              pitch, b.head_dim * 2, wg, sink.data_ptr(), stream)
+        if rc != 0:
+            raise RuntimeError(f"pkv_probe_paged_read: HIP error {rc}")
+    return min(time_each_launch([lambda wg=wg: launch(wg)], 10) for wg in (512, 1024, 2048))
+
+
 def cold_store_ms(store, device, rounds=10):
     """Median time of one store launch after a 1 GiB streaming read has
     replaced the last-level cache's contents (so neither the new rows nor the
@@ -603,7 +620,9 @@ def secondary(device, steps, warmup, algo, bf16_step_ms, partition=0, base=None)
                                torch.arange(0, b.num_seqs + 1, 8, dtype=torch.int32, device=device),
                                torch.full((b.num_seqs // 8,), 32 * b.block_size, dtype=torch.int32,
                                           device=device),
-                               b.scale, b.max_ctx, 8, 32 * b.block_size), steps, warmup)}
+                               b.scale, b.max_ctx, 8, 32 * b.block_size), steps, warmup),
+                           "paged_read_ms": paged_read_ms(b, device)}
+    res["llama_prefix"]["frac_of_paged_read_time"] = res["llama_prefix"]["paged_read_ms"] / ms
     baseline_decode(base, "llama_prefix", b)
     del dec, b
     b = W.long_splitk(device=device).batches[0]
@@ -625,7 +644,9 @@ def secondary(device, steps, warmup, algo, bf16_step_ms, partition=0, base=None)
                           "auto_choice": "balanced" if auto_part == pkv.PARTITION_BALANCED else auto_part,
                           "splitk_ms": split_ms,
                           "balanced_ms": balanced_ms(b, bt, cl, steps, warmup),
-                          "planned_ms": planned_ms(b, bt, cl, steps, warmup)}
+                          "planned_ms": planned_ms(b, bt, cl, steps, warmup),
+                          "paged_read_ms": paged_read_ms(b, device)}
+    res["long_splitk"]["frac_of_paged_read_time"] = res["long_splitk"]["paged_read_ms"] / ms
     baseline_decode(base, "long_splitk", b)
     del dec, b
     wl = W.mixed(device=device)
@@ -680,7 +701,9 @@ def secondary(device, steps, warmup, algo, bf16_step_ms, partition=0, base=None)
                     "tokens_per_s": 4224 / ((t_store + t_pre + t_dec) * 1e-3),
                     "prefill_tokens_per_s": 4096 / (t_pre * 1e-3),
                     "serial_step_ms": t_serial, "two_stream_step_ms": t_two,
-                    "tokens_per_s_two_streams": 4224 / (t_two * 1e-3)}
+                    "tokens_per_s_two_streams": 4224 / (t_two * 1e-3),
+                    "decode_paged_read_ms": paged_read_ms(db, device)}
+    res["mixed"]["decode_frac_of_paged_read_time"] = res["mixed"]["decode_paged_read_ms"] / t_dec
     baseline_decode(base, "mixed_decode", db)
     baseline_prefill(base, "mixed_prefill", pre)
     del store, prefill, dec, wl, pre, db
