@@ -522,3 +522,42 @@ def random_prefill_batch(seed, num_chunks, num_q_heads, num_kv_heads, head_dim,
                         block_size=block_size, scale=scale)
     batch.cu_seqlens_q = cu
     return batch
+
+
+def decode_batch_of_lengths(seed, context_lens, num_q_heads, num_kv_heads, head_dim, dtype,
+                            block_size=BLOCK_SIZE, device="cpu", store=True) -> PagedBatch:
+    """A decode batch with the given context lengths; dtype "e4m3" draws
+    E4M3 caches (bf16 q and new rows), any torch dtype plain caches."""
+    (rng,) = _streams(seed, 1)
+    ctx = np.asarray(context_lens, np.int32)
+    pool = make_pool(rng, ctx, block_size=block_size, reserve=2)
+    slots = decode_store_slots(pool, block_size) if store else None
+    if dtype == "e4m3":
+        return build_batch_fp8(pool, num_q_heads, num_kv_heads, head_dim, seed, 11, device,
+                               store_slots=slots, block_size=block_size)
+    return build_batch(pool, num_q_heads, num_kv_heads, head_dim, dtype, seed, 11, device,
+                       store_slots=slots, block_size=block_size)
+
+
+def prefill_batch_of_lengths(seed, rows, priors, num_q_heads, num_kv_heads, head_dim, dtype,
+                             block_size=BLOCK_SIZE, device="cpu") -> PagedBatch:
+    """Prefill chunks with the given query rows and cached tokens before them
+    (context = prior + rows); the chunks' own rows are the new rows to store.
+    dtype "e4m3" draws E4M3 caches (bf16 q and new rows)."""
+    (rng,) = _streams(seed, 1)
+    rows = np.asarray(rows, np.int32)
+    prior = np.asarray(priors, np.int32)
+    ctx = (rows + prior).astype(np.int32)
+    pool = make_pool(rng, ctx, block_size=block_size, reserve=2)
+    slots = np.concatenate(
+        [_slots_of(pool, c, np.arange(prior[c], ctx[c]), block_size) for c in range(len(ctx))]
+        + [np.zeros(0, np.int32)]).astype(np.int32)
+    cu = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
+    if dtype == "e4m3":
+        batch = build_batch_fp8(pool, num_q_heads, num_kv_heads, head_dim, seed, 12, device,
+                                num_queries=int(cu[-1]), store_slots=slots, block_size=block_size)
+    else:
+        batch = build_batch(pool, num_q_heads, num_kv_heads, head_dim, dtype, seed, 12, device,
+                            num_queries=int(cu[-1]), store_slots=slots, block_size=block_size)
+    batch.cu_seqlens_q = cu
+    return batch
