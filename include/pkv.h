@@ -112,30 +112,33 @@ int pkv_kv_cache_store(const void* k, const void* v, void* k_cache, void* v_cach
  * Bytes of workspace needed by pkv_paged_attention_decode for the same
  * num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len and
  * partition_size (0 for invalid sizes).
- *  - partition_size > 0 (split-K): 65536 int32 arrival counters (256 KiB,
- *    at the start whatever the sizes; counter s * num_kv_heads + g), then
- *    fp32 running max, sum and unnormalised output for every (sequence,
- *    q-head, partition); 0 when one partition covers max_context_len.
- *    Layout after the counters: m [num_seqs, num_q_heads, P],
+ *  Every mode that merges partial results keeps its arrival counters in one
+ *  counter block, the first 256 KiB (65536 int32) of the workspace, and its
+ *  partial results after it; every call leaves the whole block zero, so one
+ *  workspace serves calls of any mode and size in turn.
+ *  - partition_size > 0 (split-K): the counter block (counter
+ *    s * num_kv_heads + g), then fp32 running max, sum and unnormalised
+ *    output for every (sequence, q-head, partition); 0 when one partition
+ *    covers max_context_len. Layout after the counters: m [num_seqs, num_q_heads, P],
  *    l [num_seqs, num_q_heads, P], o [num_seqs, num_q_heads, P, head_dim],
  *    P = ceil(max_context_len / partition_size). Split-K takes at most
  *    65536 (sequence, kv-head) pairs.
- *  - PKV_PARTITION_BALANCED: 4096 int32 arrival counters (16 KiB, at the
- *    start whatever the sizes), then fp32 pieces of the partial results, two
- *    per wave of the largest grid (4096 waves).
+ *  - PKV_PARTITION_BALANCED: the counter block (its first 4096 counters, one
+ *    per wave of the largest grid), then fp32 pieces of the partial results,
+ *    two per wave of that grid (4096 waves).
  *  - PKV_PARTITION_PLANNED: pkv_decode_plan_size(num_seqs) (the plan).
  *  - PKV_PARTITION_AUTO: the larger of those of the choices it stands for
  *    (pkv_decode_auto_partition, and its split-K fallback).
  *  - 0 (single pass): 0.
- * The arrival counters must be zero before a workspace's first split-K or
- * work-balanced call: pkv_decode_workspace_init clears them.
+ * The counter block must be zero before a workspace's first split-K or
+ * work-balanced call: pkv_decode_workspace_init clears it.
  */
 size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_context_len,
                                  int32_t partition_size);
 
 /*
- * Zero the arrival counters at the start of a decode workspace (its first
+ * Zero the counter block at the start of a decode workspace (its first
  * min(workspace_bytes, 256 KiB) bytes, which hold the split-K and the
  * work-balanced counters), with a kernel on `stream`: no memset, so the call
  * may be captured in a graph. The rest of the workspace is scratch and needs
@@ -208,8 +211,9 @@ int pkv_decode_plan(void* plan, size_t plan_bytes, const int32_t* block_tables,
  *     finishes last, found with the workspace's arrival counters, merges
  *     them (log-sum-exp) in the same launch. The counters must be zero
  *     before the first call (e.g. a zero-filled workspace); every call leaves
- *     them zero, so one workspace serves calls of any sizes in turn, but
- *     calls that run at the same time must not share it. Sequences that fit
+ *     them zero, so one workspace serves calls of any sizes, and of the
+ *     work-balanced mode, in turn, but calls that run at the same time must
+ *     not share it. Sequences that fit
  *     in one partition are written directly.
  *     PKV_PARTITION_BALANCED (MFMA kernel, bf16, at most 8192 sequences,
  *     fewer than 2^30 16-token tiles): one launch whose grid fills the GPU
@@ -220,8 +224,8 @@ int pkv_decode_plan(void* plan, size_t plan_bytes, const int32_t* block_tables,
  *     last, found with atomic counters in the first 16 KiB of `workspace`.
  *     Those must be zero before the first call (e.g. a zero-filled
  *     workspace); every call leaves them zero, so one workspace serves calls
- *     of any sizes in turn, but calls that run at the same time must not
- *     share it. out must be 16-byte aligned.
+ *     of any sizes, and of the split-K mode, in turn, but calls that run at
+ *     the same time must not share it. out must be 16-byte aligned.
  *     PKV_PARTITION_PLANNED (MFMA kernel; bf16 or E4M3 caches): one pass per
  *     (sequence, kv-head), with the items handed out in the order of the
  *     plan that pkv_decode_plan wrote into `workspace` for the same

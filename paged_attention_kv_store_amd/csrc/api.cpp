@@ -182,10 +182,10 @@ extern "C" size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_head
     return wa > ws ? wa : ws;
   }
   if (partition_size == PKV_PARTITION_BALANCED) {
-    // one arrival counter per wave, then two pieces per wave, for the largest grid
+    // the counter block (its first kBalMaxWaves counters: one per wave), then
+    // two pieces per wave, for the largest grid
     const int64_t stride = pkv::bal_piece_stride(num_q_heads / num_kv_heads, head_dim);
-    return (size_t)(pkv::kBalMaxWaves * (int64_t)sizeof(int32_t) +
-                    2 * (int64_t)pkv::kBalMaxWaves * stride * (int64_t)sizeof(float));
+    return (size_t)(pkv::kCounterBytes + 2 * (int64_t)pkv::kBalMaxWaves * stride * (int64_t)sizeof(float));
   }
   if (partition_size == PKV_PARTITION_PLANNED) return pkv_decode_plan_size(num_seqs);
   if (partition_size <= 0) return 0;
@@ -193,10 +193,9 @@ extern "C" size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_head
   int64_t nparts;
   partitioning(max_context_len, partition_size, &part, &nparts);
   if (nparts <= 1) return 0;
-  // a fixed block of arrival counters (one per (sequence, kv-head)), then m,
-  // l, o of every (sequence, q-head, partition)
-  return (size_t)pkv::kSplitMaxItems * sizeof(int32_t) +
-         (size_t)num_seqs * num_q_heads * nparts * (head_dim + 2) * sizeof(float);
+  // the counter block (one counter per (sequence, kv-head)), then m, l, o of
+  // every (sequence, q-head, partition)
+  return (size_t)pkv::kCounterBytes + (size_t)num_seqs * num_q_heads * nparts * (head_dim + 2) * sizeof(float);
 }
 
 extern "C" int32_t pkv_decode_auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len) {
@@ -209,9 +208,8 @@ extern "C" int pkv_decode_workspace_init(void* workspace, size_t workspace_bytes
   if (workspace_bytes == 0) return PKV_OK;
   if (!workspace) return fail(PKV_EINVAL, "%s: null workspace", fn);
   if (!aligned(workspace, 4)) return fail(PKV_EINVAL, "%s: workspace must be 4-byte aligned", fn);
-  // the split-K counter block is the longer of the two counter regions
-  const size_t bytes = workspace_bytes < (size_t)pkv::kSplitMaxItems * 4 ? workspace_bytes
-                                                                          : (size_t)pkv::kSplitMaxItems * 4;
+  // the counter block shared by the split-K and the work-balanced layouts
+  const size_t bytes = workspace_bytes < (size_t)pkv::kCounterBytes ? workspace_bytes : (size_t)pkv::kCounterBytes;
   return hip_status(pkv::launch_zero_ints(reinterpret_cast<int32_t*>(workspace), (int64_t)(bytes / 4),
                                           (hipStream_t)stream), fn);
 }
@@ -364,8 +362,7 @@ int decode_impl(const char* fn, void* out, const void* q, const void* k_cache, c
                   need, workspace ? workspace_bytes : (size_t)0);
     if (!aligned(workspace, 256)) return fail(PKV_EINVAL, "%s: workspace must be 256-byte aligned", fn);
     p.bal_counters = reinterpret_cast<int32_t*>(workspace);
-    p.bal_pieces = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
-                                            pkv::kBalMaxWaves * sizeof(int32_t));
+    p.bal_pieces = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + pkv::kCounterBytes);
     p.bal_piece_stride = (int32_t)pkv::bal_piece_stride(group, head_dim);
     if (clear_counters)
       if (hipError_t e = pkv::launch_zero_ints(p.bal_counters, pkv::kBalMaxWaves, st); e != hipSuccess)
@@ -381,7 +378,7 @@ int decode_impl(const char* fn, void* out, const void* q, const void* k_cache, c
     if (!aligned(workspace, 16)) return fail(PKV_EINVAL, "%s: workspace must be 16-byte aligned", fn);
     const int64_t cells = (int64_t)num_seqs * num_q_heads * nparts;
     p.part_counters = reinterpret_cast<int32_t*>(workspace);
-    float* ws = reinterpret_cast<float*>(p.part_counters + pkv::kSplitMaxItems);
+    float* ws = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + pkv::kCounterBytes);
     p.ws_m = ws;
     p.ws_l = ws + cells;
     p.ws_o = ws + 2 * cells;

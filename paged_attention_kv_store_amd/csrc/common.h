@@ -82,7 +82,8 @@ struct DecodeParams {
   const float* k_scale;
   const float* v_scale;
   // Work-balanced decode only: arrival counters [kBalMaxWaves] (zero between
-  // calls) and per-wave pieces [2 * kBalMaxWaves][piece_stride].
+  // calls; the start of the counter block) and per-wave pieces
+  // [2 * kBalMaxWaves][piece_stride] (after the counter block).
   int32_t* bal_counters;
   float* bal_pieces;
   int32_t bal_piece_stride;  // floats per piece
@@ -113,6 +114,12 @@ struct PlanParams {
 // (sequence, kv-head)), at a fixed place so that calls of any sizes can share
 // a workspace; the partial results follow.
 constexpr int kSplitMaxItems = 65536;
+// Every decode mode that merges partial results keeps its arrival counters
+// in this block at the start of the workspace (split-K: one per (sequence,
+// kv-head); work-balanced: one per wave) and its partial results after it.
+// Every call leaves the whole block zero, so one workspace serves calls of
+// any mode and size in turn.
+constexpr int64_t kCounterBytes = (int64_t)kSplitMaxItems * 4;
 
 // Work-balanced decode limits. Every workgroup keeps the per-sequence tile
 // prefix sums in LDS, which bounds the batch; the piece area is sized for
@@ -121,6 +128,7 @@ constexpr int kBalMaxSeqs = 8192;
 constexpr int kBalMaxWorkgroups = 1024;
 constexpr int kBalWavesPerWorkgroup = 4;
 constexpr int kBalMaxWaves = kBalMaxWorkgroups * kBalWavesPerWorkgroup;
+static_assert((int64_t)kBalMaxWaves * 4 <= kCounterBytes, "work-balanced counters fit the counter block");
 
 // Floats of one piece: unnormalised output [G][D], then max [G] and sum [G],
 // rounded up to 16 bytes.

@@ -147,10 +147,11 @@ def test_workspace_size():
     assert pkv.decode_workspace_size(32, 32, 8, 128, 513, 512) == 65536 * 4 + 32 * 32 * 2 * 130 * 4
     assert lib.pkv_decode_workspace_size(4, 8, 4, 64, 100, 0) == 0
     assert lib.pkv_decode_workspace_size(4, 8, 3, 64, 100, 0) == 0       # Hq not a multiple of Hkv
-    # work-balanced: 4096 int32 counters, then 2 pieces per wave of the largest
-    # grid (4096 waves), each G*D + 2G floats rounded up to 4; no dependence on
-    # num_seqs or max_context_len
-    counters = 4096 * 4
+    # work-balanced: the 256 KiB counter block that split-K uses too (its first
+    # 4096 counters), then 2 pieces per wave of the largest grid (4096 waves),
+    # each G*D + 2G floats rounded up to 4; no dependence on num_seqs or
+    # max_context_len
+    counters = 65536 * 4
     assert pkv.decode_workspace_size(32, 32, 8, 128, 4096, "balanced") == \
         counters + 2 * 4096 * (4 * 128 + 8) * 4
     assert pkv.decode_workspace_size(60, 16, 8, 128, 1024, -1) == counters + 2 * 4096 * 260 * 4

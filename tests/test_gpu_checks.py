@@ -220,3 +220,28 @@ def test_one_call_api_reuses_its_workspace():
         ptrs.append(next(iter(binding._WS_CACHE.values())).data_ptr())
     assert len(binding._WS_CACHE) == 1
     assert ptrs[0] == ptrs[1] == ptrs[2]           # made for the first call, which needs the most
+
+
+def test_split_k_and_work_balanced_alternate_on_one_workspace():
+    """Both modes keep their arrival counters in the workspace's first 256 KiB
+    and their partial results after it, and leave the counters zero, so one
+    workspace serves them in any order. 700 sequences x 8 kv-heads put the
+    split-K counters well past the 4096 work-balanced ones, where the
+    work-balanced pieces would lie if the layouts did not share the block.
+    The one-call functions' cached workspace is checked the same way."""
+    b = W.random_decode_batch(5600, 700, 32, 8, 128, torch.bfloat16, max_ctx=2000, min_ctx=0, store=False)
+    dev = to_device(b)
+    want = oracle_decode(b, store=False)
+    order = ("balanced", 256, "balanced", 512, 256, "balanced")
+    need = max(pkv.decode_workspace_size(b.num_seqs, 32, 8, 128, b.max_ctx, p) for p in order)
+    ws = pkv.new_decode_workspace(need, "cuda")
+    for cached in (False, True):
+        for part in order:
+            say(f"700 seqs, partition {part}, {'cached' if cached else 'one'} workspace")
+            out = torch.full_like(dev["q"], float("nan"))
+            pkv.paged_attention_decode(out, dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
+                                       dev["context_lens"], b.scale, b.max_ctx, partition_size=part,
+                                       workspace=None if cached else ws, algo="mfma")
+            torch.cuda.synchronize()
+            assert_close(out.float().cpu().double().numpy(), want, torch.bfloat16, f"partition {part}")
+    assert int(ws[:65536 * 4].view(torch.int32).abs().sum()) == 0
