@@ -6,6 +6,7 @@ import pytest
 import torch
 
 import oracle
+from oracle import fp8_cache as FP8
 import paged_attention_kv_store_amd as pkv
 from paged_attention_kv_store_amd import workloads as W
 from tests.gpu_helpers import assert_close, oracle_caches, say, to_device
@@ -216,3 +217,54 @@ def test_store_and_prefill_graph_replays_match_eager():
 
     want = _replays_match(step, out, "bf16 prefill")
     assert_close(want.float().cpu().double().numpy(), oracle_prefill(b), torch.bfloat16, "graph prefill")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, "e4m3"], ids=["bf16", "e4m3"])
+def test_empty_chunks_between_others(causal, dtype):
+    """Chunks with no query rows (equal consecutive cu_seqlens_q entries,
+    with or without cached context) produce nothing and shift nothing: the
+    other chunks' rows match the oracle. An all-empty batch is a no-op."""
+    rows, priors = [5, 0, 33, 0, 1, 0], [10, 7, 0, 0, 200, 64]
+    b = W.prefill_batch_of_lengths(9200, rows, priors, 32, 8, 128, dtype)
+    say(f"empty chunks: rows {rows}, cached {priors}, causal={causal}, {dtype}")
+    mq = max(rows)
+    if dtype == "e4m3":
+        d = {k: getattr(b, k).to("cuda") for k in ("q", "k_cache", "v_cache", "k_scale", "v_scale", "k_new",
+                                                    "v_new", "slot_mapping")}
+        bt = torch.as_tensor(b.pool.block_tables, device="cuda")
+        cu = torch.as_tensor(b.cu_seqlens_q, device="cuda")
+        cl = torch.as_tensor(b.pool.context_lens, device="cuda")
+        pkv.kv_cache_store_fp8(d["k_new"], d["v_new"], d["k_cache"], d["v_cache"], d["slot_mapping"], d["k_scale"],
+                               d["v_scale"])
+        ks, vs = W.host_bits(b.k_scale), W.host_bits(b.v_scale)
+        kc, vc = FP8.kv_cache_store_fp8(W.host_bits(b.k_new), W.host_bits(b.v_new), W.host_bits(b.k_cache),
+                                        W.host_bits(b.v_cache), W.host_bits(b.slot_mapping), ks, vs, b.block_size)
+        want = FP8.paged_attention_prefill_chunk_fp8(W.host_bits(b.q), kc, vc, ks, vs, b.pool.block_tables,
+                                                     b.cu_seqlens_q, b.pool.context_lens, b.scale, b.block_size,
+                                                     causal=causal)
+        out = torch.full_like(d["q"], float("nan"))
+        pkv.paged_attention_prefill_chunk_fp8(out, d["q"], d["k_cache"], d["v_cache"], d["k_scale"], d["v_scale"],
+                                              bt, cu, cl, b.scale, mq, b.max_ctx, causal=causal)
+    else:
+        d = to_device(b)
+        pkv.kv_cache_store(d["k_new"], d["v_new"], d["k_cache"], d["v_cache"], d["slot_mapping"])
+        want = oracle_prefill(b, causal=causal)
+        out = torch.full_like(d["q"], float("nan"))
+        pkv.paged_attention_prefill_chunk(out, d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+                                          d["cu_seqlens_q"], d["context_lens"], b.scale, mq, b.max_ctx,
+                                          causal=causal)
+        bt, cu, cl = d["block_tables"], d["cu_seqlens_q"], d["context_lens"]
+    torch.cuda.synchronize()
+    assert_close(out.float().cpu().double().numpy(), want, torch.bfloat16, "rows of the non-empty chunks")
+
+    # every chunk empty: nothing to write, nothing launched that could read
+    none = torch.zeros(len(rows) + 1, dtype=torch.int32, device="cuda")
+    empty = torch.empty((0,) + tuple(out.shape[1:]), dtype=out.dtype, device="cuda")
+    if dtype == "e4m3":
+        pkv.paged_attention_prefill_chunk_fp8(empty, empty, d["k_cache"], d["v_cache"], d["k_scale"],
+                                              d["v_scale"], bt, none, cl, b.scale, 0, b.max_ctx, causal=causal)
+    else:
+        pkv.paged_attention_prefill_chunk(empty, empty, d["k_cache"], d["v_cache"], bt, none, cl, b.scale, 0,
+                                          b.max_ctx, causal=causal)
+    torch.cuda.synchronize()
