@@ -4,7 +4,8 @@ fails):
 
 * very long contexts (262,144 tokens, a ragged 131,071, 40,000 and the
   degenerate 0, 1 and 17) in every decode launch mode, over bf16 and E4M3
-  caches;
+  caches, split-K down to 16-token partitions (16,384 partials merged per
+  row);
 * prefill chunks after up to 200,000 cached tokens, bf16 and E4M3;
 * more prefill (chunk, q-tile) items than the kernel ranks in LDS (8192),
   which hands the items out in the unranked order;
@@ -130,8 +131,8 @@ def _run_prefill(b, d):
 # ---- very long contexts: 8 q / 2 kv heads, D 128 --------------------------------------------
 
 LONG_CTX = [262144, 131071, 1, 0, 40000, 17]
-LONG_MODES = [("mfma", 0), ("mfma", "planned"), ("mfma", 512), ("mfma", 4096), ("mfma", "balanced"),
-              ("mfma", "auto"), ("valu", 0), ("valu", 512)]
+LONG_MODES = [("mfma", 0), ("mfma", "planned"), ("mfma", 16), ("mfma", 512), ("mfma", 4096), ("mfma", "balanced"),
+              ("mfma", "auto"), ("valu", 0), ("valu", 16), ("valu", 512)]
 
 
 @pytest.mark.parametrize("mode", LONG_MODES, ids=lambda m: f"{m[0]}-{m[1]}")
