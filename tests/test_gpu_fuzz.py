@@ -390,3 +390,66 @@ def test_shared_prefix_random_groups(case):
                                              b.scale, b.max_ctx, size, max(prefixes))
     torch.cuda.synchronize()
     assert_close(out.float().cpu().double().numpy(), oracle_decode(b, store=False), torch.bfloat16, "shared")
+
+
+# Scales far from 1/sqrt(D) and block-table padding values, drawn from a
+# stream of their own so that the draws above stay as they are. bf16 only:
+# its 2e-2 bound holds at any scale (the fp32 bound assumes logits of order one).
+_rng_sp = np.random.default_rng(int(os.environ.get("PKV_FUZZ_SEED", "20261203")) + 1)
+
+
+def _draw_scale_pad(i):
+    hkv = int(_rng_sp.choice([1, 2, 4, 8]))
+    g = int(_rng_sp.choice([1, 2, 4, 8]))
+    d = 64 if _rng_sp.random() < 0.3 else 128
+    bs = int(_rng_sp.choice([16, 32, 64, 256]))
+    s = int(_rng_sp.integers(1, 70))
+    max_ctx = int(_rng_sp.choice(_EDGE_CTX))
+    kind = int(_rng_sp.integers(0, 4))
+    scale = [float(_rng_sp.uniform(-3.0, 3.0)), float(_rng_sp.choice([0.0, 20.0, -20.0, 100.0])),
+             float(_rng_sp.uniform(0.02, 0.2)), float(-_rng_sp.uniform(0.02, 0.2))][kind]
+    pad = int(_rng_sp.choice([-1, 2 ** 31 - 1, -(2 ** 31), 0]))
+    split = 16 * int(_rng_sp.choice([1, 4, 16, 32]))
+    return (i, s, g * hkv, hkv, d, bs, max_ctx, round(scale, 4), pad, split)
+
+
+SCALE_PAD = [_draw_scale_pad(i) for i in range(10 * _MULT)]
+
+
+@pytest.mark.parametrize("case", SCALE_PAD, ids=_ids)
+def test_decode_scales_and_table_padding(case):
+    i, s, hq, hkv, d, bs, max_ctx, scale, pad, split = case
+    b = W.random_decode_batch(9700 + i, s, hq, hkv, d, torch.bfloat16, max_ctx=max_ctx, min_ctx=0, block_size=bs,
+                              store=False, scale=scale)
+    bt = b.pool.block_tables
+    for q, c in enumerate(b.pool.context_lens.tolist()):
+        bt[q, -(-c // bs):] = pad
+    say(f"fuzz scale/padding {case}")
+    want = oracle_decode(b, store=False)
+    dv = to_device(b)
+
+    def decode(**kw):
+        def run():
+            out = torch.full_like(dv["q"], float("nan"))
+            pkv.paged_attention_decode(out, dv["q"], dv["k_cache"], dv["v_cache"], dv["block_tables"],
+                                       dv["context_lens"], b.scale, b.max_ctx, **kw)
+            torch.cuda.synchronize()
+            return out.float().cpu().double().numpy()
+        return run
+
+    def planned():
+        plan = pkv.new_decode_plan(s, "cuda")
+        pkv.decode_plan(plan, dv["block_tables"], dv["context_lens"], b.max_ctx, bs)
+        return decode(partition_size="planned", workspace=plan)()
+
+    ran = []
+    for name, fn in [("default", decode()), ("valu", decode(algo="valu")), ("auto", decode(partition_size="auto")),
+                     (f"split {split}", decode(partition_size=split)),
+                     ("balanced", decode(partition_size="balanced")), ("planned", planned)]:
+        got = _run(name, fn)
+        if got is None:
+            assert name != "default", "the default mode must support every shape drawn here"
+            continue
+        assert_close(got, want, torch.bfloat16, name)
+        ran.append(name)
+    say(f"  modes run: {ran}")
