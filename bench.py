@@ -734,7 +734,9 @@ def secondary(device, steps, warmup, algo, bf16_step_ms, partition=0, base=None)
     ms = time_region(verify, steps, warmup)
     by = decode_bytes(sv)
     res["spec_verify"] = {"ms": ms, "GBps": by / ms / 1e6, "pct_hbm_peak": 100 * by / ms / 1e6 / HBM_PEAK_GBS,
-                          "rows_per_s": sv.q.shape[0] / (ms * 1e-3), "rows_per_seq": 4}
+                          "rows_per_s": sv.q.shape[0] / (ms * 1e-3), "rows_per_seq": 4,
+                          "paged_read_ms": paged_read_ms(sv, device)}
+    res["spec_verify"]["frac_of_paged_read_time"] = res["spec_verify"]["paged_read_ms"] / ms
     baseline_prefill(base, "spec_verify", sv)
     return res
 
