@@ -264,12 +264,14 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
 
     max_context_len is a host-side bound on context_lens (it sizes the grid).
     partition_size: 0 (one pass per sequence and kv-head), a positive multiple
-    of 16 (split-K), "balanced" / PARTITION_BALANCED (work-balanced decode), or
+    of 16 (split-K), "balanced" / PARTITION_BALANCED (work-balanced decode),
     "planned" / PARTITION_PLANNED (one pass in the order of the plan passed as
-    `workspace`, written by decode_plan).
-    The workspace those need is taken from `workspace` (a uint8 device
-    tensor; zero-filled before its first work-balanced use) or allocated here
-    through torch when omitted.
+    `workspace`, written by decode_plan), or "auto" / PARTITION_AUTO.
+    The workspace those need is taken from `workspace` (a uint8 device tensor
+    whose first 256 KiB, the arrival counters, are zero before its first
+    split-K or work-balanced use: new_decode_workspace makes one so) or, when
+    omitted, from a workspace cached per (device, stream) and grown as calls
+    need, which split-K and work-balanced calls share in any order.
     """
     _dev(out, q, k_cache, v_cache, block_tables, context_lens)
     _need(q.dim() == 3 and out.shape == q.shape and out.dtype == q.dtype, "q/out must be [S, Hq, D]")
