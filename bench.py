@@ -22,7 +22,10 @@ traffic that rocprofv3 counters measured for that kernel (from
 profiles/decode_qwen3_traffic.json, null if the kernel source changed since),
 the bandwidth a plain streaming-read kernel reaches in the same run (over
 4 GiB, and over 28 buffers of one decode layer's bytes launched back to back,
-the achievable ceiling for a launch of that size), tokens/s, the other
+the achievable ceiling for a launch of that size), a plain read of each
+bandwidth workload's own K/V tiles through its block table (the ceiling of
+that access pattern; the line reports the kernel's time as a fraction of
+it), tokens/s, the other
 standard workloads (prefix-shared batch, long-context decode in the
 automatic partition mode, mixed chunked prefill + decode with the prefill's
 matrix-core utilisation and a cold-cache store, verification of 4
